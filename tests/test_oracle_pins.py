@@ -1,0 +1,408 @@
+"""Pins of the fp64 oracle against things other than itself.
+
+Each test fixes one part of the oracle by a library routine that computes the
+same quantity independently (torch's fp64 CPU attention, layer norm, RMS norm,
+SiLU and autograd), a closed form, an invariant, a hand-derived worked example
+or brute force on tiny inputs.  Together they are chosen so that a dropped
+term, a wrong sign or index, or a transposed operand anywhere in the oracle
+fails at least one of them (the mutation tests at the end check a few such
+mistakes explicitly).  CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as TF
+
+from oracle import whale_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_examples.json")
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def small_case(seed=0, B=3, C=2, n_q=3, d=16, h=2, lengths=(5, 1, 7)):
+    L = np.asarray(lengths)
+    off = np.concatenate([[0], np.cumsum(L)])
+    M, T = B * C * n_q, int(off[-1])
+    return dict(B=B, C=C, n_q=n_q, d=d, h=h, off=off,
+                Q=rnd(seed, M, d), K=rnd(seed + 1, T, d), V=rnd(seed + 2, T, d))
+
+
+def t64(x):
+    return torch.as_tensor(np.asarray(x, dtype=np.float64))
+
+
+# ------------------------------------------------------------ worked examples
+
+def test_golden_worked_examples():
+    g = json.load(open(GOLDEN))
+    e = g["attention_two_keys"]
+    A, lse = O.xattn_fwd(e["q"], e["k"], e["v"], [0, 2], C=1, n_q=1, h=1, scale=e["scale"])
+    np.testing.assert_allclose(A, e["A"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse[:, 0], e["lse"], rtol=0, atol=1e-14)
+    e = g["fusion_mlp_select"]
+    F, _ = O.fusion_mlp(e["A"], e["H_w"], e["W_F"], O.ACT_NONE)
+    np.testing.assert_array_equal(F, e["F_none"])
+    F, _ = O.fusion_mlp(e["A"], e["H_w"], e["W_F"], O.ACT_SILU)
+    np.testing.assert_allclose(F, e["F_silu"], rtol=0, atol=1e-15)
+    e = g["swiglu_tied_scalar"]
+    Y, _ = O.swiglu_ffn(e["F"], O.NORM_NONE, 0.0, [1.0], [0.0], e["W_U"], O.GATE_SHARED, e["W_D"])
+    np.testing.assert_allclose(Y, e["Y"], rtol=1e-15)
+
+
+# ------------------------------------------------------------ attention (a3)
+
+def test_attention_matches_torch_sdpa():
+    c = small_case()
+    A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    dh = c["d"] // c["h"]
+    for b in range(c["B"]):
+        rows = slice(b * c["C"] * c["n_q"], (b + 1) * c["C"] * c["n_q"])
+        lo, hi = c["off"][b], c["off"][b + 1]
+        for j in range(c["h"]):
+            cols = slice(j * dh, (j + 1) * dh)
+            q, k, v = t64(c["Q"][rows, cols]), t64(c["K"][lo:hi, cols]), t64(c["V"][lo:hi, cols])
+            ref = TF.scaled_dot_product_attention(q[None], k[None], v[None])[0].numpy()
+            np.testing.assert_allclose(A[rows, cols], ref, rtol=1e-12, atol=1e-13)
+            s = (q @ k.T).numpy() / math.sqrt(dh)
+            np.testing.assert_allclose(lse[rows, j], torch.logsumexp(torch.tensor(s), 1).numpy(),
+                                       rtol=1e-13, atol=1e-13)
+
+
+def test_attention_brute_force_fsum():
+    c = small_case(seed=3, B=2, C=2, n_q=2, d=4, h=2, lengths=(3, 4))
+    A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    dh = 2
+    for b in range(2):
+        for m in range(b * 4, (b + 1) * 4):
+            for j in range(2):
+                keys = range(c["off"][b], c["off"][b + 1])
+                sc = [math.fsum(c["Q"][m, j * dh + e] * c["K"][l, j * dh + e] for e in range(dh))
+                      / math.sqrt(dh) for l in keys]
+                w = [math.exp(x) for x in sc]
+                z = math.fsum(w)
+                assert abs(lse[m, j] - math.log(z)) < 1e-13
+                for e in range(dh):
+                    a = math.fsum(w[i] * c["V"][l, j * dh + e] for i, l in enumerate(keys)) / z
+                    assert abs(A[m, j * dh + e] - a) < 1e-13
+
+
+def test_attention_weights_sum_to_one():
+    c = small_case(seed=5)
+    ones = np.ones_like(c["V"])
+    A, _ = O.xattn_fwd(c["Q"], c["K"], ones, c["off"], c["C"], c["n_q"], c["h"])
+    np.testing.assert_allclose(A, 1.0, rtol=0, atol=1e-14)
+
+
+def test_single_key_returns_value_row_exactly():
+    c = small_case(seed=7, lengths=(1, 1, 1))
+    A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    per = c["C"] * c["n_q"]
+    for b in range(c["B"]):
+        np.testing.assert_array_equal(A[b * per:(b + 1) * per], np.repeat(c["V"][b:b + 1], per, 0))
+
+
+def test_uniform_scores_give_average_pooling():
+    # Q = 0 makes every score equal: the attention reduces to the mean of the
+    # history's values, the average-pooling ablation of Table 1.
+    c = small_case(seed=9)
+    A, lse = O.xattn_fwd(np.zeros_like(c["Q"]), c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    per = c["C"] * c["n_q"]
+    for b in range(c["B"]):
+        lo, hi = c["off"][b], c["off"][b + 1]
+        np.testing.assert_allclose(A[b * per:(b + 1) * per], np.repeat(c["V"][lo:hi].mean(0, keepdims=True), per, 0),
+                                   rtol=1e-14, atol=1e-14)
+        np.testing.assert_allclose(lse[b * per:(b + 1) * per], math.log(hi - lo), rtol=1e-14)
+
+
+def test_one_hot_saturated_scores_pick_one_row():
+    c = small_case(seed=11, B=1, C=1, n_q=2, d=4, h=1, lengths=(9,))
+    K = np.zeros((9, 4))
+    K[6] = [2000.0, 0, 0, 0]      # score gap 1000: exp(-1000) underflows to 0 in fp64
+    Q = np.array([[1.0, 0, 0, 0], [1.0, 0, 0, 0]])
+    A, lse = O.xattn_fwd(Q, K, c["V"], c["off"], 1, 2, 1)
+    np.testing.assert_array_equal(A, np.repeat(c["V"][6:7], 2, 0))
+
+
+def test_history_permutation_invariance():
+    c = small_case(seed=13)
+    A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    perm = np.concatenate([c["off"][b] + np.random.default_rng(b).permutation(c["off"][b + 1] - c["off"][b])
+                           for b in range(c["B"])])
+    A2, lse2 = O.xattn_fwd(c["Q"], c["K"][perm], c["V"][perm], c["off"], c["C"], c["n_q"], c["h"])
+    np.testing.assert_allclose(A2, A, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(lse2, lse, rtol=1e-13, atol=1e-14)
+
+
+def test_candidate_independence():
+    # Sharing K/V across the C candidates equals attending per candidate.
+    c = small_case(seed=17)
+    A, _ = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    n_q, C = c["n_q"], c["C"]
+    for b in range(c["B"]):
+        lo, hi = c["off"][b], c["off"][b + 1]
+        for cc in range(C):
+            rows = slice((b * C + cc) * n_q, (b * C + cc + 1) * n_q)
+            A1, _ = O.xattn_fwd(c["Q"][rows], c["K"][lo:hi], c["V"][lo:hi], [0, hi - lo], 1, n_q, c["h"])
+            np.testing.assert_allclose(A1, A[rows], rtol=1e-13, atol=1e-14)
+
+
+def test_empty_history():
+    c = small_case(seed=19, lengths=(4, 0, 3))
+    A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    per = c["C"] * c["n_q"]
+    assert np.all(A[per:2 * per] == 0) and np.all(np.isneginf(lse[per:2 * per]))
+    dA = rnd(1, *A.shape)
+    dQ, dK, dV = O.xattn_bwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"], None, dA)
+    assert np.all(dQ[per:2 * per] == 0)
+
+
+# ------------------------------------------------------------ norms, act
+
+@pytest.mark.parametrize("kind", [O.NORM_LAYER, O.NORM_RMS, O.NORM_NONE])
+def test_norm_matches_torch(kind):
+    x, g, b = rnd(1, 6, 16) * 3 + 1, rnd(2, 16), rnd(3, 16)
+    y, xhat, rstd = O.norm_fwd(x, kind, g, b, 1e-5)
+    if kind == O.NORM_LAYER:
+        ref = TF.layer_norm(t64(x), (16,), t64(g), t64(b), 1e-5).numpy()
+        np.testing.assert_allclose(xhat.mean(1), 0, atol=1e-14)
+        np.testing.assert_allclose(xhat.var(1), 1, rtol=1e-5)
+    elif kind == O.NORM_RMS:
+        ref = TF.rms_norm(t64(x), (16,), t64(g), 1e-5).numpy()
+        np.testing.assert_allclose(np.sqrt((xhat ** 2).mean(1)), 1, rtol=1e-5)
+    else:
+        ref = x
+    np.testing.assert_allclose(y, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_silu_and_derivative_match_torch():
+    z = t64(np.linspace(-30, 30, 601)).requires_grad_()
+    s = TF.silu(z)
+    s.sum().backward()
+    np.testing.assert_allclose(O.silu(z.detach().numpy()), s.detach().numpy(), rtol=1e-15, atol=1e-300)
+    np.testing.assert_allclose(O.dsilu(z.detach().numpy()), z.grad.numpy(), rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------------------ a1, a2, a4, a5
+
+def test_identity_projection():
+    Hw, Hs = rnd(1, 6, 8), rnd(2, 5, 8)
+    I = np.eye(8)
+    Q, K, V = O.proj_qkv(Hw, Hs, O.NORM_NONE, 0.0, None, None, None, None, I, I, I)
+    np.testing.assert_array_equal(Q, Hw)
+    np.testing.assert_array_equal(K, Hs)
+    np.testing.assert_array_equal(V, Hs)
+
+
+def test_projection_matches_torch_linear():
+    Hw, Hs = rnd(1, 6, 8), rnd(2, 5, 8)
+    Wq, Wk, Wv = rnd(3, 8, 8), rnd(4, 8, 8), rnd(5, 8, 8)
+    g, b = rnd(6, 8), rnd(7, 8)
+    Q, K, V = O.proj_qkv(Hw, Hs, O.NORM_LAYER, 1e-5, g, b, g, b, Wq, Wk, Wv)
+    Xq = TF.layer_norm(t64(Hw), (8,), t64(g), t64(b), 1e-5)
+    Xs = TF.layer_norm(t64(Hs), (8,), t64(g), t64(b), 1e-5)
+    np.testing.assert_allclose(Q, TF.linear(Xq, t64(Wq)).numpy(), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(K, TF.linear(Xs, t64(Wk)).numpy(), rtol=1e-13, atol=1e-13)
+    np.testing.assert_allclose(V, TF.linear(Xs, t64(Wv)).numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_fusion_mlp_closed_forms():
+    A, Hw = rnd(1, 5, 4), rnd(2, 5, 4)
+    I, Z0 = np.eye(4), np.zeros((4, 4))
+    F, _ = O.fusion_mlp(A, Hw, np.zeros((4, 8)), O.ACT_SILU)
+    np.testing.assert_array_equal(F, Hw)                       # SiLU(0) = 0
+    F, _ = O.fusion_mlp(A, Hw, np.hstack([I, Z0]), O.ACT_NONE)
+    np.testing.assert_array_equal(F, Hw + A)                   # attended half first
+    F, _ = O.fusion_mlp(A, Hw, np.hstack([Z0, I]), O.ACT_NONE)
+    np.testing.assert_array_equal(F, 2 * Hw)                   # Wukong half second
+    W = rnd(3, 4, 8)
+    F, Z = O.fusion_mlp(A, Hw, W, O.ACT_SILU)
+    ref = t64(Hw) + TF.silu(TF.linear(torch.cat([t64(A), t64(Hw)], 1), t64(W)))
+    np.testing.assert_allclose(F, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def test_swiglu_closed_forms():
+    Fm = rnd(1, 6, 4)
+    d, H = 4, 4
+    Wu, Wd = rnd(2, H, d), rnd(3, d, H)
+    Y, U = O.swiglu_ffn(Fm, O.NORM_NONE, 0.0, None, None, Wu, O.GATE_SHARED, np.zeros((d, H)))
+    np.testing.assert_array_equal(Y, Fm)                         # W_D = 0
+    Y, U = O.swiglu_ffn(Fm, O.NORM_NONE, 0.0, None, None, np.eye(4), O.GATE_SHARED, np.eye(4))
+    sig = 1 / (1 + np.exp(-Fm))
+    np.testing.assert_allclose(Y, Fm + Fm * Fm * sig, rtol=1e-14)   # G = U^2 sigma(U)
+    # separate gate with W_G = W_U equals the tied gate
+    g, b = rnd(4, d), rnd(5, d)
+    Yt, _ = O.swiglu_ffn(Fm, O.NORM_LAYER, 1e-5, g, b, Wu, O.GATE_SHARED, Wd)
+    Ys, _ = O.swiglu_ffn(Fm, O.NORM_LAYER, 1e-5, g, b, np.vstack([Wu, Wu]), O.GATE_SEPARATE, Wd)
+    np.testing.assert_allclose(Ys, Yt, rtol=1e-14, atol=1e-14)
+    # separate gate against torch with distinct W_G, W_U
+    Wg = rnd(6, H, d)
+    Ys, _ = O.swiglu_ffn(Fm, O.NORM_LAYER, 1e-5, g, b, np.vstack([Wg, Wu]), O.GATE_SEPARATE, Wd)
+    X = TF.layer_norm(t64(Fm), (d,), t64(g), t64(b), 1e-5)
+    ref = t64(Fm) + TF.linear(TF.silu(TF.linear(X, t64(Wg))) * TF.linear(X, t64(Wu)), t64(Wd))
+    np.testing.assert_allclose(Ys, ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+# ------------------------------------------------------------ backward
+
+def _layer_case(seed, lengths=(3, 1, 0), norm=O.NORM_LAYER, gate=O.GATE_SHARED, ffn=True):
+    B, C, n_q, d, h, H = len(lengths), 2, 2, 8, 2, 12
+    off = np.concatenate([[0], np.cumsum(lengths)])
+    r = np.random.default_rng(seed)
+    p = {k: r.standard_normal((d, d)) * 0.4 for k in ("W_Q", "W_K", "W_V")}
+    p["W_F"] = r.standard_normal((d, 2 * d)) * 0.3
+    p["W_U"] = r.standard_normal(((2 if gate == O.GATE_SEPARATE else 1) * H, d)) * 0.3
+    p["W_D"] = r.standard_normal((d, H)) * 0.3
+    for k in ("g_q", "g_kv", "g_f"):
+        p[k] = 1 + 0.3 * r.standard_normal(d)
+    for k in ("b_q", "b_kv", "b_f"):
+        p[k] = 0.3 * r.standard_normal(d)
+    x = dict(H_w=r.standard_normal((B * C * n_q, d)), H_s=r.standard_normal((int(off[-1]), d)))
+    dY = r.standard_normal((B * C * n_q, d))
+    kw = dict(offsets=off, C=C, n_q=n_q, h=h, norm=norm, gate=gate, ffn=ffn)
+    return x, p, dY, kw
+
+
+GRAD_OF = {"H_w": "dH_w", "H_s": "dH_s", "W_Q": "dW_Q", "W_K": "dW_K", "W_V": "dW_V",
+           "W_F": "dW_F", "W_U": "dW_U", "W_D": "dW_D", "g_q": "dg_q", "b_q": "db_q",
+           "g_kv": "dg_kv", "b_kv": "db_kv", "g_f": "dg_f", "b_f": "db_f"}
+
+
+@pytest.mark.parametrize("norm,gate,ffn", [(O.NORM_LAYER, O.GATE_SHARED, True),
+                                           (O.NORM_RMS, O.GATE_SEPARATE, True),
+                                           (O.NORM_LAYER, O.GATE_SHARED, False)])
+def test_layer_gradients_match_finite_differences(norm, gate, ffn):
+    x, p, dY, kw = _layer_case(21, norm=norm, gate=gate, ffn=ffn)
+
+    def loss():
+        out = O.layer_fwd(x["H_w"], x["H_s"], p=p, **kw)
+        return float((out["Y"] * dY).sum())
+
+    g = O.layer_bwd(x["H_w"], x["H_s"], p=p, dY=dY, **kw)
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        if not ffn and name in ("W_U", "W_D", "g_f", "b_f"):
+            continue
+        if norm == O.NORM_RMS and name in ("b_q", "b_kv", "b_f"):
+            np.testing.assert_array_equal(g[gname], 0)
+            continue
+        arr = x[name] if name in x else p[name]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = loss()
+            arr[idx] = old - eps
+            lm = loss()
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gname], num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+
+def test_gradients_match_torch_autograd():
+    x, p, dY, kw = _layer_case(23, lengths=(6, 2, 5))
+    g = O.layer_bwd(x["H_w"], x["H_s"], p=p, dY=dY, **kw)
+    T = {k: t64(v).requires_grad_() for k, v in {**x, **p}.items()}
+    C, n_q, h, off = kw["C"], kw["n_q"], kw["h"], kw["offsets"]
+    d = T["H_w"].shape[1]
+    Xq = TF.layer_norm(T["H_w"], (d,), T["g_q"], T["b_q"], 1e-5)
+    Xs = TF.layer_norm(T["H_s"], (d,), T["g_kv"], T["b_kv"], 1e-5)
+    Q, K, V = Xq @ T["W_Q"].T, Xs @ T["W_K"].T, Xs @ T["W_V"].T
+    dh = d // h
+    A_rows = []
+    for b in range(len(off) - 1):
+        q = Q[b * C * n_q:(b + 1) * C * n_q].reshape(-1, h, dh).transpose(0, 1)
+        k = K[off[b]:off[b + 1]].reshape(-1, h, dh).transpose(0, 1)
+        v = V[off[b]:off[b + 1]].reshape(-1, h, dh).transpose(0, 1)
+        A_rows.append(TF.scaled_dot_product_attention(q, k, v).transpose(0, 1).reshape(-1, d))
+    A = torch.cat(A_rows)
+    F = T["H_w"] + TF.silu(torch.cat([A, T["H_w"]], 1) @ T["W_F"].T)
+    U = TF.layer_norm(F, (d,), T["g_f"], T["b_f"], 1e-5) @ T["W_U"].T
+    Y = F + (TF.silu(U) * U) @ T["W_D"].T
+    (Y * t64(dY)).sum().backward()
+    for name, gname in GRAD_OF.items():
+        np.testing.assert_allclose(g[gname], T[name].grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
+
+
+def test_single_key_backward_closed_form():
+    c = small_case(seed=29, lengths=(1, 1, 1))
+    dA = rnd(31, *c["Q"].shape)
+    dQ, dK, dV = O.xattn_bwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"], None, dA)
+    per = c["C"] * c["n_q"]
+    np.testing.assert_allclose(dQ, 0, atol=1e-14)
+    np.testing.assert_allclose(dK, 0, atol=1e-13)
+    for b in range(c["B"]):
+        np.testing.assert_allclose(dV[b], dA[b * per:(b + 1) * per].sum(0), rtol=1e-13)
+
+
+def test_kv_gradient_sums_over_candidates():
+    # dK, dV of the shared K/V = the sum over candidates of each candidate's own.
+    c = small_case(seed=37)
+    dA = rnd(41, *c["Q"].shape)
+    _, dK, dV = O.xattn_bwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"], None, dA)
+    n_q, C = c["n_q"], c["C"]
+    for b in range(c["B"]):
+        lo, hi = c["off"][b], c["off"][b + 1]
+        sk, sv = np.zeros((hi - lo, c["d"])), np.zeros((hi - lo, c["d"]))
+        for cc in range(C):
+            rows = slice((b * C + cc) * n_q, (b * C + cc + 1) * n_q)
+            _, k1, v1 = O.xattn_bwd(c["Q"][rows], c["K"][lo:hi], c["V"][lo:hi], [0, hi - lo], 1, n_q,
+                                    c["h"], None, dA[rows])
+            sk += k1
+            sv += v1
+        np.testing.assert_allclose(dK[lo:hi], sk, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(dV[lo:hi], sv, rtol=1e-12, atol=1e-13)
+
+
+# ------------------------------------------------------------ planted mistakes
+
+def _mutant_xattn(kind):
+    """A copy of the oracle's attention with one plausible mistake planted."""
+    def f(Q, K, V, offsets, C, n_q, h, scale=None):
+        Q, K, V = np.asarray(Q, float), np.asarray(K, float), np.asarray(V, float)
+        M, d = Q.shape
+        dh = d // h
+        sc = 1 / np.sqrt(dh) if kind != "no_scale" else 1.0
+        A = np.zeros((M, d))
+        for b in range(len(offsets) - 1):
+            rows = slice(b * C * n_q, (b + 1) * C * n_q)
+            if kind == "row_by_request_only":
+                rows = slice(b * n_q, (b + 1) * n_q) if b * n_q < M else slice(0, 0)
+            lo, hi = offsets[b], offsets[b + 1]
+            if kind == "drop_last_key":
+                hi = max(lo + 1, hi - 1)
+            for j in range(h):
+                cols = slice(j * dh, (j + 1) * dh)
+                s = sc * Q[rows, cols] @ K[lo:hi, cols].T
+                e = np.exp(s - s.max(1, keepdims=True))
+                p = e / e.sum(1, keepdims=True)
+                if kind == "transposed_head":
+                    A[rows, cols] = p @ V[lo:hi, (slice((h - 1 - j) * dh, (h - j) * dh))]
+                else:
+                    A[rows, cols] = p @ V[lo:hi, cols]
+        return A
+    return f
+
+
+@pytest.mark.parametrize("kind", ["no_scale", "row_by_request_only", "drop_last_key", "transposed_head"])
+def test_pins_catch_planted_attention_mistakes(kind):
+    c = small_case(seed=43, lengths=(5, 4, 7))
+    mut = _mutant_xattn(kind)(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    ok, _ = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
+    dh = c["d"] // c["h"]
+    ref = np.zeros_like(ok)
+    for b in range(c["B"]):
+        rows = slice(b * c["C"] * c["n_q"], (b + 1) * c["C"] * c["n_q"])
+        lo, hi = c["off"][b], c["off"][b + 1]
+        for j in range(c["h"]):
+            cols = slice(j * dh, (j + 1) * dh)
+            ref[rows, cols] = TF.scaled_dot_product_attention(
+                t64(c["Q"][rows, cols])[None], t64(c["K"][lo:hi, cols])[None], t64(c["V"][lo:hi, cols])[None])[0].numpy()
+    np.testing.assert_allclose(ok, ref, rtol=1e-12, atol=1e-13)
+    assert not np.allclose(mut, ref, rtol=1e-6, atol=1e-8)
