@@ -1,0 +1,466 @@
+// libwhalefuse C ABI: argument validation, workspace sizing and dispatch.
+// Every check runs on the host before anything is enqueued; no call reads
+// device memory on the host or synchronises (the host shape hints max_L and
+// total_L replace any read of the offsets: gist.science Technical Summary
+// §2.2, "shape hint tensors").
+#include <cmath>
+#include <cstring>
+
+#include "../../include/whalefuse.h"
+#include "kernels.h"
+
+namespace {
+
+struct Shape {
+  int64_t M, T;
+  int B, C, n_q, d, h, dh, QR, max_L;
+};
+
+whale_status_t check_dims(const whale_dims_t* dims, whale_dtype_t dtype, Shape* s) {
+  if (dims == nullptr) return WHALE_ERR_NULL;
+  if (dtype != WHALE_F32 && dtype != WHALE_BF16) return WHALE_ERR_DTYPE;
+  const whale_dims_t& x = *dims;
+  if (x.B <= 0 || x.C <= 0 || x.n_q <= 0 || x.d <= 0 || x.h <= 0 || x.max_L < 0 || x.total_L < 0)
+    return WHALE_ERR_SHAPE;
+  if (x.d % x.h != 0) return WHALE_ERR_SHAPE;
+  const int64_t QR = (int64_t)x.C * x.n_q;
+  const int64_t M = QR * x.B;
+  if (QR > (1 << 30) || M > ((int64_t)1 << 31) - 1) return WHALE_ERR_SHAPE;
+  if ((int64_t)x.max_L > x.total_L) return WHALE_ERR_SHAPE;
+  if (x.total_L > (int64_t)x.B * x.max_L) return WHALE_ERR_SHAPE;
+  const int dh = x.d / x.h;
+  if (dh != 32 && dh != 64) return WHALE_ERR_UNSUPPORTED;
+  if (x.d > 512) return WHALE_ERR_UNSUPPORTED;
+  s->M = M;
+  s->T = x.total_L;
+  s->B = x.B; s->C = x.C; s->n_q = x.n_q; s->d = x.d; s->h = x.h; s->dh = dh;
+  s->QR = (int)QR;
+  s->max_L = x.max_L;
+  return WHALE_OK;
+}
+
+bool norm_ok(whale_norm_t n) { return n == WHALE_NORM_LAYER || n == WHALE_NORM_RMS || n == WHALE_NORM_NONE; }
+
+// Norm parameters required by a norm kind (gamma for layer/rms, beta for layer).
+bool norm_params_ok(whale_norm_t n, const float* g, const float* b) {
+  if (n == WHALE_NORM_NONE) return true;
+  if (g == nullptr) return false;
+  return n == WHALE_NORM_RMS || b != nullptr;
+}
+
+whale_status_t ret(hipError_t e) { return e == hipSuccess ? WHALE_OK : WHALE_ERR_LAUNCH; }
+#define WHALE_TRY(expr)                       \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return WHALE_ERR_LAUNCH; \
+  } while (0)
+
+size_t esz(whale_dtype_t t) { return t == WHALE_BF16 ? 2 : 4; }
+
+// Bump allocator over a caller-provided workspace (256-byte aligned pieces).
+struct Carve {
+  char* base;
+  size_t used = 0;
+  explicit Carve(void* p) : base((char*)p) {}
+  void* take(size_t bytes) {
+    void* p = base ? base + used : nullptr;
+    used += (bytes + 255) / 256 * 256;
+    return p;
+  }
+};
+
+GemmArgs gemm_defaults() {
+  GemmArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.norm_kind = 2;
+  return a;
+}
+
+WgradArgs wgrad_defaults() {
+  WgradArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.norm_kind = 2;
+  return a;
+}
+
+size_t wgrad_partial_bytes(int64_t M, int N, int K) {
+  const int s = wgrad_splits(M, N, K);
+  return s > 1 ? (size_t)s * N * K * 4 : 0;
+}
+
+hipError_t wgrad(const void* G, int ldg, const void* X, int ldx, int pro, int64_t M, int N, int K, float* dW,
+                 float* partial, bool bf16, hipStream_t st, const float* stats = nullptr,
+                 const float* gamma = nullptr, const float* beta = nullptr, int norm_kind = 2,
+                 const void* X2 = nullptr, int ldx2 = 0, int ksplit = 0, int gate_H = 0) {
+  WgradArgs a = wgrad_defaults();
+  a.G = G; a.ldg = ldg; a.X = X; a.ldx = ldx; a.X2 = X2; a.ldx2 = ldx2; a.ksplit = ksplit;
+  a.stats = stats; a.gamma = gamma; a.beta = beta; a.norm_kind = norm_kind; a.gate_H = gate_H;
+  a.dW = dW; a.partial = partial; a.M = M; a.N = N; a.K = K; a.splits = wgrad_splits(M, N, K); a.pro = pro;
+  if (pro == WPRO_NORM && norm_kind == 2) a.pro = WPRO_PLAIN;
+  return launch_wgrad(a, bf16, st);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* whale_status_string(whale_status_t s) {
+  switch (s) {
+    case WHALE_OK: return "WHALE_OK";
+    case WHALE_ERR_NULL: return "WHALE_ERR_NULL: a required pointer is NULL";
+    case WHALE_ERR_SHAPE: return "WHALE_ERR_SHAPE: inconsistent sizes or values";
+    case WHALE_ERR_DTYPE: return "WHALE_ERR_DTYPE: unknown data type";
+    case WHALE_ERR_UNSUPPORTED: return "WHALE_ERR_UNSUPPORTED: shape not implemented (d_h must be 32 or 64, d <= 512, H % 64 == 0)";
+    case WHALE_ERR_WORKSPACE: return "WHALE_ERR_WORKSPACE: workspace too small";
+    case WHALE_ERR_LAUNCH: return "WHALE_ERR_LAUNCH: kernel launch failed";
+  }
+  return "WHALE_ERR_UNKNOWN";
+}
+
+const char* whale_version(void) { return "0.1.0"; }
+
+// ------------------------------------------------------------------ forward
+
+whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, const void* H_w, const void* H_s,
+                              whale_norm_t norm, float eps, const float* g_q, const float* b_q, const float* g_kv,
+                              const float* b_kv, const void* W_Q, const void* W_K, const void* W_V, void* Q, void* K,
+                              void* V, float* stats_q, float* stats_kv, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!norm_ok(norm) || !(eps >= 0.f) || !std::isfinite(eps)) return WHALE_ERR_SHAPE;
+  if (!H_w || !W_Q || !W_K || !W_V || !Q) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!H_s || !K || !V)) return WHALE_ERR_NULL;
+  if (!norm_params_ok(norm, g_q, b_q) || !norm_params_ok(norm, g_kv, b_kv)) return WHALE_ERR_NULL;
+  if (norm != WHALE_NORM_NONE && (!stats_q || (s.T > 0 && !stats_kv))) return WHALE_ERR_NULL;
+  const bool bf = dtype == WHALE_BF16;
+  const int nk = (int)norm;
+  if (norm != WHALE_NORM_NONE) {
+    WHALE_TRY(launch_norm_stats(H_w, stats_q, s.M, s.d, nk, eps, bf, stream));
+    WHALE_TRY(launch_norm_stats(H_s, stats_kv, s.T, s.d, nk, eps, bf, stream));
+  }
+  GemmArgs a = gemm_defaults();
+  a.X = H_w; a.ldx = s.d; a.stats = stats_q; a.gamma = g_q; a.beta = b_q; a.norm_kind = nk;
+  a.W = W_Q; a.ldw = s.d; a.Y = Q; a.ldy = s.d; a.M = s.M; a.N = s.d; a.K = s.d;
+  a.pro = norm == WHALE_NORM_NONE ? PRO_PLAIN : PRO_NORM; a.epi = EPI_STORE;
+  WHALE_TRY(launch_gemm_nt(a, bf, stream));
+  if (s.T > 0) {
+    // K and V in one pass over H_s: weight rows [0, d) from W_K, [d, 2d) from W_V.
+    GemmArgs b = a;
+    b.X = H_s; b.stats = stats_kv; b.gamma = g_kv; b.beta = b_kv;
+    b.W = W_K; b.Y = K; b.M = s.T; b.N = 2 * s.d;
+    WHALE_TRY(launch_gemm_nt_dual(b, s.d, W_V, V, bf, stream));
+  }
+  return WHALE_OK;
+}
+
+whale_status_t whale_jagged_xattn_fwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                                      const void* V, const int64_t* offsets, float scale, void* A, float* lse,
+                                      hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!Q || !A || !offsets) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!K || !V)) return WHALE_ERR_NULL;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return WHALE_ERR_SHAPE;
+  XattnArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.offsets = offsets; a.A = A; a.lse = lse;
+  a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh;
+  a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
+  return ret(launch_xattn_fwd(a, dtype == WHALE_BF16, stream));
+}
+
+whale_status_t whale_fusion_mlp(const whale_dims_t* dims, whale_dtype_t dtype, const void* A, const void* H_w,
+                                const void* W_F, whale_act_t act, void* F, void* Z_saved, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (act != WHALE_ACT_SILU && act != WHALE_ACT_NONE) return WHALE_ERR_SHAPE;
+  if (!A || !H_w || !W_F || !F) return WHALE_ERR_NULL;
+  GemmArgs a = gemm_defaults();
+  a.X = A; a.ldx = s.d; a.X2 = H_w; a.ldx2 = s.d; a.ksplit = s.d;
+  a.W = W_F; a.ldw = 2 * s.d; a.Y = F; a.ldy = s.d; a.R = H_w; a.ldr = s.d; a.Z = Z_saved; a.ldz = s.d;
+  a.M = s.M; a.N = s.d; a.K = 2 * s.d; a.pro = PRO_CONCAT;
+  a.epi = act == WHALE_ACT_SILU ? EPI_SILU_RESID : EPI_RESID;
+  return ret(launch_gemm_nt(a, dtype == WHALE_BF16, stream));
+}
+
+static bool ffn_h_ok(int32_t H) { return H > 0 && H % 64 == 0 && H <= (1 << 16); }
+
+size_t whale_swiglu_ffn_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype, whale_gate_t gate, int32_t H) {
+  Shape s;
+  if (check_dims(dims, dtype, &s) != WHALE_OK || !ffn_h_ok(H)) return 0;
+  (void)gate;
+  Carve c(nullptr);
+  c.take((size_t)s.M * H * esz(dtype));      // G
+  return c.used;
+}
+
+whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, const void* F, whale_norm_t norm,
+                                float eps, const float* g_f, const float* b_f, const void* W_U, whale_gate_t gate,
+                                int32_t H, const void* W_D, void* Y, void* U_saved, float* stats_f, void* workspace,
+                                size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!norm_ok(norm) || !(eps >= 0.f) || !std::isfinite(eps)) return WHALE_ERR_SHAPE;
+  if (gate != WHALE_GATE_SHARED && gate != WHALE_GATE_SEPARATE) return WHALE_ERR_SHAPE;
+  if (!ffn_h_ok(H)) return WHALE_ERR_UNSUPPORTED;
+  if (!F || !W_U || !W_D || !Y) return WHALE_ERR_NULL;
+  if (!norm_params_ok(norm, g_f, b_f)) return WHALE_ERR_NULL;
+  if (norm != WHALE_NORM_NONE && !stats_f) return WHALE_ERR_NULL;
+  const size_t need = whale_swiglu_ffn_workspace_size(dims, dtype, gate, H);
+  if (!workspace) return WHALE_ERR_NULL;
+  if (ws_bytes < need) return WHALE_ERR_WORKSPACE;
+  const bool bf = dtype == WHALE_BF16;
+  Carve c(workspace);
+  void* G = c.take((size_t)s.M * H * esz(dtype));
+  if (norm != WHALE_NORM_NONE) WHALE_TRY(launch_norm_stats(F, stats_f, s.M, s.d, (int)norm, eps, bf, stream));
+  GemmArgs a = gemm_defaults();
+  a.X = F; a.ldx = s.d; a.stats = stats_f; a.gamma = g_f; a.beta = b_f; a.norm_kind = (int)norm;
+  a.W = W_U; a.ldw = s.d; a.Y = G; a.ldy = H; a.Z = U_saved;
+  a.M = s.M; a.K = s.d;
+  a.pro = norm == WHALE_NORM_NONE ? PRO_PLAIN : PRO_NORM;
+  if (gate == WHALE_GATE_SHARED) { a.N = H; a.epi = EPI_GATE_TIED; a.ldz = H; }
+  else { a.N = 2 * H; a.epi = EPI_GATE_SEP; a.ldz = 2 * H; }
+  WHALE_TRY(launch_gemm_nt(a, bf, stream));
+  GemmArgs b = gemm_defaults();
+  b.X = G; b.ldx = H; b.W = W_D; b.ldw = H; b.Y = Y; b.ldy = s.d; b.R = F; b.ldr = s.d;
+  b.M = s.M; b.N = s.d; b.K = H; b.pro = PRO_PLAIN; b.epi = EPI_RESID;
+  return ret(launch_gemm_nt(b, bf, stream));
+}
+
+// ------------------------------------------------------------------ backward
+
+size_t whale_jagged_xattn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype) {
+  Shape s;
+  if (check_dims(dims, dtype, &s) != WHALE_OK) return 0;
+  Carve c(nullptr);
+  c.take((size_t)s.M * s.h * 4);
+  const int splits = xattn_bwd_splits(s.B, s.h, s.QR, s.max_L, s.dh);
+  if (splits > 1) c.take((size_t)splits * 2 * s.T * s.d * 4);
+  return c.used;
+}
+
+whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                                      const void* V, const int64_t* offsets, float scale, const void* A,
+                                      const float* lse, const void* dA, void* dQ, void* dK, void* dV,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!Q || !offsets || !A || !lse || !dA || !dQ || !workspace) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!K || !V || !dK || !dV)) return WHALE_ERR_NULL;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return WHALE_ERR_SHAPE;
+  if (ws_bytes < whale_jagged_xattn_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
+  Carve c(workspace);
+  XattnBwdArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.offsets = offsets; a.A = A; a.lse = lse; a.dA = dA;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
+  a.Dbuf = (float*)c.take((size_t)s.M * s.h * 4);
+  a.splits = xattn_bwd_splits(s.B, s.h, s.QR, s.max_L, s.dh);
+  a.partial = a.splits > 1 ? (float*)c.take((size_t)a.splits * 2 * s.T * s.d * 4) : nullptr;
+  a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh; a.max_L = s.max_L; a.T = s.T;
+  a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
+  return ret(launch_xattn_bwd(a, dtype == WHALE_BF16, stream));
+}
+
+size_t whale_fusion_mlp_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype) {
+  Shape s;
+  if (check_dims(dims, dtype, &s) != WHALE_OK) return 0;
+  Carve c(nullptr);
+  c.take((size_t)s.M * s.d * esz(dtype));            // dZ
+  c.take((size_t)2 * s.d * s.d * esz(dtype));        // W_F^T
+  c.take(wgrad_partial_bytes(s.M, s.d, 2 * s.d));
+  return c.used;
+}
+
+whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* A, const void* H_w,
+                                    const void* W_F, whale_act_t act, const void* Z_saved, const void* dF, void* dA,
+                                    void* dH_w, float* dW_F, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (act != WHALE_ACT_SILU && act != WHALE_ACT_NONE) return WHALE_ERR_SHAPE;
+  if (!A || !H_w || !W_F || !dF || !dA || !dH_w || !dW_F || !workspace) return WHALE_ERR_NULL;
+  if (act == WHALE_ACT_SILU && !Z_saved) return WHALE_ERR_NULL;
+  if (ws_bytes < whale_fusion_mlp_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
+  const bool bf = dtype == WHALE_BF16;
+  const int d = s.d;
+  Carve c(workspace);
+  void* dZ = c.take((size_t)s.M * d * esz(dtype));
+  void* WFt = c.take((size_t)2 * d * d * esz(dtype));
+  float* part = (float*)c.take(wgrad_partial_bytes(s.M, d, 2 * d));
+  WHALE_TRY(launch_dact(dF, Z_saved, dZ, s.M * d, (int)act, bf, stream));
+  WHALE_TRY(launch_transpose(W_F, d, 2 * d, WFt, d, 0, bf, stream));   // [2d, d]
+  // dW_F = dZ^T [A, H_w]
+  WHALE_TRY(wgrad(dZ, d, A, d, WPRO_CONCAT, s.M, d, 2 * d, dW_F, part, bf, stream, nullptr, nullptr, nullptr, 2,
+                  H_w, d, d));
+  // dA = dZ W_F[:, :d]  ;  dH_w = dF + dZ W_F[:, d:]
+  GemmArgs g = gemm_defaults();
+  g.X = dZ; g.ldx = d; g.W = WFt; g.ldw = d; g.Y = dA; g.ldy = d; g.M = s.M; g.N = d; g.K = d;
+  g.pro = PRO_PLAIN; g.epi = EPI_STORE;
+  WHALE_TRY(launch_gemm_nt(g, bf, stream));
+  g.W = (const char*)WFt + (size_t)d * d * esz(dtype);
+  g.Y = dH_w; g.R = dF; g.ldr = d; g.epi = EPI_RESID;
+  return ret(launch_gemm_nt(g, bf, stream));
+}
+
+size_t whale_swiglu_ffn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype, whale_gate_t gate,
+                                           int32_t H) {
+  Shape s;
+  if (check_dims(dims, dtype, &s) != WHALE_OK || !ffn_h_ok(H)) return 0;
+  const int Hu = gate == WHALE_GATE_SEPARATE ? 2 * H : H;
+  Carve c(nullptr);
+  c.take((size_t)H * s.d * esz(dtype));              // W_D^T [H, d]
+  c.take((size_t)s.M * Hu * esz(dtype));             // dU
+  c.take((size_t)s.d * Hu * esz(dtype));             // W_U^T [d, Hu]
+  c.take((size_t)s.M * s.d * 4);                     // dX_f fp32
+  const size_t p1 = wgrad_partial_bytes(s.M, s.d, H), p2 = wgrad_partial_bytes(s.M, Hu, s.d);
+  c.take(p1 > p2 ? p1 : p2);
+  c.take((size_t)norm_bwd_blocks(s.M) * 2 * s.d * 4);
+  return c.used;
+}
+
+whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* F, whale_norm_t norm,
+                                    float eps, const float* g_f, const float* b_f, const float* stats_f,
+                                    const void* W_U, whale_gate_t gate, int32_t H, const void* W_D,
+                                    const void* U_saved, const void* dY, void* dF, float* dW_U, float* dW_D,
+                                    float* dg_f, float* db_f, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!norm_ok(norm) || !(eps >= 0.f) || !std::isfinite(eps)) return WHALE_ERR_SHAPE;
+  if (gate != WHALE_GATE_SHARED && gate != WHALE_GATE_SEPARATE) return WHALE_ERR_SHAPE;
+  if (!ffn_h_ok(H)) return WHALE_ERR_UNSUPPORTED;
+  if (!F || !W_U || !W_D || !U_saved || !dY || !dF || !dW_U || !dW_D || !workspace) return WHALE_ERR_NULL;
+  if (!norm_params_ok(norm, g_f, b_f)) return WHALE_ERR_NULL;
+  if (norm != WHALE_NORM_NONE && (!stats_f || !dg_f || (norm == WHALE_NORM_LAYER && !db_f))) return WHALE_ERR_NULL;
+  if (ws_bytes < whale_swiglu_ffn_bwd_workspace_size(dims, dtype, gate, H)) return WHALE_ERR_WORKSPACE;
+  const bool bf = dtype == WHALE_BF16;
+  const bool sep = gate == WHALE_GATE_SEPARATE;
+  const int d = s.d, Hu = sep ? 2 * H : H;
+  Carve c(workspace);
+  void* WDt = c.take((size_t)H * d * esz(dtype));
+  void* dU = c.take((size_t)s.M * Hu * esz(dtype));
+  void* WUt = c.take((size_t)d * Hu * esz(dtype));
+  float* dXf = (float*)c.take((size_t)s.M * d * 4);
+  const size_t p1 = wgrad_partial_bytes(s.M, d, H), p2 = wgrad_partial_bytes(s.M, Hu, d);
+  float* part = (float*)c.take(p1 > p2 ? p1 : p2);
+  float* npart = (float*)c.take((size_t)norm_bwd_blocks(s.M) * 2 * d * 4);
+
+  // dW_D = dY^T G, with G recomputed from U in the loader.
+  WHALE_TRY(wgrad(dY, d, U_saved, Hu, sep ? WPRO_GATE_SEP : WPRO_GATE_TIED, s.M, d, H, dW_D, part, bf, stream,
+                  nullptr, nullptr, nullptr, 2, nullptr, 0, 0, H));
+  // dU = (dY W_D) * gate'(U)
+  WHALE_TRY(launch_transpose(W_D, d, H, WDt, d, 0, bf, stream));       // [H, d]
+  GemmArgs g = gemm_defaults();
+  g.X = dY; g.ldx = d; g.W = WDt; g.ldw = d; g.Y = dU; g.ldy = Hu; g.Z = (void*)U_saved; g.ldz = Hu;
+  g.M = s.M; g.N = H; g.K = d; g.pro = PRO_PLAIN; g.epi = sep ? EPI_DGATE_SEP : EPI_DGATE_TIED;
+  WHALE_TRY(launch_gemm_nt(g, bf, stream));
+  // dW_U = dU^T Norm_f(F)
+  WHALE_TRY(wgrad(dU, Hu, F, d, WPRO_NORM, s.M, Hu, d, dW_U, part, bf, stream, stats_f, g_f, b_f, (int)norm));
+  // dX_f = dU W_U (fp32)
+  WHALE_TRY(launch_transpose(W_U, Hu, d, WUt, Hu, 0, bf, stream));     // [d, Hu]
+  GemmArgs x = gemm_defaults();
+  x.X = dU; x.ldx = Hu; x.W = WUt; x.ldw = Hu; x.Y = dXf; x.ldy = d; x.y_f32 = true;
+  x.M = s.M; x.N = d; x.K = Hu; x.pro = PRO_PLAIN; x.epi = EPI_STORE;
+  WHALE_TRY(launch_gemm_nt(x, bf, stream));
+  // dF = dY + Norm_f backward(dX_f)
+  int nblk = 0;
+  WHALE_TRY(launch_norm_bwd(F, stats_f, g_f, dXf, dY, dF, npart, s.M, d, (int)norm, bf, &nblk, stream));
+  if (norm != WHALE_NORM_NONE)
+    WHALE_TRY(launch_colsum_reduce(npart, nblk, d, dg_f, norm == WHALE_NORM_LAYER ? db_f : nullptr, stream));
+  if (norm == WHALE_NORM_RMS && db_f) WHALE_TRY(launch_fill_zero(db_f, d, stream));
+  return WHALE_OK;
+}
+
+size_t whale_proj_qkv_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype) {
+  Shape s;
+  if (check_dims(dims, dtype, &s) != WHALE_OK) return 0;
+  Carve c(nullptr);
+  c.take((size_t)s.d * s.d * esz(dtype));            // W_Q^T
+  c.take((size_t)2 * s.d * s.d * esz(dtype));        // [W_K^T | W_V^T]
+  c.take((size_t)s.M * s.d * 4);                     // dX_q
+  c.take((size_t)s.T * s.d * 4);                     // dX_s
+  const size_t p1 = wgrad_partial_bytes(s.M, s.d, s.d), p2 = wgrad_partial_bytes(s.T, s.d, s.d);
+  c.take(p1 > p2 ? p1 : p2);
+  c.take((size_t)norm_bwd_blocks(s.M) * 2 * s.d * 4);
+  c.take((size_t)norm_bwd_blocks(s.T) * 2 * s.d * 4);
+  return c.used;
+}
+
+whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* H_w, const void* H_s,
+                                  whale_norm_t norm, float eps, const float* g_q, const float* b_q, const float* g_kv,
+                                  const float* b_kv, const float* stats_q, const float* stats_kv, const void* W_Q,
+                                  const void* W_K, const void* W_V, const void* dQ, const void* dK, const void* dV,
+                                  const void* dH_w_in, void* dH_w, void* dH_s, float* dW_Q, float* dW_K, float* dW_V,
+                                  float* dg_q, float* db_q, float* dg_kv, float* db_kv, void* workspace,
+                                  size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!norm_ok(norm) || !(eps >= 0.f) || !std::isfinite(eps)) return WHALE_ERR_SHAPE;
+  if (!H_w || !W_Q || !W_K || !W_V || !dQ || !dH_w || !dW_Q || !dW_K || !dW_V || !workspace) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!H_s || !dK || !dV || !dH_s)) return WHALE_ERR_NULL;
+  if (!norm_params_ok(norm, g_q, b_q) || !norm_params_ok(norm, g_kv, b_kv)) return WHALE_ERR_NULL;
+  if (norm != WHALE_NORM_NONE) {
+    if (!stats_q || (s.T > 0 && !stats_kv) || !dg_q || !dg_kv) return WHALE_ERR_NULL;
+    if (norm == WHALE_NORM_LAYER && (!db_q || !db_kv)) return WHALE_ERR_NULL;
+  }
+  if (ws_bytes < whale_proj_qkv_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
+  const bool bf = dtype == WHALE_BF16;
+  const int d = s.d, nk = (int)norm;
+  Carve c(workspace);
+  void* WQt = c.take((size_t)d * d * esz(dtype));
+  void* WKVt = c.take((size_t)2 * d * d * esz(dtype));
+  float* dXq = (float*)c.take((size_t)s.M * d * 4);
+  float* dXs = (float*)c.take((size_t)s.T * d * 4);
+  const size_t p1 = wgrad_partial_bytes(s.M, d, d), p2 = wgrad_partial_bytes(s.T, d, d);
+  float* part = (float*)c.take(p1 > p2 ? p1 : p2);
+  float* npq = (float*)c.take((size_t)norm_bwd_blocks(s.M) * 2 * d * 4);
+  float* npk = (float*)c.take((size_t)norm_bwd_blocks(s.T) * 2 * d * 4);
+
+  // Weight gradients with the normalised inputs recomputed in the loader.
+  WHALE_TRY(wgrad(dQ, d, H_w, d, WPRO_NORM, s.M, d, d, dW_Q, part, bf, stream, stats_q, g_q, b_q, nk));
+  if (s.T > 0) {
+    WHALE_TRY(wgrad(dK, d, H_s, d, WPRO_NORM, s.T, d, d, dW_K, part, bf, stream, stats_kv, g_kv, b_kv, nk));
+    WHALE_TRY(wgrad(dV, d, H_s, d, WPRO_NORM, s.T, d, d, dW_V, part, bf, stream, stats_kv, g_kv, b_kv, nk));
+  } else {
+    WHALE_TRY(launch_fill_zero(dW_K, (int64_t)d * d, stream));
+    WHALE_TRY(launch_fill_zero(dW_V, (int64_t)d * d, stream));
+  }
+  // dX_q = dQ W_Q ; dX_s = [dK, dV] [W_K ; W_V]
+  WHALE_TRY(launch_transpose(W_Q, d, d, WQt, d, 0, bf, stream));
+  WHALE_TRY(launch_transpose(W_K, d, d, WKVt, 2 * d, 0, bf, stream));
+  WHALE_TRY(launch_transpose(W_V, d, d, WKVt, 2 * d, d, bf, stream));
+  GemmArgs g = gemm_defaults();
+  g.X = dQ; g.ldx = d; g.W = WQt; g.ldw = d; g.Y = dXq; g.ldy = d; g.y_f32 = true;
+  g.M = s.M; g.N = d; g.K = d; g.pro = PRO_PLAIN; g.epi = EPI_STORE;
+  WHALE_TRY(launch_gemm_nt(g, bf, stream));
+  if (s.T > 0) {
+    GemmArgs k = g;
+    k.X = dK; k.X2 = dV; k.ldx2 = d; k.ksplit = d; k.W = WKVt; k.ldw = 2 * d; k.Y = dXs;
+    k.M = s.T; k.K = 2 * d; k.pro = PRO_CONCAT;
+    WHALE_TRY(launch_gemm_nt(k, bf, stream));
+  }
+  int nb = 0;
+  WHALE_TRY(launch_norm_bwd(H_w, stats_q, g_q, dXq, dH_w_in, dH_w, npq, s.M, d, nk, bf, &nb, stream));
+  if (norm != WHALE_NORM_NONE)
+    WHALE_TRY(launch_colsum_reduce(npq, nb, d, dg_q, norm == WHALE_NORM_LAYER ? db_q : nullptr, stream));
+  if (s.T > 0) {
+    WHALE_TRY(launch_norm_bwd(H_s, stats_kv, g_kv, dXs, nullptr, dH_s, npk, s.T, d, nk, bf, &nb, stream));
+    if (norm != WHALE_NORM_NONE)
+      WHALE_TRY(launch_colsum_reduce(npk, nb, d, dg_kv, norm == WHALE_NORM_LAYER ? db_kv : nullptr, stream));
+  } else if (norm != WHALE_NORM_NONE) {
+    WHALE_TRY(launch_fill_zero(dg_kv, d, stream));
+    if (db_kv) WHALE_TRY(launch_fill_zero(db_kv, d, stream));
+  }
+  if (norm == WHALE_NORM_RMS) {
+    if (db_q) WHALE_TRY(launch_fill_zero(db_q, d, stream));
+    if (db_kv) WHALE_TRY(launch_fill_zero(db_kv, d, stream));
+  }
+  return WHALE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Shared device helpers for the libwhalefuse kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+#define WHALE_DEV __device__ __forceinline__
+
+// --------------------------------------------------------------- element types
+// Every MFMA operand chunk holds 8 elements per lane.  For bf16 this is one
+// v_mfma_f32_32x32x16_bf16 operand.  For fp32 it is fed to eight
+// v_mfma_f32_32x32x2_f32 issues, element i of every lane going to issue i;
+// the contraction index each (lane half, element) pair stands for is then a
+// bijection onto the 16 k values of the step, the same for A and B, so the
+// sum is the full contraction either way.
+template <typename T> struct Vec;
+template <> struct Vec<bf16> { typedef bf16x8 x8; typedef bf16x4 x4; };
+template <> struct Vec<float> { typedef f32x8 x8; typedef f32x4 x4; };
+
+template <typename T> using x8_t = typename Vec<T>::x8;
+template <typename T> using x4_t = typename Vec<T>::x4;
+
+WHALE_DEV float to_f(bf16 x) { return (float)x; }
+WHALE_DEV float to_f(float x) { return x; }
+template <typename T> WHALE_DEV T from_f(float x);
+template <> WHALE_DEV bf16 from_f<bf16>(float x) { return (bf16)x; }   // v_cvt_pk_bf16_f32: nearest even
+template <> WHALE_DEV float from_f<float>(float x) { return x; }
+
+template <typename T> WHALE_DEV x8_t<T> zero8() { x8_t<T> v; for (int i = 0; i < 8; ++i) v[i] = from_f<T>(0.f); return v; }
+
+template <typename T> WHALE_DEV x8_t<T> ld8(const T* p) { return *reinterpret_cast<const x8_t<T>*>(p); }
+template <typename T> WHALE_DEV void st8(T* p, const x8_t<T>& v) { *reinterpret_cast<x8_t<T>*>(p) = v; }
+template <typename T> WHALE_DEV x4_t<T> ld4(const T* p) { return *reinterpret_cast<const x4_t<T>*>(p); }
+template <typename T> WHALE_DEV void st4(T* p, const x4_t<T>& v) { *reinterpret_cast<x4_t<T>*>(p) = v; }
+
+// Two 4-element runs -> one 8-element operand.
+template <typename T> WHALE_DEV x8_t<T> cat44(const x4_t<T>& a, const x4_t<T>& b) {
+  x8_t<T> v;
+  v[0] = a[0]; v[1] = a[1]; v[2] = a[2]; v[3] = a[3];
+  v[4] = b[0]; v[5] = b[1]; v[6] = b[2]; v[7] = b[3];
+  return v;
+}
+
+// --------------------------------------------------------------- MFMA
+// D[32x32] += A[32x16] * B[16x32].  Lane l supplies row (A) / column (B)
+// l % 32 and eight contraction values for half l / 32.  The accumulator
+// register r of lane l holds D[8*(r/4) + 4*(l/32) + r%4][l % 32].
+WHALE_DEV void mma32(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+WHALE_DEV void mma32(f32x16& acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[i], b[i], acc, 0, 0, 0);
+}
+
+// Row of accumulator register r for lane half hh (column is lane % 32).
+WHALE_DEV constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + (r & 3); }
+
+WHALE_DEV f32x16 zero16() { f32x16 v; for (int i = 0; i < 16; ++i) v[i] = 0.f; return v; }
+
+// --------------------------------------------------------------- misc
+// Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  This
+// gives each XCD one contiguous range of logical ids so that workgroups
+// that read the same data (one request's K/V, one weight tile) share that
+// XCD's L2.  A bijection on [0, n).
+WHALE_DEV int xcd_remap(int id, int n) {
+  const int nx = 8;
+  const int per = n / nx, rem = n % nx;
+  const int x = id % nx, i = id / nx;
+  return x * per + (x < rem ? x : rem) + i;
+}
+
+WHALE_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+WHALE_DEV float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
+WHALE_DEV float siluf_(float z) { return z * sigmoidf_(z); }
+WHALE_DEV float dsiluf_(float z) { float s = sigmoidf_(z); return s * (1.f + z * (1.f - s)); }
+
+WHALE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;

@@ -1,0 +1,261 @@
+// Jagged softmax cross-attention, forward (Eq. (4) of the WHALE paper as
+// described by the pith.science verdict record, pith_extraction.key_machinery,
+// and the paper-daily.com deep reading, §2): every query token of every
+// candidate of request b attends over request b's whole history, K/V shared
+// by all C candidates (M-FALCON, Footnote 1 in the pith.science referee
+// report).
+//
+// Design (gfx950):
+//  * One workgroup = 4 waves = one (request b, head j, block of 4*QPW
+//    queries).  Its K/V tiles of BN = 64 history rows are staged in LDS once
+//    and read by all of its queries; the query blocks of one (b, j) are
+//    adjacent logical ids placed on one XCD, so they stream the same K/V
+//    through that XCD's L2 at about the same time.
+//  * Each wave owns QPW queries.  It computes S^T = K Q^T with 32x32x16 MFMA
+//    (A = K rows from LDS, B = its Q fragments held in registers for the
+//    whole history).  In the S^T accumulator layout a lane holds one query
+//    column and 16 history rows, so the softmax max/sum reduce inside the
+//    lane plus one exchange between the two lane halves, and the
+//    probabilities P^T are already laid out as the B operand of the next
+//    product O^T += V^T P^T: no data movement between the two products.
+//    V is written to LDS transposed so that the A operand of that product
+//    (V^T rows, 8 history rows per lane) is two 4-element reads.
+//  * Online softmax in base 2 with the scale folded in.  Lazy rescaling:
+//    the running reference max is only moved when a tile's max exceeds it by
+//    more than kTau (probabilities then stay below 2^kTau, harmless in fp32
+//    accumulation and bf16 operands); the result O / l is independent of the
+//    reference, and lse = ref + log2(l) is exact.
+//  * The ragged tail is masked (scores of rows past L_b set to -inf, their
+//    K/V never loaded and zero in LDS): no padding of the history.
+#include "common.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kNW = 4;            // waves per workgroup
+constexpr int kBN = 64;           // history rows per tile
+constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
+
+template <typename T, int DH>
+struct FwdTile {
+  static constexpr int KLD = DH + 8;          // K tile row stride (elements)
+  static constexpr int VLD = kBN + 4;         // V^T tile row stride (elements)
+  static constexpr int CPR = DH / 8;          // 8-element chunks per row
+  static constexpr int NCH = kBN * CPR / (kNW * 64);   // chunks per thread per tensor
+  static_assert(NCH >= 1 && kBN * CPR % (kNW * 64) == 0, "tile/threads mismatch");
+};
+
+template <typename T, int DH, int QPW>
+__global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int64_t* __restrict__ offsets, T* __restrict__ A, float* __restrict__ lse,
+    int d, int h, int QR, int nqb, float c, int nblocks) {
+  using TT = FwdTile<T, DH>;
+  constexpr int NQ = QPW / 32, KS = DH / 16, NE = DH / 32, QB = kNW * QPW;
+  constexpr int KLD = TT::KLD, VLD = TT::VLD, CPR = TT::CPR, NCH = TT::NCH;
+  __shared__ __attribute__((aligned(32))) T Ks[2][kBN * KLD];
+  __shared__ __attribute__((aligned(32))) T Vt[2][DH * VLD];
+
+  const int lid = xcd_remap(blockIdx.x, nblocks);
+  const int qbi = lid % nqb;
+  const int bj = lid / nqb;
+  const int j = bj % h, b = bj / h;
+  const int64_t lo = offsets[b];
+  const int L = (int)(offsets[b + 1] - lo);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int64_t qrow0 = (int64_t)b * QR;
+  const int qbase = qbi * QB + w * QPW;
+
+  // Q fragments: B operand of S^T = K Q^T, lane = query column.
+  x8_t<T> qf[NQ][KS];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const int q = qbase + 32 * qb + l32;
+    const T* src = Q + (qrow0 + q) * d + j * DH + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = (q < QR) ? ld8<T>(src + 16 * ks) : zero8<T>();
+  }
+
+  f32x16 oacc[NE][NQ];
+#pragma unroll
+  for (int e = 0; e < NE; ++e)
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) oacc[e][qb] = zero16();
+  float mref[NQ], lsum[NQ];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = -INFINITY; lsum[qb] = 0.f; }
+
+  const int ntiles = (L + kBN - 1) / kBN;
+  const T* Kh = K + lo * d + j * DH;
+  const T* Vh = V + lo * d + j * DH;
+
+  x8_t<T> kr[NCH], vr[NCH];
+  auto load_tile = [&](int t) {
+    const int nvalid = min(kBN, L - t * kBN);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = tid + i * kNW * 64;
+      const int row = ch / CPR, e0 = 8 * (ch % CPR);
+      const int64_t off = (int64_t)(t * kBN + row) * d + e0;
+      kr[i] = row < nvalid ? ld8<T>(Kh + off) : zero8<T>();
+      vr[i] = row < nvalid ? ld8<T>(Vh + off) : zero8<T>();
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = tid + i * kNW * 64;
+      const int row = ch / CPR, e0 = 8 * (ch % CPR);
+      st8<T>(&Ks[buf][row * KLD + e0], kr[i]);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) Vt[buf][(e0 + u) * VLD + row] = vr[i][u];
+    }
+  };
+
+  if (ntiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
+
+  for (int t = 0; t < ntiles; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < ntiles) load_tile(t + 1);
+    const int nvalid = min(kBN, L - t * kBN);
+
+    // S^T[key][q] for two 32-row key blocks.
+    f32x16 s[2][NQ];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) s[kb][qb] = zero16();
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const x8_t<T> a = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb) mma32(s[kb][qb], a, qf[qb][ks]);
+      }
+    }
+    if (nvalid < kBN) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + acc_row(r, hh) >= nvalid) s[kb][qb][r] = -INFINITY;
+    }
+
+    // Tile max per query column, shared by both lane halves.
+    float mnew[NQ];
+    bool need = false;
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      float mx = s[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
+      mnew[qb] = fmaxf(mref[qb], mx);
+      need |= mnew[qb] > mref[qb] + kTau;
+    }
+    if (__ballot(need)) {
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) {
+        if (mnew[qb] > mref[qb] + kTau) {
+          const float alpha = fast_exp2(mref[qb] - mnew[qb]);
+          mref[qb] = mnew[qb];
+          lsum[qb] *= alpha;
+#pragma unroll
+          for (int e = 0; e < NE; ++e)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[e][qb][r] *= alpha;
+        }
+      }
+    }
+
+    // P^T = exp2(s*c - ref), row sums kept per lane half, packed as B operands.
+    x8_t<T> pf[2][NQ][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = fast_exp2(fmaf(s[kb][qb][r], c, -mref[qb]));
+          lsum[qb] += p;
+          pf[kb][qb][r >> 3][r & 7] = from_f<T>(p);
+        }
+
+    // O^T[e][q] += V^T[e][key] P^T[key][q].  Operand element u of lane half
+    // hh is history row 4*hh + u (u < 4) or 8 + 4*hh + (u - 4) of the
+    // 16-row step, matching the accumulator rows of P^T.
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          const T* vp = &Vt[buf][(32 * e + l32) * VLD + 32 * kb + 16 * mm + 4 * hh];
+          const x8_t<T> a = cat44<T>(ld4<T>(vp), ld4<T>(vp + 8));
+#pragma unroll
+          for (int qb = 0; qb < NQ; ++qb) mma32(oacc[e][qb], a, pf[kb][qb][mm]);
+        }
+    }
+
+    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // Epilogue: combine the two lane halves' sums, normalise, store A and lse.
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const int q = qbase + 32 * qb + l32;
+    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (q < QR) {
+      T* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          x4_t<T> o;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = from_f<T>(oacc[e][qb][4 * g + u] * inv);
+          st4<T>(dst + 32 * e + 8 * g, o);
+        }
+      if (lse != nullptr && hh == 0)
+        lse[(qrow0 + q) * h + j] = ltot > 0.f ? (mref[qb] + log2f(ltot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <typename T, int DH, int QPW>
+hipError_t launch_fwd_t(const XattnArgs& a, hipStream_t st) {
+  constexpr int QB = kNW * QPW;
+  const int nqb = (a.QR + QB - 1) / QB;
+  const int64_t nblk = (int64_t)a.B * a.h * nqb;
+  if (nblk == 0) return hipSuccess;
+  const float c = a.scale * kLog2e;
+  hipLaunchKernelGGL((xattn_fwd_kernel<T, DH, QPW>), dim3((unsigned)nblk), dim3(kNW * 64), 0, st,
+                     (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (T*)a.A, a.lse,
+                     a.d, a.h, a.QR, nqb, c, (int)nblk);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_fwd_dh(const XattnArgs& a, hipStream_t st) {
+  const bool wide = a.QR >= 1024;
+  switch (a.dh) {
+    case 32: return wide ? launch_fwd_t<T, 32, 64>(a, st) : launch_fwd_t<T, 32, 32>(a, st);
+    case 64: return wide ? launch_fwd_t<T, 64, 64>(a, st) : launch_fwd_t<T, 64, 32>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_xattn_fwd(const XattnArgs& a, bool bf16_data, hipStream_t st) {
+  return bf16_data ? launch_fwd_dh<bf16>(a, st) : launch_fwd_dh<float>(a, st);
+}

@@ -1,0 +1,111 @@
+"""One WHALE fusion layer driven through the C ABI.
+
+This only allocates buffers with torch and calls the libwhalefuse entry points
+in the order of the module (gist.science Technical Summary §2.1): projections,
+jagged cross-attention, fusion MLP, shared-gate SwiGLU FFN, and their
+backward in reverse order.  No arithmetic of the module happens here.
+"""
+import torch
+
+from . import binding as wb
+
+
+def _empty(shape, dtype, dev):
+    return torch.empty(shape, dtype=dtype, device=dev)
+
+
+def _ws(nbytes, dev):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=dev)
+
+
+class FusionLayer:
+    """Weights are torch device tensors in the layer's dtype (W_Q, W_K, W_V,
+    W_F, W_U, W_D); norm parameters are fp32 (g_q, b_q, g_kv, b_kv, g_f, b_f)."""
+
+    def __init__(self, params, C, n_q, h, norm=wb.NORM_LAYER, eps=1e-5, act=wb.ACT_SILU, gate=wb.GATE_SHARED,
+                 ffn=True, scale=0.0):
+        self.p = params
+        self.C, self.n_q, self.h = C, n_q, h
+        self.norm, self.eps, self.act, self.gate, self.ffn = norm, eps, act, gate, ffn
+        self.scale = scale
+        self.d = params["W_Q"].shape[0]
+        self.H = params["W_D"].shape[1]
+        self.ctx = None
+
+    def dims(self, H_w, max_L, total_L):
+        B = H_w.shape[0] // (self.C * self.n_q)
+        return wb.dims(B, self.C, self.n_q, self.d, self.h, max_L, total_L)
+
+    def forward(self, H_w, H_s, offsets, max_L, save=True, stream=None):
+        p, dev, dt = self.p, H_w.device, H_w.dtype
+        M, T, d = H_w.shape[0], H_s.shape[0], self.d
+        dm = self.dims(H_w, max_L, T)
+        nn = self.norm != wb.NORM_NONE
+        Q, K, V = _empty((M, d), dt, dev), _empty((T, d), dt, dev), _empty((T, d), dt, dev)
+        sq = _empty((M, 2), torch.float32, dev) if nn else None
+        skv = _empty((T, 2), torch.float32, dev) if nn else None
+        wb.whale_proj_qkv(dm, H_w, H_s, self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"], p["W_Q"],
+                          p["W_K"], p["W_V"], Q, K, V, sq, skv, stream)
+        A, lse = _empty((M, d), dt, dev), _empty((M, self.h), torch.float32, dev)
+        wb.whale_jagged_xattn_fwd(dm, Q, K, V, offsets, self.scale, A, lse, stream)
+        F = _empty((M, d), dt, dev)
+        Z = _empty((M, d), dt, dev) if (save and self.act == wb.ACT_SILU) else None
+        wb.whale_fusion_mlp(dm, A, H_w, p["W_F"], self.act, F, Z, stream)
+        out = dict(Q=Q, K=K, V=V, A=A, lse=lse, F=F, Z=Z, stats_q=sq, stats_kv=skv)
+        if self.ffn:
+            H = self.H
+            Hu = 2 * H if self.gate == wb.GATE_SEPARATE else H
+            Y = _empty((M, d), dt, dev)
+            U = _empty((M, Hu), dt, dev) if save else None
+            sf = _empty((M, 2), torch.float32, dev) if nn else None
+            ws = _ws(wb.whale_swiglu_ffn_workspace_size(dm, wb._dtype_code(F), self.gate, H), dev)
+            wb.whale_swiglu_ffn(dm, F, self.norm, self.eps, p["g_f"], p["b_f"], p["W_U"], self.gate, H, p["W_D"], Y, U,
+                                sf, ws, stream)
+            out.update(Y=Y, U=U, stats_f=sf)
+        else:
+            out["Y"] = F
+        if save:
+            self.ctx = dict(out, H_w=H_w, H_s=H_s, offsets=offsets, dims=dm)
+        return out
+
+    def backward(self, dY, stream=None):
+        c, p = self.ctx, self.p
+        if c is None:
+            raise RuntimeError("forward(save=True) must run before backward")
+        dm, dev, dt = c["dims"], dY.device, dY.dtype
+        code = wb._dtype_code(dY)
+        M, d = dY.shape
+        T = c["H_s"].shape[0]
+        g = {}
+        if self.ffn:
+            dF = _empty((M, d), dt, dev)
+            g["dW_U"] = _empty(tuple(p["W_U"].shape), torch.float32, dev)
+            g["dW_D"] = _empty(tuple(p["W_D"].shape), torch.float32, dev)
+            g["dg_f"], g["db_f"] = _empty((d,), torch.float32, dev), _empty((d,), torch.float32, dev)
+            ws = _ws(wb.whale_swiglu_ffn_bwd_workspace_size(dm, code, self.gate, self.H), dev)
+            wb.whale_swiglu_ffn_bwd(dm, c["F"], self.norm, self.eps, p["g_f"], p["b_f"], c["stats_f"], p["W_U"],
+                                    self.gate, self.H, p["W_D"], c["U"], dY, dF, g["dW_U"], g["dW_D"], g["dg_f"],
+                                    g["db_f"], ws, stream)
+        else:
+            dF = dY
+        dA, dHw_mlp = _empty((M, d), dt, dev), _empty((M, d), dt, dev)
+        g["dW_F"] = _empty(tuple(p["W_F"].shape), torch.float32, dev)
+        ws = _ws(wb.whale_fusion_mlp_bwd_workspace_size(dm, code), dev)
+        wb.whale_fusion_mlp_bwd(dm, c["A"], c["H_w"], p["W_F"], self.act, c["Z"], dF, dA, dHw_mlp, g["dW_F"], ws,
+                                stream)
+        dQ, dK, dV = _empty((M, d), dt, dev), _empty((T, d), dt, dev), _empty((T, d), dt, dev)
+        ws = _ws(wb.whale_jagged_xattn_bwd_workspace_size(dm, code), dev)
+        wb.whale_jagged_xattn_bwd(dm, c["Q"], c["K"], c["V"], c["offsets"], self.scale, c["A"], c["lse"], dA, dQ, dK,
+                                  dV, ws, stream)
+        g["dH_w"], g["dH_s"] = _empty((M, d), dt, dev), _empty((T, d), dt, dev)
+        for k in ("dW_Q", "dW_K", "dW_V"):
+            g[k] = _empty((d, d), torch.float32, dev)
+        for k in ("dg_q", "db_q", "dg_kv", "db_kv"):
+            g[k] = _empty((d,), torch.float32, dev)
+        ws = _ws(wb.whale_proj_qkv_bwd_workspace_size(dm, code), dev)
+        wb.whale_proj_qkv_bwd(dm, c["H_w"], c["H_s"], self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"],
+                              c["stats_q"], c["stats_kv"], p["W_Q"], p["W_K"], p["W_V"], dQ, dK, dV, dHw_mlp,
+                              g["dH_w"], g["dH_s"], g["dW_Q"], g["dW_K"], g["dW_V"], g["dg_q"], g["db_q"], g["dg_kv"],
+                              g["db_kv"], ws, stream)
+        g.update(dA=dA, dQ=dQ, dK=dK, dV=dV, dF=dF)
+        return g

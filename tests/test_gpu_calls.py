@@ -1,0 +1,262 @@
+"""GPU parity of every C-ABI call against the fp64 oracle, element by element,
+at sizes the oracle finishes in seconds that still span several tiles and a
+ragged tail (history lengths 0, 1, 63, 64, 65, 257, ...; query blocks with a
+partial last block).  Tolerance: relative Frobenius error <= 1e-5 (fp32) and
+<= 2e-2 (bf16), max-abs error printed."""
+import numpy as np
+import pytest
+import torch
+
+from candidate_conditioned_sequence_amd import binding as wb
+from candidate_conditioned_sequence_amd import synth
+from oracle import whale_oracle as O
+from tests.util import assert_close, f32_dev, host, i64_dev, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def draw(seed, shape, dtype, scale=1.0):
+    x = np.random.default_rng(seed).standard_normal(shape).astype(np.float32) * scale
+    return synth.round_bf16(x) if dtype == "bf16" else x
+
+
+def weights(seed, out_f, in_f, dtype):
+    a = np.sqrt(6.0 / (in_f + out_f))
+    w = np.random.default_rng(seed).uniform(-a, a, (out_f, in_f)).astype(np.float32)
+    return synth.round_bf16(w) if dtype == "bf16" else w
+
+
+def offsets(lengths):
+    return synth.offsets_of(lengths)
+
+
+XATTN_CASES = [
+    # dtype, d, h, C, n_q, lengths
+    ("f32", 64, 2, 4, 8, [256]),
+    ("f32", 128, 2, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 128, 4, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 256, 4, 20, 15, [130, 1, 700, 64]),
+    ("bf16", 256, 4, 64, 32, [1000, 333]),
+    ("bf16", 512, 8, 8, 16, [97, 640]),
+    ("f32", 128, 2, 40, 8, [300, 5]),
+]
+
+
+@pytest.mark.parametrize("case", XATTN_CASES, ids=lambda c: f"{c[0]}-d{c[1]}h{c[2]}-C{c[3]}nq{c[4]}-L{c[5]}")
+def test_xattn_fwd(gpu, case):
+    dtype, d, h, C, n_q, L = case
+    print(f"\n[xattn_fwd] {case}", flush=True)
+    B = len(L)
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Q, K, V = draw(1, (M, d), dtype), draw(2, (T, d), dtype), draw(3, (T, d), dtype)
+    A_ref, lse_ref = O.xattn_fwd(Q, K, V, off, C, n_q, h)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tQ, tK, tV = to_dev(Q, dtype, gpu), to_dev(K, dtype, gpu), to_dev(V, dtype, gpu)
+    A = torch.full_like(tQ, float("nan"))
+    lse = torch.full((M, h), float("nan"), device=gpu)
+    wb.whale_jagged_xattn_fwd(dm, tQ, tK, tV, i64_dev(off, gpu), 0.0, A, lse)
+    torch.cuda.synchronize()
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(host(lse)), fin), "empty-history rows must give lse = -inf exactly"
+    assert np.all(host(lse)[~fin] == -np.inf)
+    assert_close("A", A, A_ref, dtype)
+    got = host(lse)
+    assert_close("lse", got[fin], lse_ref[fin], dtype, factor=0.1)
+
+
+@pytest.mark.parametrize("dtype,norm", [("f32", O.NORM_LAYER), ("bf16", O.NORM_LAYER), ("bf16", O.NORM_RMS),
+                                        ("f32", O.NORM_NONE)])
+def test_proj_qkv(gpu, dtype, norm):
+    print(f"\n[proj_qkv] {dtype} norm={norm}", flush=True)
+    B, C, n_q, d, h, L = 3, 5, 7, 128, 2, [0, 200, 77]
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Hw, Hs = draw(4, (M, d), dtype, 2.0) + 0.5, draw(5, (T, d), dtype)
+    Wq, Wk, Wv = (weights(s, d, d, dtype) for s in (6, 7, 8))
+    g = 1 + 0.2 * draw(9, (2, d), "f32")
+    bt = 0.2 * draw(10, (2, d), "f32")
+    Qr, Kr, Vr = O.proj_qkv(Hw, Hs, norm, 1e-5, g[0], bt[0], g[1], bt[1], Wq, Wk, Wv)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    Q, K, V = (torch.empty((n, d), dtype=to_dev(Hw[:1], dtype, gpu).dtype, device=gpu) for n in (M, T, T))
+    sq, skv = torch.empty((M, 2), device=gpu), torch.empty((T, 2), device=gpu)
+    wb.whale_proj_qkv(dm, to_dev(Hw, dtype, gpu), to_dev(Hs, dtype, gpu), norm, 1e-5, f32_dev(g[0], gpu),
+                      f32_dev(bt[0], gpu), f32_dev(g[1], gpu), f32_dev(bt[1], gpu), to_dev(Wq, dtype, gpu),
+                      to_dev(Wk, dtype, gpu), to_dev(Wv, dtype, gpu), Q, K, V, sq, skv)
+    torch.cuda.synchronize()
+    for name, got, ref in (("Q", Q, Qr), ("K", K, Kr), ("V", V, Vr)):
+        assert_close(name, got, ref, dtype)
+
+
+@pytest.mark.parametrize("dtype,act", [("f32", O.ACT_SILU), ("bf16", O.ACT_SILU), ("bf16", O.ACT_NONE)])
+def test_fusion_mlp(gpu, dtype, act):
+    print(f"\n[fusion_mlp] {dtype} act={act}", flush=True)
+    M, d = 300, 256
+    A, Hw = draw(11, (M, d), dtype), draw(12, (M, d), dtype)
+    Wf = weights(13, d, 2 * d, dtype)
+    F_ref, Z_ref = O.fusion_mlp(A, Hw, Wf, act)
+    dm = wb.dims(1, M, 1, d, 4, 0, 0)
+    tA = to_dev(A, dtype, gpu)
+    F, Z = torch.empty_like(tA), torch.empty_like(tA)
+    wb.whale_fusion_mlp(dm, tA, to_dev(Hw, dtype, gpu), to_dev(Wf, dtype, gpu), act, F, Z)
+    torch.cuda.synchronize()
+    assert_close("F", F, F_ref, dtype)
+    if act == O.ACT_SILU:
+        assert_close("Z", Z, Z_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype,gate,norm,d", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128),
+                                               ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256),
+                                               ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128),
+                                               ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64)])
+def test_swiglu_ffn(gpu, dtype, gate, norm, d):
+    print(f"\n[swiglu_ffn] {dtype} gate={gate} norm={norm} d={d}", flush=True)
+    M, H = 200, 4 * d
+    Fm = draw(14, (M, d), dtype)
+    Wu = weights(15, (2 if gate == O.GATE_SEPARATE else 1) * H, d, dtype)
+    Wd = weights(16, d, H, dtype)
+    g, bt = 1 + 0.2 * draw(17, (d,), "f32"), 0.2 * draw(18, (d,), "f32")
+    Y_ref, U_ref = O.swiglu_ffn(Fm, norm, 1e-5, g, bt, Wu, gate, Wd)
+    dm = wb.dims(1, M, 1, d, d // 64 if d >= 64 else 1, 0, 0)
+    tF = to_dev(Fm, dtype, gpu)
+    Y = torch.empty_like(tF)
+    U = torch.empty((M, Wu.shape[0]), dtype=tF.dtype, device=gpu)
+    sf = torch.empty((M, 2), device=gpu)
+    ws = torch.empty(wb.whale_swiglu_ffn_workspace_size(dm, wb._dtype_code(tF), gate, H), dtype=torch.uint8,
+                     device=gpu)
+    wb.whale_swiglu_ffn(dm, tF, norm, 1e-5, f32_dev(g, gpu), f32_dev(bt, gpu), to_dev(Wu, dtype, gpu), gate, H,
+                        to_dev(Wd, dtype, gpu), Y, U, sf, ws)
+    torch.cuda.synchronize()
+    assert_close("Y", Y, Y_ref, dtype)
+    assert_close("U", U, U_ref, dtype)
+
+
+BWD_CASES = [
+    ("f32", 64, 2, 4, 8, [256]),
+    ("f32", 128, 2, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 128, 4, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 256, 4, 20, 15, [130, 1, 700, 64]),
+    ("bf16", 256, 4, 64, 32, [900, 333]),
+]
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=lambda c: f"{c[0]}-d{c[1]}h{c[2]}-C{c[3]}nq{c[4]}-L{c[5]}")
+def test_xattn_bwd(gpu, case):
+    dtype, d, h, C, n_q, L = case
+    print(f"\n[xattn_bwd] {case}", flush=True)
+    B = len(L)
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Q, K, V, dA = draw(21, (M, d), dtype), draw(22, (T, d), dtype), draw(23, (T, d), dtype), draw(24, (M, d), dtype)
+    dQ_ref, dK_ref, dV_ref = O.xattn_bwd(Q, K, V, off, C, n_q, h, None, dA)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tQ, tK, tV, tdA = (to_dev(x, dtype, gpu) for x in (Q, K, V, dA))
+    toff = i64_dev(off, gpu)
+    A, lse = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    wb.whale_jagged_xattn_fwd(dm, tQ, tK, tV, toff, 0.0, A, lse)
+    dQ, dK, dV = torch.empty_like(tQ), torch.empty_like(tK), torch.empty_like(tV)
+    ws = torch.empty(wb.whale_jagged_xattn_bwd_workspace_size(dm, wb._dtype_code(tQ)), dtype=torch.uint8, device=gpu)
+    wb.whale_jagged_xattn_bwd(dm, tQ, tK, tV, toff, 0.0, A, lse, tdA, dQ, dK, dV, ws)
+    torch.cuda.synchronize()
+    assert_close("dQ", dQ, dQ_ref, dtype)
+    assert_close("dK", dK, dK_ref, dtype)
+    assert_close("dV", dV, dV_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype,act", [("f32", O.ACT_SILU), ("bf16", O.ACT_SILU), ("bf16", O.ACT_NONE)])
+def test_fusion_mlp_bwd(gpu, dtype, act):
+    print(f"\n[fusion_mlp_bwd] {dtype} act={act}", flush=True)
+    M, d = 300, 128
+    A, Hw, dF = draw(31, (M, d), dtype), draw(32, (M, d), dtype), draw(33, (M, d), dtype)
+    Wf = weights(34, d, 2 * d, dtype)
+    dA_ref, dHw_ref, dWf_ref = O.fusion_mlp_bwd(A, Hw, Wf, act, dF)
+    _, Z = O.fusion_mlp(A, Hw, Wf, act)
+    dm = wb.dims(1, M, 1, d, 2, 0, 0)
+    tA, tHw, tWf = to_dev(A, dtype, gpu), to_dev(Hw, dtype, gpu), to_dev(Wf, dtype, gpu)
+    F, tZ = torch.empty_like(tA), torch.empty_like(tA)
+    wb.whale_fusion_mlp(dm, tA, tHw, tWf, act, F, tZ if act == O.ACT_SILU else None)
+    dA, dHw = torch.empty_like(tA), torch.empty_like(tA)
+    dWf = torch.empty((d, 2 * d), device=gpu)
+    ws = torch.empty(wb.whale_fusion_mlp_bwd_workspace_size(dm, wb._dtype_code(tA)), dtype=torch.uint8, device=gpu)
+    wb.whale_fusion_mlp_bwd(dm, tA, tHw, tWf, act, tZ if act == O.ACT_SILU else None, to_dev(dF, dtype, gpu), dA,
+                            dHw, dWf, ws)
+    torch.cuda.synchronize()
+    assert_close("dA", dA, dA_ref, dtype)
+    assert_close("dH_w", dHw, dHw_ref, dtype)
+    assert_close("dW_F", dWf, dWf_ref, dtype)
+
+
+@pytest.mark.parametrize("dtype,gate,norm", [("f32", O.GATE_SHARED, O.NORM_LAYER),
+                                             ("bf16", O.GATE_SHARED, O.NORM_LAYER),
+                                             ("bf16", O.GATE_SEPARATE, O.NORM_RMS),
+                                             ("f32", O.GATE_SEPARATE, O.NORM_NONE)])
+def test_swiglu_ffn_bwd(gpu, dtype, gate, norm):
+    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm}", flush=True)
+    M, d = 300, 128
+    H = 4 * d
+    Fm, dY = draw(41, (M, d), dtype), draw(42, (M, d), dtype)
+    Wu = weights(43, (2 if gate == O.GATE_SEPARATE else 1) * H, d, dtype)
+    Wd = weights(44, d, H, dtype)
+    g, bt = 1 + 0.2 * draw(45, (d,), "f32"), 0.2 * draw(46, (d,), "f32")
+    ref = O.swiglu_ffn_bwd(Fm, norm, 1e-5, g, bt, Wu, gate, Wd, dY)
+    dm = wb.dims(1, M, 1, d, 2, 0, 0)
+    tF, tWu, tWd = to_dev(Fm, dtype, gpu), to_dev(Wu, dtype, gpu), to_dev(Wd, dtype, gpu)
+    tg, tb = f32_dev(g, gpu), f32_dev(bt, gpu)
+    Y, U = torch.empty_like(tF), torch.empty((M, Wu.shape[0]), dtype=tF.dtype, device=gpu)
+    sf = torch.empty((M, 2), device=gpu)
+    code = wb._dtype_code(tF)
+    ws = torch.empty(wb.whale_swiglu_ffn_workspace_size(dm, code, gate, H), dtype=torch.uint8, device=gpu)
+    wb.whale_swiglu_ffn(dm, tF, norm, 1e-5, tg, tb, tWu, gate, H, tWd, Y, U, sf, ws)
+    dF = torch.empty_like(tF)
+    dWu, dWd = torch.empty(tuple(Wu.shape), device=gpu), torch.empty(tuple(Wd.shape), device=gpu)
+    dg, db = torch.empty(d, device=gpu), torch.empty(d, device=gpu)
+    ws = torch.empty(wb.whale_swiglu_ffn_bwd_workspace_size(dm, code, gate, H), dtype=torch.uint8, device=gpu)
+    wb.whale_swiglu_ffn_bwd(dm, tF, norm, 1e-5, tg, tb, sf, tWu, gate, H, tWd, U, to_dev(dY, dtype, gpu), dF, dWu,
+                            dWd, dg, db, ws)
+    torch.cuda.synchronize()
+    assert_close("dF", dF, ref["dF"], dtype)
+    assert_close("dW_U", dWu, ref["dW_U"], dtype)
+    assert_close("dW_D", dWd, ref["dW_D"], dtype)
+    if norm != O.NORM_NONE:
+        assert_close("dg_f", dg, ref["dg_f"], dtype)
+    if norm == O.NORM_LAYER:
+        assert_close("db_f", db, ref["db_f"], dtype)
+
+
+@pytest.mark.parametrize("dtype,norm", [("f32", O.NORM_LAYER), ("bf16", O.NORM_LAYER), ("bf16", O.NORM_RMS)])
+def test_proj_qkv_bwd(gpu, dtype, norm):
+    print(f"\n[proj_qkv_bwd] {dtype} norm={norm}", flush=True)
+    B, C, n_q, d, h, L = 3, 5, 7, 128, 2, [0, 200, 77]
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Hw, Hs = draw(51, (M, d), dtype), draw(52, (T, d), dtype)
+    Wq, Wk, Wv = (weights(s, d, d, dtype) for s in (53, 54, 55))
+    dQ, dK, dV, extra = draw(56, (M, d), dtype), draw(57, (T, d), dtype), draw(58, (T, d), dtype), \
+        draw(59, (M, d), dtype)
+    g = 1 + 0.2 * draw(60, (2, d), "f32")
+    bt = 0.2 * draw(61, (2, d), "f32")
+    ref = O.proj_qkv_bwd(Hw, Hs, norm, 1e-5, g[0], bt[0], g[1], bt[1], Wq, Wk, Wv, dQ, dK, dV)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tHw, tHs = to_dev(Hw, dtype, gpu), to_dev(Hs, dtype, gpu)
+    tW = [to_dev(w, dtype, gpu) for w in (Wq, Wk, Wv)]
+    tg = [f32_dev(x, gpu) for x in (g[0], bt[0], g[1], bt[1])]
+    Q, K, V = torch.empty_like(tHw), torch.empty_like(tHs), torch.empty_like(tHs)
+    sq, skv = torch.empty((M, 2), device=gpu), torch.empty((T, 2), device=gpu)
+    wb.whale_proj_qkv(dm, tHw, tHs, norm, 1e-5, *tg, *tW, Q, K, V, sq, skv)
+    dHw, dHs = torch.empty_like(tHw), torch.empty_like(tHs)
+    dW = [torch.empty((d, d), device=gpu) for _ in range(3)]
+    dgb = [torch.empty(d, device=gpu) for _ in range(4)]
+    ws = torch.empty(wb.whale_proj_qkv_bwd_workspace_size(dm, wb._dtype_code(tHw)), dtype=torch.uint8, device=gpu)
+    wb.whale_proj_qkv_bwd(dm, tHw, tHs, norm, 1e-5, *tg, sq, skv, *tW, to_dev(dQ, dtype, gpu),
+                          to_dev(dK, dtype, gpu), to_dev(dV, dtype, gpu), to_dev(extra, dtype, gpu), dHw, dHs, *dW,
+                          *dgb, ws)
+    torch.cuda.synchronize()
+    assert_close("dH_w", dHw, ref["dH_w"] + extra, dtype)
+    assert_close("dH_s", dHs, ref["dH_s"], dtype)
+    for name, got in zip(("dW_Q", "dW_K", "dW_V"), dW):
+        assert_close(name, got, ref[name], dtype)
+    assert_close("dg_q", dgb[0], ref["dg_q"], dtype)
+    assert_close("dg_kv", dgb[2], ref["dg_kv"], dtype)
+    if norm == O.NORM_LAYER:
+        assert_close("db_q", dgb[1], ref["db_q"], dtype)
+        assert_close("db_kv", dgb[3], ref["db_kv"], dtype)

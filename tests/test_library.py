@@ -1,0 +1,79 @@
+"""CPU checks of the C ABI: the library loads, exports every symbol the header
+declares, and rejects bad arguments on the host before enqueueing anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from candidate_conditioned_sequence_amd import binding as wb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "whalefuse.h")
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(whale_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_and_binding_agree():
+    assert header_functions() == sorted(wb.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = wb.load()
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    assert wb.version().count(".") == 2
+
+
+def test_status_strings():
+    for code, name in enumerate(wb.STATUS):
+        assert wb.status_string(code).startswith(name)
+
+
+def _dims(**kw):
+    base = dict(B=2, C=4, n_q=8, d=128, h=2, max_L=100, total_L=150)
+    base.update(kw)
+    return wb.dims(**base)
+
+
+def test_host_validation_rejects_before_launch():
+    lib = wb.load()
+    fake = ctypes.c_void_p(256)      # never dereferenced: validation fails first
+    d = _dims()
+    # NULL dims, bad dtype
+    assert lib.whale_jagged_xattn_fwd(None, 1, fake, fake, fake, fake, 0.0, fake, None, None) == 1
+    assert lib.whale_jagged_xattn_fwd(ctypes.byref(d), 7, fake, fake, fake, fake, 0.0, fake, None, None) == 3
+    # NULL required pointer
+    assert lib.whale_jagged_xattn_fwd(ctypes.byref(d), 1, None, fake, fake, fake, 0.0, fake, None, None) == 1
+    # d % h != 0, shape hints inconsistent, negative scale
+    for bad in (_dims(h=3), _dims(max_L=200, total_L=150), _dims(max_L=10, total_L=150), _dims(B=0)):
+        assert lib.whale_jagged_xattn_fwd(ctypes.byref(bad), 1, fake, fake, fake, fake, 0.0, fake, None, None) == 2
+    assert lib.whale_jagged_xattn_fwd(ctypes.byref(d), 1, fake, fake, fake, fake, -1.0, fake, None, None) == 2
+    # unsupported head width (d_h = 128) and width above 512
+    for bad in (_dims(d=256, h=2), _dims(d=1024, h=16)):
+        assert lib.whale_jagged_xattn_fwd(ctypes.byref(bad), 1, fake, fake, fake, fake, 0.0, fake, None, None) == 4
+    # FFN hidden width not a multiple of 64, workspace too small
+    assert lib.whale_swiglu_ffn(ctypes.byref(d), 1, fake, 0, 1e-5, fake, fake, fake, 0, 100, fake, fake, None, fake,
+                                fake, 1 << 30, None) == 4
+    assert lib.whale_swiglu_ffn(ctypes.byref(d), 1, fake, 0, 1e-5, fake, fake, fake, 0, 512, fake, fake, None, fake,
+                                fake, 16, None) == 5
+    # LayerNorm without its statistics buffer
+    assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 0, 1e-5, fake, fake, fake, fake, fake, fake, fake, fake,
+                              fake, fake, None, fake, None) == 1
+
+
+def test_workspace_sizes_are_host_only_and_monotone():
+    lib = wb.load()
+    small, big = _dims(), _dims(B=8, total_L=600)
+    for fn in ("whale_jagged_xattn_bwd_workspace_size", "whale_fusion_mlp_bwd_workspace_size",
+               "whale_proj_qkv_bwd_workspace_size"):
+        f = getattr(lib, fn)
+        a, b = f(ctypes.byref(small), 1), f(ctypes.byref(big), 1)
+        assert 0 < a <= b, fn
+    assert lib.whale_swiglu_ffn_bwd_workspace_size(ctypes.byref(small), 1, 0, 512) > 0
+    assert lib.whale_swiglu_ffn_workspace_size(ctypes.byref(small), 1, 1, 512) == \
+        lib.whale_swiglu_ffn_workspace_size(ctypes.byref(small), 1, 0, 512)
