@@ -30,7 +30,7 @@ whale_status_t check_dims(const whale_dims_t* dims, whale_dtype_t dtype, Shape* 
   if (x.total_L > (int64_t)x.B * x.max_L) return WHALE_ERR_SHAPE;
   const int dh = x.d / x.h;
   if (dh != 32 && dh != 64) return WHALE_ERR_UNSUPPORTED;
-  if (x.d > 512) return WHALE_ERR_UNSUPPORTED;
+  if (x.d != 64 && x.d != 128 && x.d != 256 && x.d != 512) return WHALE_ERR_UNSUPPORTED;
   s->M = M;
   s->T = x.total_L;
   s->B = x.B; s->C = x.C; s->n_q = x.n_q; s->d = x.d; s->h = x.h; s->dh = dh;
@@ -73,6 +73,7 @@ GemmArgs gemm_defaults() {
   GemmArgs a;
   std::memset(&a, 0, sizeof(a));
   a.norm_kind = 2;
+  a.nsplit = 1 << 30;
   return a;
 }
 
@@ -83,21 +84,43 @@ WgradArgs wgrad_defaults() {
   return a;
 }
 
-size_t wgrad_partial_bytes(int64_t M, int N, int K) {
-  const int s = wgrad_splits(M, N, K);
-  return s > 1 ? (size_t)s * N * K * 4 : 0;
+size_t wgrad_partial_bytes(int64_t M, int N, int K, bool dual = false) {
+  const int sp = wgrad_splits(M, N, K);
+  return (sp > 1 || dual) ? (size_t)sp * N * K * 4 : 0;
 }
 
-hipError_t wgrad(const void* G, int ldg, const void* X, int ldx, int pro, int64_t M, int N, int K, float* dW,
-                 float* partial, bool bf16, hipStream_t st, const float* stats = nullptr,
-                 const float* gamma = nullptr, const float* beta = nullptr, int norm_kind = 2,
-                 const void* X2 = nullptr, int ldx2 = 0, int ksplit = 0, int gate_H = 0) {
-  WgradArgs a = wgrad_defaults();
-  a.G = G; a.ldg = ldg; a.X = X; a.ldx = ldx; a.X2 = X2; a.ldx2 = ldx2; a.ksplit = ksplit;
-  a.stats = stats; a.gamma = gamma; a.beta = beta; a.norm_kind = norm_kind; a.gate_H = gate_H;
-  a.dW = dW; a.partial = partial; a.M = M; a.N = N; a.K = K; a.splits = wgrad_splits(M, N, K); a.pro = pro;
-  if (pro == WPRO_NORM && norm_kind == 2) a.pro = WPRO_PLAIN;
-  return launch_wgrad(a, bf16, st);
+struct Wg {
+  WgradArgs a;
+  Wg(const void* G, int ldg, const void* X, int ldx, int pro, int64_t M, int N, int K, float* dW, float* partial) {
+    a = wgrad_defaults();
+    a.G = G; a.ldg = ldg; a.X = X; a.ldx = ldx; a.pro = pro;
+    a.M = M; a.N = N; a.K = K; a.dW = dW; a.partial = partial; a.splits = wgrad_splits(M, N, K);
+  }
+  Wg& norm(const float* stats, const float* g, const float* b, int kind) {
+    a.stats = stats; a.gamma = g; a.beta = b; a.norm_kind = kind;
+    if (kind == 2 && a.pro == WPRO_NORM) a.pro = WPRO_PLAIN;
+    return *this;
+  }
+  Wg& concat(const void* X2, int ldx2, int ksplit) { a.X2 = X2; a.ldx2 = ldx2; a.ksplit = ksplit; return *this; }
+  Wg& dual(const void* G2, int nsplit, float* dW2) { a.G2 = G2; a.nsplit = nsplit; a.dW2 = dW2; return *this; }
+  Wg& gz(const void* Z) { a.Gz = Z; return *this; }
+  Wg& gate(int H) { a.gate_H = H; return *this; }
+  hipError_t run(bool bf, hipStream_t st) { return launch_wgrad(a, bf, st); }
+};
+
+size_t norm_part_bytes(int64_t M, int d) { return (size_t)gemm_norm_bwd_tiles(M) * 2 * d * 4; }
+
+// dX = dY W (as an NT GEMM with the pre-transposed weight Wt [K_out, N_in]) followed,
+// in the same kernel, by the norm backward: out = Norm backward(dX) + R.
+hipError_t norm_bwd_gemm(const void* dY, int ldy_in, const void* dY2, int ksplit, const void* Wt, int ldw, int K,
+                         const void* nx, const float* stats, const float* gamma, int norm_kind, const void* R,
+                         void* out, float* part, int64_t M, int d, bool bf, hipStream_t st) {
+  GemmArgs g = gemm_defaults();
+  g.X = dY; g.ldx = ldy_in; g.X2 = dY2; g.ldx2 = ldy_in; g.ksplit = ksplit;
+  g.W = Wt; g.ldw = ldw; g.Y = out; g.ldy = d; g.R = R; g.ldr = d;
+  g.nx = nx; g.stats = stats; g.gamma = gamma; g.norm_kind = norm_kind; g.part = part;
+  g.M = M; g.N = d; g.K = K; g.pro = dY2 ? PRO_CONCAT : PRO_PLAIN; g.epi = EPI_NORM_BWD;
+  return launch_gemm_nt(g, bf, st);
 }
 
 }  // namespace
@@ -148,8 +171,8 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
     // K and V in one pass over H_s: weight rows [0, d) from W_K, [d, 2d) from W_V.
     GemmArgs b = a;
     b.X = H_s; b.stats = stats_kv; b.gamma = g_kv; b.beta = b_kv;
-    b.W = W_K; b.Y = K; b.M = s.T; b.N = 2 * s.d;
-    WHALE_TRY(launch_gemm_nt_dual(b, s.d, W_V, V, bf, stream));
+    b.W = W_K; b.W2 = W_V; b.nsplit = s.d; b.Y = K; b.Y2 = V; b.M = s.T; b.N = 2 * s.d;
+    WHALE_TRY(launch_gemm_nt(b, bf, stream));
   }
   return WHALE_OK;
 }
@@ -269,8 +292,7 @@ size_t whale_fusion_mlp_bwd_workspace_size(const whale_dims_t* dims, whale_dtype
   Shape s;
   if (check_dims(dims, dtype, &s) != WHALE_OK) return 0;
   Carve c(nullptr);
-  c.take((size_t)s.M * s.d * esz(dtype));            // dZ
-  c.take((size_t)2 * s.d * s.d * esz(dtype));        // W_F^T
+  c.take((size_t)2 * s.d * s.d * esz(dtype));        // W_F^T [2d, d]
   c.take(wgrad_partial_bytes(s.M, s.d, 2 * s.d));
   return c.used;
 }
@@ -286,23 +308,22 @@ whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   if (act == WHALE_ACT_SILU && !Z_saved) return WHALE_ERR_NULL;
   if (ws_bytes < whale_fusion_mlp_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
   const bool bf = dtype == WHALE_BF16;
+  const bool silu = act == WHALE_ACT_SILU;
   const int d = s.d;
   Carve c(workspace);
-  void* dZ = c.take((size_t)s.M * d * esz(dtype));
   void* WFt = c.take((size_t)2 * d * d * esz(dtype));
   float* part = (float*)c.take(wgrad_partial_bytes(s.M, d, 2 * d));
-  WHALE_TRY(launch_dact(dF, Z_saved, dZ, s.M * d, (int)act, bf, stream));
-  WHALE_TRY(launch_transpose(W_F, d, 2 * d, WFt, d, 0, bf, stream));   // [2d, d]
-  // dW_F = dZ^T [A, H_w]
-  WHALE_TRY(wgrad(dZ, d, A, d, WPRO_CONCAT, s.M, d, 2 * d, dW_F, part, bf, stream, nullptr, nullptr, nullptr, 2,
-                  H_w, d, d));
-  // dA = dZ W_F[:, :d]  ;  dH_w = dF + dZ W_F[:, d:]
+  // dW_F = dZ^T [A, H_w], dZ = dF * act'(Z) formed in the loader.
+  Wg w(dF, d, A, d, WPRO_CONCAT, s.M, d, 2 * d, dW_F, part);
+  w.concat(H_w, d, d);
+  if (silu) w.gz(Z_saved);
+  WHALE_TRY(w.run(bf, stream));
+  // [dA | dH_w - dF] = dZ W_F: one GEMM against W_F^T [2d, d]; columns >= d get the residual dF.
+  WHALE_TRY(launch_transpose(W_F, d, 2 * d, WFt, d, 0, bf, stream));
   GemmArgs g = gemm_defaults();
-  g.X = dZ; g.ldx = d; g.W = WFt; g.ldw = d; g.Y = dA; g.ldy = d; g.M = s.M; g.N = d; g.K = d;
-  g.pro = PRO_PLAIN; g.epi = EPI_STORE;
-  WHALE_TRY(launch_gemm_nt(g, bf, stream));
-  g.W = (const char*)WFt + (size_t)d * d * esz(dtype);
-  g.Y = dH_w; g.R = dF; g.ldr = d; g.epi = EPI_RESID;
+  g.X = dF; g.ldx = d; g.X2 = Z_saved; g.ldx2 = d;
+  g.W = WFt; g.ldw = d; g.Y = dA; g.Y2 = dH_w; g.ldy = d; g.nsplit = d; g.R = dF; g.ldr = d;
+  g.M = s.M; g.N = 2 * d; g.K = d; g.pro = silu ? PRO_DACT : PRO_PLAIN; g.epi = EPI_DUAL_RESID2;
   return ret(launch_gemm_nt(g, bf, stream));
 }
 
@@ -315,10 +336,10 @@ size_t whale_swiglu_ffn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype
   c.take((size_t)H * s.d * esz(dtype));              // W_D^T [H, d]
   c.take((size_t)s.M * Hu * esz(dtype));             // dU
   c.take((size_t)s.d * Hu * esz(dtype));             // W_U^T [d, Hu]
-  c.take((size_t)s.M * s.d * 4);                     // dX_f fp32
   const size_t p1 = wgrad_partial_bytes(s.M, s.d, H), p2 = wgrad_partial_bytes(s.M, Hu, s.d);
   c.take(p1 > p2 ? p1 : p2);
-  c.take((size_t)norm_bwd_blocks(s.M) * 2 * s.d * 4);
+  c.take(norm_part_bytes(s.M, s.d));
+  c.take((size_t)colsum_scratch_floats(s.d) * 4);
   return c.used;
 }
 
@@ -339,19 +360,19 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   if (ws_bytes < whale_swiglu_ffn_bwd_workspace_size(dims, dtype, gate, H)) return WHALE_ERR_WORKSPACE;
   const bool bf = dtype == WHALE_BF16;
   const bool sep = gate == WHALE_GATE_SEPARATE;
-  const int d = s.d, Hu = sep ? 2 * H : H;
+  const int d = s.d, Hu = sep ? 2 * H : H, nk = (int)norm;
   Carve c(workspace);
   void* WDt = c.take((size_t)H * d * esz(dtype));
   void* dU = c.take((size_t)s.M * Hu * esz(dtype));
   void* WUt = c.take((size_t)d * Hu * esz(dtype));
-  float* dXf = (float*)c.take((size_t)s.M * d * 4);
   const size_t p1 = wgrad_partial_bytes(s.M, d, H), p2 = wgrad_partial_bytes(s.M, Hu, d);
   float* part = (float*)c.take(p1 > p2 ? p1 : p2);
-  float* npart = (float*)c.take((size_t)norm_bwd_blocks(s.M) * 2 * d * 4);
+  float* npart = (float*)c.take(norm_part_bytes(s.M, d));
+  float* cscr = (float*)c.take((size_t)colsum_scratch_floats(d) * 4);
 
   // dW_D = dY^T G, with G recomputed from U in the loader.
-  WHALE_TRY(wgrad(dY, d, U_saved, Hu, sep ? WPRO_GATE_SEP : WPRO_GATE_TIED, s.M, d, H, dW_D, part, bf, stream,
-                  nullptr, nullptr, nullptr, 2, nullptr, 0, 0, H));
+  Wg w1(dY, d, U_saved, Hu, sep ? WPRO_GATE_SEP : WPRO_GATE_TIED, s.M, d, H, dW_D, part);
+  WHALE_TRY(w1.gate(H).run(bf, stream));
   // dU = (dY W_D) * gate'(U)
   WHALE_TRY(launch_transpose(W_D, d, H, WDt, d, 0, bf, stream));       // [H, d]
   GemmArgs g = gemm_defaults();
@@ -359,18 +380,14 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   g.M = s.M; g.N = H; g.K = d; g.pro = PRO_PLAIN; g.epi = sep ? EPI_DGATE_SEP : EPI_DGATE_TIED;
   WHALE_TRY(launch_gemm_nt(g, bf, stream));
   // dW_U = dU^T Norm_f(F)
-  WHALE_TRY(wgrad(dU, Hu, F, d, WPRO_NORM, s.M, Hu, d, dW_U, part, bf, stream, stats_f, g_f, b_f, (int)norm));
-  // dX_f = dU W_U (fp32)
+  Wg w2(dU, Hu, F, d, WPRO_NORM, s.M, Hu, d, dW_U, part);
+  WHALE_TRY(w2.norm(stats_f, g_f, b_f, nk).run(bf, stream));
+  // dF = dY + Norm_f backward(dU W_U), one kernel.
   WHALE_TRY(launch_transpose(W_U, Hu, d, WUt, Hu, 0, bf, stream));     // [d, Hu]
-  GemmArgs x = gemm_defaults();
-  x.X = dU; x.ldx = Hu; x.W = WUt; x.ldw = Hu; x.Y = dXf; x.ldy = d; x.y_f32 = true;
-  x.M = s.M; x.N = d; x.K = Hu; x.pro = PRO_PLAIN; x.epi = EPI_STORE;
-  WHALE_TRY(launch_gemm_nt(x, bf, stream));
-  // dF = dY + Norm_f backward(dX_f)
-  int nblk = 0;
-  WHALE_TRY(launch_norm_bwd(F, stats_f, g_f, dXf, dY, dF, npart, s.M, d, (int)norm, bf, &nblk, stream));
+  WHALE_TRY(norm_bwd_gemm(dU, Hu, nullptr, 0, WUt, Hu, Hu, F, stats_f, g_f, nk, dY, dF, npart, s.M, d, bf, stream));
   if (norm != WHALE_NORM_NONE)
-    WHALE_TRY(launch_colsum_reduce(npart, nblk, d, dg_f, norm == WHALE_NORM_LAYER ? db_f : nullptr, stream));
+    WHALE_TRY(launch_colsum_reduce(npart, gemm_norm_bwd_tiles(s.M), d, dg_f,
+                                   norm == WHALE_NORM_LAYER ? db_f : nullptr, cscr, stream));
   if (norm == WHALE_NORM_RMS && db_f) WHALE_TRY(launch_fill_zero(db_f, d, stream));
   return WHALE_OK;
 }
@@ -381,12 +398,11 @@ size_t whale_proj_qkv_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t
   Carve c(nullptr);
   c.take((size_t)s.d * s.d * esz(dtype));            // W_Q^T
   c.take((size_t)2 * s.d * s.d * esz(dtype));        // [W_K^T | W_V^T]
-  c.take((size_t)s.M * s.d * 4);                     // dX_q
-  c.take((size_t)s.T * s.d * 4);                     // dX_s
-  const size_t p1 = wgrad_partial_bytes(s.M, s.d, s.d), p2 = wgrad_partial_bytes(s.T, s.d, s.d);
+  const size_t p1 = wgrad_partial_bytes(s.M, s.d, s.d), p2 = wgrad_partial_bytes(s.T, 2 * s.d, s.d, true);
   c.take(p1 > p2 ? p1 : p2);
-  c.take((size_t)norm_bwd_blocks(s.M) * 2 * s.d * 4);
-  c.take((size_t)norm_bwd_blocks(s.T) * 2 * s.d * 4);
+  c.take(norm_part_bytes(s.M, s.d));
+  c.take(norm_part_bytes(s.T, s.d));
+  c.take((size_t)colsum_scratch_floats(s.d) * 4);
   return c.used;
 }
 
@@ -414,44 +430,38 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
   Carve c(workspace);
   void* WQt = c.take((size_t)d * d * esz(dtype));
   void* WKVt = c.take((size_t)2 * d * d * esz(dtype));
-  float* dXq = (float*)c.take((size_t)s.M * d * 4);
-  float* dXs = (float*)c.take((size_t)s.T * d * 4);
-  const size_t p1 = wgrad_partial_bytes(s.M, d, d), p2 = wgrad_partial_bytes(s.T, d, d);
+  const size_t p1 = wgrad_partial_bytes(s.M, d, d), p2 = wgrad_partial_bytes(s.T, 2 * d, d, true);
   float* part = (float*)c.take(p1 > p2 ? p1 : p2);
-  float* npq = (float*)c.take((size_t)norm_bwd_blocks(s.M) * 2 * d * 4);
-  float* npk = (float*)c.take((size_t)norm_bwd_blocks(s.T) * 2 * d * 4);
+  float* npq = (float*)c.take(norm_part_bytes(s.M, d));
+  float* npk = (float*)c.take(norm_part_bytes(s.T, d));
+  float* cscr = (float*)c.take((size_t)colsum_scratch_floats(d) * 4);
 
-  // Weight gradients with the normalised inputs recomputed in the loader.
-  WHALE_TRY(wgrad(dQ, d, H_w, d, WPRO_NORM, s.M, d, d, dW_Q, part, bf, stream, stats_q, g_q, b_q, nk));
+  // Weight gradients with the normalised inputs recomputed in the loader;
+  // dW_K and dW_V share one pass over H_s.
+  Wg wq(dQ, d, H_w, d, WPRO_NORM, s.M, d, d, dW_Q, part);
+  WHALE_TRY(wq.norm(stats_q, g_q, b_q, nk).run(bf, stream));
   if (s.T > 0) {
-    WHALE_TRY(wgrad(dK, d, H_s, d, WPRO_NORM, s.T, d, d, dW_K, part, bf, stream, stats_kv, g_kv, b_kv, nk));
-    WHALE_TRY(wgrad(dV, d, H_s, d, WPRO_NORM, s.T, d, d, dW_V, part, bf, stream, stats_kv, g_kv, b_kv, nk));
+    Wg wkv(dK, d, H_s, d, WPRO_NORM, s.T, 2 * d, d, dW_K, part);
+    WHALE_TRY(wkv.norm(stats_kv, g_kv, b_kv, nk).dual(dV, d, dW_V).run(bf, stream));
   } else {
     WHALE_TRY(launch_fill_zero(dW_K, (int64_t)d * d, stream));
     WHALE_TRY(launch_fill_zero(dW_V, (int64_t)d * d, stream));
   }
-  // dX_q = dQ W_Q ; dX_s = [dK, dV] [W_K ; W_V]
+  // dH_w = Norm_q backward(dQ W_Q) + dH_w_in ; dH_s = Norm_kv backward([dK, dV] [W_K; W_V])
   WHALE_TRY(launch_transpose(W_Q, d, d, WQt, d, 0, bf, stream));
-  WHALE_TRY(launch_transpose(W_K, d, d, WKVt, 2 * d, 0, bf, stream));
-  WHALE_TRY(launch_transpose(W_V, d, d, WKVt, 2 * d, d, bf, stream));
-  GemmArgs g = gemm_defaults();
-  g.X = dQ; g.ldx = d; g.W = WQt; g.ldw = d; g.Y = dXq; g.ldy = d; g.y_f32 = true;
-  g.M = s.M; g.N = d; g.K = d; g.pro = PRO_PLAIN; g.epi = EPI_STORE;
-  WHALE_TRY(launch_gemm_nt(g, bf, stream));
-  if (s.T > 0) {
-    GemmArgs k = g;
-    k.X = dK; k.X2 = dV; k.ldx2 = d; k.ksplit = d; k.W = WKVt; k.ldw = 2 * d; k.Y = dXs;
-    k.M = s.T; k.K = 2 * d; k.pro = PRO_CONCAT;
-    WHALE_TRY(launch_gemm_nt(k, bf, stream));
-  }
-  int nb = 0;
-  WHALE_TRY(launch_norm_bwd(H_w, stats_q, g_q, dXq, dH_w_in, dH_w, npq, s.M, d, nk, bf, &nb, stream));
+  WHALE_TRY(norm_bwd_gemm(dQ, d, nullptr, 0, WQt, d, d, H_w, stats_q, g_q, nk, dH_w_in, dH_w, npq, s.M, d, bf,
+                          stream));
   if (norm != WHALE_NORM_NONE)
-    WHALE_TRY(launch_colsum_reduce(npq, nb, d, dg_q, norm == WHALE_NORM_LAYER ? db_q : nullptr, stream));
+    WHALE_TRY(launch_colsum_reduce(npq, gemm_norm_bwd_tiles(s.M), d, dg_q,
+                                   norm == WHALE_NORM_LAYER ? db_q : nullptr, cscr, stream));
   if (s.T > 0) {
-    WHALE_TRY(launch_norm_bwd(H_s, stats_kv, g_kv, dXs, nullptr, dH_s, npk, s.T, d, nk, bf, &nb, stream));
+    WHALE_TRY(launch_transpose(W_K, d, d, WKVt, 2 * d, 0, bf, stream));
+    WHALE_TRY(launch_transpose(W_V, d, d, WKVt, 2 * d, d, bf, stream));
+    WHALE_TRY(norm_bwd_gemm(dK, d, dV, d, WKVt, 2 * d, 2 * d, H_s, stats_kv, g_kv, nk, nullptr, dH_s, npk, s.T, d,
+                            bf, stream));
     if (norm != WHALE_NORM_NONE)
-      WHALE_TRY(launch_colsum_reduce(npk, nb, d, dg_kv, norm == WHALE_NORM_LAYER ? db_kv : nullptr, stream));
+      WHALE_TRY(launch_colsum_reduce(npk, gemm_norm_bwd_tiles(s.T), d, dg_kv,
+                                     norm == WHALE_NORM_LAYER ? db_kv : nullptr, cscr, stream));
   } else if (norm != WHALE_NORM_NONE) {
     WHALE_TRY(launch_fill_zero(dg_kv, d, stream));
     if (db_kv) WHALE_TRY(launch_fill_zero(db_kv, d, stream));

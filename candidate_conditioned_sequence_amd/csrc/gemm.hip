@@ -2,17 +2,21 @@
 //
 //  * gemm_nt: Y[M,N] = op(X)[M,K] W[N,K]^T.  Both operands are
 //    K-contiguous, so the 32x32x16 MFMA operands are 16-byte rows of the LDS
-//    tiles.  The X tile loader can apply the row norm (stats + gamma/beta)
-//    or read the concatenation [X | X2]; W rows may come from two matrices
-//    (K and V projections in one pass over H_s, or the gate and up halves of
-//    a separate-gate SwiGLU side by side).  Epilogues fuse the residual,
-//    SiLU, the shared-gate SwiGLU product G = SiLU(U) U (gist.science
-//    Technical Summary §2.2; paper-daily.com deep reading §2), and the
-//    gate derivatives of the backward.
-//  * wgrad: dW[N,K] = sum_m G[m,n] X[m,k] (the weight gradients).  The
-//    contraction runs over rows of both operands, so both tiles are stored
-//    transposed in LDS.  M is split into fixed chunks whose fp32 partials a
-//    second kernel sums in a fixed order: deterministic, no atomics.
+//    tiles.  The X tile loader can apply the row norm (stats + gamma/beta),
+//    read the concatenation [X | X2], or form dZ = dF * SiLU'(Z) on the fly.
+//    W rows may come from two matrices (K and V projections in one pass over
+//    H_s; gate and up halves of a separate-gate SwiGLU side by side).
+//    The accumulators are staged through LDS so that the epilogue reads its
+//    other operands and writes its outputs in 16-byte coalesced chunks; the
+//    epilogue fuses the residual, SiLU, the shared-gate SwiGLU product
+//    G = SiLU(U) U (gist.science Technical Summary §2.2; paper-daily.com deep
+//    reading §2), the gate derivatives, and -- for tiles that span whole rows
+//    -- the norm backward, so dX never goes to memory.
+//  * wgrad: dW[N,K] = sum_m G[m,n] X[m,k].  The contraction runs over the
+//    rows of both operands.  Each thread loads an 8x8 block, transposes it in
+//    registers and writes eight 16-byte rows of the transposed LDS tile.  M is
+//    split into fixed chunks whose fp32 partials a second kernel sums in a
+//    fixed order: deterministic, no atomics.
 #include <type_traits>
 
 #include "common.h"
@@ -20,218 +24,438 @@
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32, LDT = BK + 8;
-
 template <typename T>
 WHALE_DEV x8_t<T> norm8(const x8_t<T>& v, float mean, float rstd, const float* g, const float* bt, int kind) {
+  const f32x4 g0 = *reinterpret_cast<const f32x4*>(g), g1 = *reinterpret_cast<const f32x4*>(g + 4);
+  f32x4 b0 = {0.f, 0.f, 0.f, 0.f}, b1 = b0;
+  if (kind == 0) { b0 = *reinterpret_cast<const f32x4*>(bt); b1 = *reinterpret_cast<const f32x4*>(bt + 4); }
   x8_t<T> o;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    float x = (to_f(v[u]) - mean) * rstd * g[u];
-    if (kind == 0) x += bt[u];
-    o[u] = from_f<T>(x);
+  for (int u = 0; u < 4; ++u) {
+    o[u] = from_f<T>((to_f(v[u]) - mean) * rstd * g0[u] + b0[u]);
+    o[u + 4] = from_f<T>((to_f(v[u + 4]) - mean) * rstd * g1[u] + b1[u]);
   }
   return o;
 }
 
-template <typename T, int PRO, int EPI, bool YF32>
-__global__ __launch_bounds__(256, 2) void gemm_nt_kernel(GemmArgs a, int tiles_n, int ntiles, int nsplit,
-                                                         const T* __restrict__ W2, void* __restrict__ Y2) {
-  __shared__ __attribute__((aligned(32))) T As[2][BM * LDT];
-  __shared__ __attribute__((aligned(32))) T Bs[2][BN * LDT];
-  typedef typename std::conditional<YF32, float, T>::type YT;
+template <typename T>
+WHALE_DEV x8_t<T> dact8(const x8_t<T>& g, const x8_t<T>& z) {
+  x8_t<T> o;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) o[u] = from_f<T>(to_f(g[u]) * dsiluf_(to_f(z[u])));
+  return o;
+}
 
-  const int lid = xcd_remap(blockIdx.x, ntiles);
-  const int tn = lid % tiles_n, tm = lid / tiles_n;
-  const int64_t m0 = (int64_t)tm * BM;
-  const int n0 = tn * BN;
+template <typename T> WHALE_DEV void ld8f(const T* p, float* f) {
+  const x8_t<T> v = ld8<T>(p);
+#pragma unroll
+  for (int u = 0; u < 8; ++u) f[u] = to_f(v[u]);
+}
+template <typename T> WHALE_DEV void st8f(T* p, const float* f) {
+  x8_t<T> v;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = from_f<T>(f[u]);
+  st8<T>(p, v);
+}
+
+// ------------------------------------------------------------------ gemm_nt
+// Persistent kernel: each workgroup walks a strided list of BM x BN output
+// tiles inside its XCD's contiguous tile range (so the column tiles of one row
+// block meet in one L2), BK-deep K steps double-buffered in LDS, one wave per
+// 64x64 sub-tile.  The first K step of the next tile is loaded into registers
+// before the epilogue of the current one, so its latency hides behind the
+// epilogue.  The fp32 accumulators are staged through LDS, SROWS rows at a
+// time, for coalesced 16-byte epilogue accesses.
+template <typename T, int PRO, int EPI, bool YF32, int BM, int BN, int BK>
+__global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(GemmArgs a, int tiles_n, int ntiles) {
+  constexpr int NWN = BN / 64, NWM = BM / 64, NT = NWM * NWN * 64;
+  constexpr int LDT = BK + 8;                 // LDS tile row stride (elements)
+  constexpr int SLD = BN + 4;                 // staging row stride (floats)
+  constexpr int CPR = BK / 8;                 // 8-element chunks per tile row
+  constexpr int ACH = (BM * CPR + NT - 1) / NT, BCH = (BN * CPR + NT - 1) / NT;   // chunks per thread
+  static_assert((BM * CPR) % 64 == 0 && (BN * CPR) % NT == 0, "tile/threads");
+  // Row-complete tiles (norm backward) stage the whole tile; others 64 rows per pass.
+  constexpr int SROWS = (EPI == EPI_NORM_BWD) ? BM : 64;
+  constexpr int TILE_BYTES = 2 * (BM + BN) * LDT * (int)sizeof(T);
+  constexpr int STG_BYTES = SROWS * SLD * 4;
+  __shared__ __attribute__((aligned(32))) char smem[TILE_BYTES > STG_BYTES ? TILE_BYTES : STG_BYTES];
+  T* As = reinterpret_cast<T*>(smem);                    // [2][BM*LDT]
+  T* Bs = As + 2 * BM * LDT;                             // [2][BN*LDT]
+  float* stg = reinterpret_cast<float*>(smem);           // [SROWS][SLD], between K loops
+  typedef typename std::conditional<YF32, float, T>::type YT;
+  // Norm prologue: gamma / beta of the K columns (K = d <= 512) held in LDS.
+  __shared__ __attribute__((aligned(16))) float sgb[PRO == PRO_NORM ? 2 * 512 : 4];
+  if (PRO == PRO_NORM) {
+    for (int k = threadIdx.x; k < a.K && k < 512; k += blockDim.x) {
+      sgb[k] = a.norm_kind != 2 ? a.gamma[k] : 1.f;
+      sgb[512 + k] = a.norm_kind == 0 ? a.beta[k] : 0.f;
+    }
+    __syncthreads();
+  }
+
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / NWN, wn = w % NWN;
   const int64_t M = a.M;
   const int N = a.N, K = a.K;
   const T* X = (const T*)a.X;
   const T* X2 = (const T*)a.X2;
   const T* W = (const T*)a.W;
+  const T* W2 = (const T*)a.W2;
   const int Hs = N / 2;   // EPI_GATE_SEP: number of gate rows
-
-  // Loader assignment: 2 chunks of 8 elements per thread per operand.
-  int arow[2], ak0[2];
-  float amean[2], arstd[2];
-  const T* brow_ptr[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int ch = tid + 256 * i;
-    arow[i] = ch >> 2;
-    ak0[i] = 8 * (ch & 3);
-    const int64_t m = m0 + arow[i];
-    amean[i] = 0.f;
-    arstd[i] = 1.f;
-    if (PRO == PRO_NORM && m < M && a.norm_kind != 2) {
-      amean[i] = a.stats[2 * m];
-      arstd[i] = a.stats[2 * m + 1];
-    }
-    // weight row for tile row arow[i]
-    const int tr = arow[i];
-    int n;
-    if (EPI == EPI_GATE_SEP) {
-      const int wn_ = tr >> 6, jj = (tr >> 5) & 1, rr = tr & 31;
-      n = n0 / 2 + wn_ * 32 + rr;                 // output column
-      brow_ptr[i] = (n < Hs) ? W + (int64_t)(jj ? Hs + n : n) * a.ldw : nullptr;
-    } else {
-      n = n0 + tr;
-      if (n >= N) brow_ptr[i] = nullptr;
-      else if (W2 != nullptr && n >= nsplit) brow_ptr[i] = W2 + (int64_t)(n - nsplit) * a.ldw;
-      else brow_ptr[i] = W + (int64_t)n * a.ldw;
-    }
-  }
-
-  x8_t<T> ar[2], br[2];
-  auto load = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int64_t m = m0 + arow[i];
-      const int k = k0 + ak0[i];
-      if (m < M) {
-        if (PRO == PRO_CONCAT && k >= a.ksplit) ar[i] = ld8<T>(X2 + m * a.ldx2 + (k - a.ksplit));
-        else ar[i] = ld8<T>(X + m * a.ldx + k);
-        if (PRO == PRO_NORM && a.norm_kind != 2)
-          ar[i] = norm8<T>(ar[i], amean[i], arstd[i], a.gamma + k, a.beta + k, a.norm_kind);
-      } else {
-        ar[i] = zero8<T>();
-      }
-      br[i] = brow_ptr[i] ? ld8<T>(brow_ptr[i] + k) : zero8<T>();
-    }
-  };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      st8<T>(&As[buf][arow[i] * LDT + ak0[i]], ar[i]);
-      st8<T>(&Bs[buf][arow[i] * LDT + ak0[i]], br[i]);
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
-
-  const int nk = K / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      x8_t<T> af[2], bf[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = ld8<T>(&As[buf][(wm * 64 + 32 * i + l32) * LDT + 16 * ks + 8 * hh]);
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) bf[jj] = ld8<T>(&Bs[buf][(wn * 64 + 32 * jj + l32) * LDT + 16 * ks + 8 * hh]);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) mma32(acc[i][jj], af[i], bf[jj]);
-    }
-    if (kt + 1 < nk) store(buf ^ 1);
-    __syncthreads();
-  }
-
-  // Epilogue.
   YT* Y = (YT*)a.Y;
   const T* R = (const T*)a.R;
   T* Z = (T*)a.Z;
+
+  // This workgroup's tiles: XCD x = blockIdx % 8 owns [x n / 8, (x+1) n / 8).
+  const int G = gridDim.x, xcd = blockIdx.x & 7, rnk = blockIdx.x >> 3;
+  const int gx = (G - xcd + 7) >> 3;
+  const int t_lo = (int)((int64_t)xcd * ntiles / 8), t_hi = (int)((int64_t)(xcd + 1) * ntiles / 8);
+
+  float amean[ACH], arstd[ACH];
+  const T* aptr[ACH];
+  const T* aptr2[ACH];
+  const T* bptr[BCH];
+  // PIPE K steps in flight in registers (slot = K step mod PIPE).
+  constexpr int PIPE = 2;
+  x8_t<T> ar[PIPE][ACH], br[PIPE][BCH];
+
+  auto setup = [&](int tile) {
+    const int tn = tile % tiles_n, tm = tile / tiles_n;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int n0 = tn * BN;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < ACH; ++i) {
+      const int ch = tid + NT * i;
+      const int64_t m = m0 + ch / CPR;
+      const bool ok = m < M && ch < BM * CPR;
+      amean[i] = 0.f;
+      arstd[i] = 1.f;
+      if (PRO == PRO_NORM && ok && a.norm_kind != 2) { amean[i] = a.stats[2 * m]; arstd[i] = a.stats[2 * m + 1]; }
+      aptr[i] = ok ? X + m * a.ldx + 8 * (ch % CPR) : nullptr;
+      aptr2[i] = (ok && X2) ? X2 + m * a.ldx2 + 8 * (ch % CPR) : nullptr;
+    }
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t m = m0 + wm * 64 + 32 * i + acc_row(r, hh);
-      if (m >= M) continue;
+    for (int i = 0; i < BCH; ++i) {
+      const int ch = tid + NT * i;
+      const int tr = ch / CPR;
+      const T* p = nullptr;
       if (EPI == EPI_GATE_SEP) {
-        const int n = n0 / 2 + wn * 32 + l32;
-        if (n >= Hs) continue;
-        const float g = acc[i][0][r], u = acc[i][1][r];
-        Y[m * a.ldy + n] = from_f<YT>(siluf_(g) * u);
-        if (Z) { Z[m * a.ldz + n] = from_f<T>(g); Z[m * a.ldz + Hs + n] = from_f<T>(u); }
-        continue;
+        // tile rows [64 v, 64 v + 32) gate rows, [64 v + 32, 64 v + 64) up rows, same output columns
+        const int n = n0 / 2 + (tr >> 6) * 32 + (tr & 31);
+        if (n < Hs) p = W + (int64_t)(((tr >> 5) & 1) ? Hs + n : n) * a.ldw;
+      } else {
+        const int n = n0 + tr;
+        if (n < N) p = (W2 != nullptr && n >= a.nsplit) ? W2 + (int64_t)(n - a.nsplit) * a.ldw : W + (int64_t)n * a.ldw;
       }
+      bptr[i] = p ? p + 8 * (ch % CPR) : nullptr;
+    }
+  };
+  // Raw loads of one K step into a slot; the prologue math (norm, dZ) is
+  // applied when the slot is written to LDS, so the loads stay in flight.
+  auto load = [&](int slot, int k0) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int n = n0 + wn * 64 + 32 * jj + l32;
-        if (n >= N) continue;
-        const float v = acc[i][jj][r];
-        if (EPI == EPI_STORE) {
-          if (Y2 != nullptr && n >= nsplit) ((YT*)Y2)[m * a.ldy + (n - nsplit)] = from_f<YT>(v);
-          else Y[m * a.ldy + n] = from_f<YT>(v);
-        } else if (EPI == EPI_RESID) {
-          Y[m * a.ldy + n] = from_f<YT>(to_f(R[m * a.ldr + n]) + v);
-        } else if (EPI == EPI_SILU_RESID) {
-          Y[m * a.ldy + n] = from_f<YT>(to_f(R[m * a.ldr + n]) + siluf_(v));
-          if (Z) Z[m * a.ldz + n] = from_f<T>(v);
-        } else if (EPI == EPI_GATE_TIED) {
-          Y[m * a.ldy + n] = from_f<YT>(siluf_(v) * v);
-          if (Z) Z[m * a.ldz + n] = from_f<T>(v);
-        } else if (EPI == EPI_DGATE_TIED) {
-          const float u = to_f(Z[m * a.ldz + n]);
-          Y[m * a.ldy + n] = from_f<YT>(v * (dsiluf_(u) * u + siluf_(u)));
-        } else if (EPI == EPI_DGATE_SEP) {
-          const float ug = to_f(Z[m * a.ldz + n]), uu = to_f(Z[m * a.ldz + N + n]);
-          Y[m * a.ldy + n] = from_f<YT>(v * uu * dsiluf_(ug));
-          Y[m * a.ldy + N + n] = from_f<YT>(v * siluf_(ug));
+    for (int i = 0; i < ACH; ++i) {
+      if (aptr[i] == nullptr) { ar[slot][i] = zero8<T>(); continue; }
+      if (PRO == PRO_CONCAT && k0 >= a.ksplit) ar[slot][i] = ld8<T>(aptr2[i] + (k0 - a.ksplit));
+      else ar[slot][i] = ld8<T>(aptr[i] + k0);
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) br[slot][i] = bptr[i] ? ld8<T>(bptr[i] + k0) : zero8<T>();
+  };
+  auto store = [&](int slot, int buf, int k0) {
+#pragma unroll
+    for (int i = 0; i < ACH; ++i) {
+      const int ch = tid + NT * i;
+      if (ch >= BM * CPR) continue;
+      x8_t<T> v = ar[slot][i];
+      if (aptr[i] != nullptr) {
+        if (PRO == PRO_DACT) {
+          v = dact8<T>(v, ld8<T>(aptr2[i] + k0));
+        } else if (PRO == PRO_NORM && a.norm_kind != 2) {
+          const int k = k0 + 8 * (ch % CPR);
+          v = norm8<T>(v, amean[i], arstd[i], &sgb[k], &sgb[512 + k], 0);
         }
       }
+      st8<T>(&As[buf * BM * LDT + (ch / CPR) * LDT + 8 * (ch % CPR)], v);
+    }
+#pragma unroll
+    for (int i = 0; i < BCH; ++i) {
+      const int ch = tid + NT * i;
+      st8<T>(&Bs[buf * BN * LDT + (ch / CPR) * LDT + 8 * (ch % CPR)], br[slot][i]);
+    }
+  };
+  auto prefetch_tile = [&](int t) {
+    setup(t);
+#pragma unroll
+    for (int u = 0; u < PIPE; ++u)
+      if (u * BK < a.K) load(u, u * BK);
+  };
+
+  const int nk = K / BK;
+  int tile = t_lo + rnk;
+  if (tile < t_hi) prefetch_tile(tile);
+
+  for (; tile < t_hi; tile += gx) {
+    const int tn = tile % tiles_n, tm = tile / tiles_n;
+    const int64_t m0 = (int64_t)tm * BM;
+    const int n0 = tn * BN;
+    store(0, 0, 0);
+    __syncthreads();
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
+    for (int kt0 = 0; kt0 < nk; kt0 += PIPE) {
+#pragma unroll
+      for (int u = 0; u < PIPE; ++u) {
+        const int kt = kt0 + u;
+        if (kt < nk) {
+          const int buf = kt & 1;
+          // slot u (K step kt) is in LDS now: refill it with K step kt + PIPE
+          if (kt + PIPE < nk) load(u, (kt + PIPE) * BK);
+          const T* At = As + buf * BM * LDT;
+          const T* Bt = Bs + buf * BN * LDT;
+#pragma unroll
+          for (int ks = 0; ks < BK / 16; ++ks) {
+            x8_t<T> af[2], bf[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) af[i] = ld8<T>(&At[(wm * 64 + 32 * i + l32) * LDT + 16 * ks + 8 * hh]);
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) bf[jj] = ld8<T>(&Bt[(wn * 64 + 32 * jj + l32) * LDT + 16 * ks + 8 * hh]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int jj = 0; jj < 2; ++jj) mma32(acc[i][jj], af[i], bf[jj]);
+          }
+          if (kt + 1 < nk) store((u + 1) % PIPE, buf ^ 1, (kt + 1) * BK);
+          __syncthreads();
+        }
+      }
+    }
+    // The next tile's first K steps go in flight during this epilogue.
+    if (tile + gx < t_hi) prefetch_tile(tile + gx);
+
+    for (int pass = 0; pass < BM / SROWS; ++pass) {
+      // Stage rows [pass*SROWS, (pass+1)*SROWS) of the tile (fp32).
+      if (SROWS == BM || wm == pass) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              stg[(wm * 64 - pass * SROWS + 32 * i + acc_row(r, hh)) * SLD + wn * 64 + 32 * jj + l32] = acc[i][jj][r];
+      }
+      __syncthreads();
+      const int64_t r0 = m0 + pass * SROWS;
+
+      if (EPI == EPI_NORM_BWD) {
+        // The tile spans whole rows (BN >= N).  A group of N/8 lanes owns a row.
+        constexpr int LPRmax = BN / 8;
+        const int LPR = N / 8;                      // lanes per row (power of two, <= 64)
+        const int rpp = 64 / LPR;                   // rows per wave pass
+        const int sub = lane / LPR, cl = lane % LPR;
+        const int c0 = 8 * cl;
+        float pg[8], pb[8], gmm[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { pg[u] = 0.f; pb[u] = 0.f; gmm[u] = a.norm_kind == 2 ? 1.f : a.gamma[c0 + u]; }
+        const float invn = 1.f / N;
+        for (int rb = w * rpp; rb < SROWS; rb += (NT / 64) * rpp) {
+          const int row = rb + sub;
+          const int64_t m = r0 + row;
+          const bool ok = m < M;
+          float dxn[8], xh[8];
+          float mean = 0.f, rstd = 1.f;
+          if (ok && a.norm_kind != 2) { mean = a.stats[2 * m]; rstd = a.stats[2 * m + 1]; }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) dxn[u] = stg[row * SLD + c0 + u];
+          if (ok) ld8f<T>((const T*)a.nx + m * N + c0, xh);
+          else for (int u = 0; u < 8; ++u) xh[u] = 0.f;
+          float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            xh[u] = (xh[u] - mean) * rstd;
+            const float gd = ok ? dxn[u] * gmm[u] : 0.f;
+            s1 += gd;
+            s2 += gd * xh[u];
+            if (ok) { pg[u] += dxn[u] * xh[u]; pb[u] += dxn[u]; }
+          }
+#pragma unroll
+          for (int o = 1; o < LPRmax; o <<= 1)
+            if (o < LPR) { s1 += __shfl_xor(s1, o); s2 += __shfl_xor(s2, o); }
+          s1 *= invn;
+          s2 *= invn;
+          if (a.norm_kind != 0) s1 = 0.f;
+          if (ok) {
+            float o8[8];
+            if (R) ld8f<T>(R + m * a.ldr + c0, o8);
+            else for (int u = 0; u < 8; ++u) o8[u] = 0.f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              o8[u] += a.norm_kind == 2 ? dxn[u] : rstd * (dxn[u] * gmm[u] - s1 - xh[u] * s2);
+            st8f<YT>(Y + m * a.ldy + c0, o8);
+          }
+        }
+        // Column partials of dgamma / dbeta over this tile's rows, fixed order.
+        __syncthreads();
+        float* red = stg;   // [NT/64 * rpp][2][N]
+        const int slot = w * rpp + sub;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { red[(slot * 2 + 0) * N + c0 + u] = pg[u]; red[(slot * 2 + 1) * N + c0 + u] = pb[u]; }
+        __syncthreads();
+        const int nslots = (NT / 64) * rpp;
+        for (int c = tid; c < 2 * N; c += NT) {
+          const int which = c / N, col = c % N;
+          float sacc = 0.f;
+          for (int q = 0; q < nslots; ++q) sacc += red[(q * 2 + which) * N + col];
+          a.part[(int64_t)tm * 2 * N + c] = sacc;
+        }
+      } else {
+        // Generic epilogue: 8-column chunks, coalesced 16-byte accesses.
+        constexpr int OUTC = (EPI == EPI_GATE_SEP) ? BN / 2 : BN;   // output columns per tile
+        constexpr int CH = SROWS * OUTC / 8;
+        for (int c = tid; c < CH; c += NT) {
+          const int row = c / (OUTC / 8), col = 8 * (c % (OUTC / 8));
+          const int64_t m = r0 + row;
+          if (m >= M) continue;
+          float v[8];
+          if (EPI == EPI_GATE_SEP) {
+            const int n = n0 / 2 + col;
+            if (n >= Hs) continue;
+            const int sc = (col / 32) * 64 + (col % 32);
+            float u8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) { v[u] = stg[row * SLD + sc + u]; u8[u] = stg[row * SLD + sc + 32 + u]; }
+            float g8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) g8[u] = siluf_(v[u]) * u8[u];
+            st8f<YT>(Y + m * a.ldy + n, g8);
+            if (Z) { st8f<T>(Z + m * a.ldz + n, v); st8f<T>(Z + m * a.ldz + Hs + n, u8); }
+            continue;
+          }
+          const int n = n0 + col;
+          if (n >= N) continue;
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = stg[row * SLD + col + u];
+          if (EPI == EPI_STORE) {
+            if (a.Y2 != nullptr && n >= a.nsplit) st8f<YT>((YT*)a.Y2 + m * a.ldy + (n - a.nsplit), v);
+            else st8f<YT>(Y + m * a.ldy + n, v);
+          } else if (EPI == EPI_RESID) {
+            float r8[8];
+            ld8f<T>(R + m * a.ldr + n, r8);
+            for (int u = 0; u < 8; ++u) r8[u] += v[u];
+            st8f<YT>(Y + m * a.ldy + n, r8);
+          } else if (EPI == EPI_DUAL_RESID2) {
+            if (n < a.nsplit) {
+              st8f<YT>(Y + m * a.ldy + n, v);
+            } else {
+              float r8[8];
+              ld8f<T>(R + m * a.ldr + (n - a.nsplit), r8);
+              for (int u = 0; u < 8; ++u) r8[u] += v[u];
+              st8f<YT>((YT*)a.Y2 + m * a.ldy + (n - a.nsplit), r8);
+            }
+          } else if (EPI == EPI_SILU_RESID) {
+            float r8[8];
+            ld8f<T>(R + m * a.ldr + n, r8);
+            for (int u = 0; u < 8; ++u) r8[u] += siluf_(v[u]);
+            st8f<YT>(Y + m * a.ldy + n, r8);
+            if (Z) st8f<T>(Z + m * a.ldz + n, v);
+          } else if (EPI == EPI_GATE_TIED) {
+            float g8[8];
+            for (int u = 0; u < 8; ++u) g8[u] = siluf_(v[u]) * v[u];
+            st8f<YT>(Y + m * a.ldy + n, g8);
+            if (Z) st8f<T>(Z + m * a.ldz + n, v);
+          } else if (EPI == EPI_DGATE_TIED) {
+            float u8[8];
+            ld8f<T>(Z + m * a.ldz + n, u8);
+            for (int u = 0; u < 8; ++u) v[u] *= dsiluf_(u8[u]) * u8[u] + siluf_(u8[u]);
+            st8f<YT>(Y + m * a.ldy + n, v);
+          } else if (EPI == EPI_DGATE_SEP) {
+            float ug[8], uu[8], o1[8], o2[8];
+            ld8f<T>(Z + m * a.ldz + n, ug);
+            ld8f<T>(Z + m * a.ldz + N + n, uu);
+            for (int u = 0; u < 8; ++u) { o1[u] = v[u] * uu[u] * dsiluf_(ug[u]); o2[u] = v[u] * siluf_(ug[u]); }
+            st8f<YT>(Y + m * a.ldy + n, o1);
+            st8f<YT>(Y + m * a.ldy + N + n, o2);
+          }
+        }
+      }
+      __syncthreads();
     }
   }
 }
 
-template <typename T, int PRO, int EPI>
-hipError_t gemm_go(const GemmArgs& a, hipStream_t st, int nsplit, const void* W2, void* Y2) {
-  const int Nrows = a.N;     // rows of W (2H for EPI_GATE_SEP)
-  const int tiles_n = (Nrows + BN - 1) / BN;
+// Resident workgroups per CU for the persistent launch (bounded by LDS and registers).
+constexpr int kCUs = 256;
+
+template <typename T, int PRO, int EPI, int BM, int BN, int BK>
+hipError_t gemm_go(const GemmArgs& a, hipStream_t st) {
+  const int tiles_n = (a.N + BN - 1) / BN;
   const int64_t tiles_m = (a.M + BM - 1) / BM;
   const int64_t nt = tiles_m * tiles_n;
   if (nt == 0) return hipSuccess;
+  if (nt > (int64_t)1 << 30) return hipErrorInvalidValue;
+  constexpr int NT = (BM / 64) * (BN / 64) * 64;
+  constexpr int LDT = BK + 8, SLD = BN + 4;
+  constexpr int SROWS = (EPI == EPI_NORM_BWD) ? BM : 64;
+  constexpr int lds = (2 * (BM + BN) * LDT * (int)sizeof(T) > SROWS * SLD * 4) ? 2 * (BM + BN) * LDT * (int)sizeof(T)
+                                                                               : SROWS * SLD * 4;
+  constexpr int per_cu_lds = 160 * 1024 / lds;
+  constexpr int per_cu_thr = 2048 / NT;
+  constexpr int per_cu = per_cu_lds < per_cu_thr ? (per_cu_lds < 3 ? per_cu_lds : 3) : (per_cu_thr < 3 ? per_cu_thr : 3);
+  int64_t g = (int64_t)kCUs * (per_cu > 0 ? per_cu : 1);
+  if (g > nt) g = nt;
+  g = (g + 7) / 8 * 8;                       // every XCD gets workgroups
   if (a.y_f32)
-    hipLaunchKernelGGL((gemm_nt_kernel<T, PRO, EPI, true>), dim3((unsigned)nt), dim3(256), 0, st, a, tiles_n, (int)nt,
-                       nsplit, (const T*)W2, Y2);
+    hipLaunchKernelGGL((gemm_nt_kernel<T, PRO, EPI, true, BM, BN, BK>), dim3((unsigned)g), dim3(NT), 0, st, a,
+                       tiles_n, (int)nt);
   else
-    hipLaunchKernelGGL((gemm_nt_kernel<T, PRO, EPI, false>), dim3((unsigned)nt), dim3(256), 0, st, a, tiles_n, (int)nt,
-                       nsplit, (const T*)W2, Y2);
+    hipLaunchKernelGGL((gemm_nt_kernel<T, PRO, EPI, false, BM, BN, BK>), dim3((unsigned)g), dim3(NT), 0, st, a,
+                       tiles_n, (int)nt);
   return hipGetLastError();
 }
 
 template <typename T, int PRO>
-hipError_t gemm_epi(const GemmArgs& a, hipStream_t st, int nsplit, const void* W2, void* Y2) {
+hipError_t gemm_epi(const GemmArgs& a, hipStream_t st) {
   switch (a.epi) {
-    case EPI_STORE: return gemm_go<T, PRO, EPI_STORE>(a, st, nsplit, W2, Y2);
-    case EPI_RESID: return gemm_go<T, PRO, EPI_RESID>(a, st, nsplit, W2, Y2);
-    case EPI_SILU_RESID: return gemm_go<T, PRO, EPI_SILU_RESID>(a, st, nsplit, W2, Y2);
-    case EPI_GATE_TIED: return gemm_go<T, PRO, EPI_GATE_TIED>(a, st, nsplit, W2, Y2);
-    case EPI_GATE_SEP: return gemm_go<T, PRO, EPI_GATE_SEP>(a, st, nsplit, W2, Y2);
-    case EPI_DGATE_TIED: return gemm_go<T, PRO, EPI_DGATE_TIED>(a, st, nsplit, W2, Y2);
-    case EPI_DGATE_SEP: return gemm_go<T, PRO, EPI_DGATE_SEP>(a, st, nsplit, W2, Y2);
+    case EPI_STORE: return gemm_go<T, PRO, EPI_STORE, 128, 128, 32>(a, st);
+    case EPI_RESID: return gemm_go<T, PRO, EPI_RESID, 128, 128, 32>(a, st);
+    case EPI_SILU_RESID: return gemm_go<T, PRO, EPI_SILU_RESID, 128, 128, 32>(a, st);
+    case EPI_GATE_TIED: return gemm_go<T, PRO, EPI_GATE_TIED, 128, 128, 32>(a, st);
+    case EPI_GATE_SEP: return gemm_go<T, PRO, EPI_GATE_SEP, 128, 128, 32>(a, st);
+    case EPI_DGATE_TIED: return gemm_go<T, PRO, EPI_DGATE_TIED, 128, 128, 32>(a, st);
+    case EPI_DGATE_SEP: return gemm_go<T, PRO, EPI_DGATE_SEP, 128, 128, 32>(a, st);
+    case EPI_DUAL_RESID2: return gemm_go<T, PRO, EPI_DUAL_RESID2, 128, 128, 32>(a, st);
+    case EPI_NORM_BWD:
+      // Row-complete tiles (BN >= N); the K step shrinks with the tile so
+      // that the double-buffered tiles fit in LDS.
+      if (a.N <= 64) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 64, 32>(a, st);
+      if (a.N <= 128) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 128, 32>(a, st);
+      if (a.N <= 256) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 256, 32>(a, st);
+      return gemm_go<T, PRO, EPI_NORM_BWD, 64, 512, sizeof(T) == 2 ? 32 : 16>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename T>
-hipError_t gemm_pro(const GemmArgs& a, hipStream_t st, int nsplit, const void* W2, void* Y2) {
+hipError_t gemm_pro(const GemmArgs& a, hipStream_t st) {
   switch (a.pro) {
-    case PRO_PLAIN: return gemm_epi<T, PRO_PLAIN>(a, st, nsplit, W2, Y2);
-    case PRO_NORM: return gemm_epi<T, PRO_NORM>(a, st, nsplit, W2, Y2);
-    case PRO_CONCAT: return gemm_epi<T, PRO_CONCAT>(a, st, nsplit, W2, Y2);
+    case PRO_PLAIN: return gemm_epi<T, PRO_PLAIN>(a, st);
+    case PRO_NORM: return gemm_epi<T, PRO_NORM>(a, st);
+    case PRO_CONCAT: return gemm_epi<T, PRO_CONCAT>(a, st);
+    case PRO_DACT: return gemm_epi<T, PRO_DACT>(a, st);
   }
   return hipErrorInvalidValue;
 }
 
 // ------------------------------------------------------------------ wgrad
 
-constexpr int WN = 128, WK = 128, WM = 32, LDW = WM + 8;
+constexpr int WN = 128, WK = 128, WM = 64, LDW = WM + 8;
 
-template <typename T, int PRO>
-__global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a, int tiles_k, int ntiles, int64_t chunk) {
+template <typename T, int PRO, int GPRO>
+__global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, int ntiles, int64_t chunk) {
   __shared__ __attribute__((aligned(32))) T Gt[2][WN * LDW];   // [n][m]
   __shared__ __attribute__((aligned(32))) T Xt[2][WK * LDW];   // [k][m]
   const int split = blockIdx.y;
@@ -244,49 +468,72 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a, int tiles_k,
   const int64_t mb = (int64_t)split * chunk;
   const int64_t me = min(a.M, mb + chunk);
   const T* G = (const T*)a.G;
+  const T* G2 = (const T*)a.G2;
+  const T* Gz = (const T*)a.Gz;
   const T* X = (const T*)a.X;
   const T* X2 = (const T*)a.X2;
 
-  // Each thread loads 2 chunks of 8 consecutive columns of one row per operand.
-  x8_t<T> gr[2], xr[2];
+  // Threads 0..127 load 8x8 blocks of G, threads 128..255 of X.  Block b:
+  // rows 8 (b % 8) .. +8 of the m-step, columns 8 (b / 8) .. +8 of the tile.
+  const bool isG = tid < 128;
+  const int b = tid & 127, rb = 8 * (b & 7), cb = 8 * (b >> 3);
+  const int col = (isG ? n0 : k0) + cb;
+  const bool cok = col < (isG ? N : K);
+  const T* src = nullptr;     // column base of this thread's 8 columns
+  const T* srcz = nullptr;    // second operand of the prologue
+  int ld = 0;
+  if (cok) {
+    if (isG) {
+      if (G2 != nullptr && col >= a.nsplit) { src = G2 + (col - a.nsplit); }
+      else src = G + col;
+      ld = a.ldg;
+      if (GPRO == 1) srcz = Gz + col;
+    } else if (PRO == WPRO_CONCAT && col >= a.ksplit) {
+      src = X2 + (col - a.ksplit); ld = a.ldx2;
+    } else {
+      src = X + col; ld = a.ldx;
+      if (PRO == WPRO_GATE_SEP) srcz = X + a.gate_H + col;
+    }
+  }
+  float gm[8], bt[8];
+  if (!isG && PRO == WPRO_NORM && cok) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { gm[u] = a.gamma[col + u]; bt[u] = a.norm_kind == 0 ? a.beta[col + u] : 0.f; }
+  }
+
+  x8_t<T> r8[8];
   auto load = [&](int64_t mbase) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ch = tid + 256 * i;
-      const int mr = ch >> 4, c0 = 8 * (ch & 15);
-      const int64_t m = mbase + mr;
-      const bool mok = m < me;
-      const int n = n0 + c0, k = k0 + c0;
-      gr[i] = (mok && n < N) ? ld8<T>(G + m * a.ldg + n) : zero8<T>();
-      if (!mok || k >= K) { xr[i] = zero8<T>(); continue; }
-      if (PRO == WPRO_CONCAT && k >= a.ksplit) {
-        xr[i] = ld8<T>(X2 + m * a.ldx2 + (k - a.ksplit));
+    for (int i = 0; i < 8; ++i) {
+      const int64_t m = mbase + rb + i;
+      if (src == nullptr || m >= me) { r8[i] = zero8<T>(); continue; }
+      const x8_t<T> v = ld8<T>(src + m * ld);
+      if (isG) {
+        r8[i] = GPRO == 1 ? dact8<T>(v, ld8<T>(srcz + m * ld)) : v;
       } else if (PRO == WPRO_GATE_TIED) {
-        const x8_t<T> u = ld8<T>(X + m * a.ldx + k);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { const float uf = to_f(u[e]); xr[i][e] = from_f<T>(siluf_(uf) * uf); }
+        for (int e = 0; e < 8; ++e) { const float uf = to_f(v[e]); r8[i][e] = from_f<T>(siluf_(uf) * uf); }
       } else if (PRO == WPRO_GATE_SEP) {
-        const x8_t<T> ug = ld8<T>(X + m * a.ldx + k);
-        const x8_t<T> uu = ld8<T>(X + m * a.ldx + a.gate_H + k);
+        const x8_t<T> uu = ld8<T>(srcz + m * ld);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) xr[i][e] = from_f<T>(siluf_(to_f(ug[e])) * to_f(uu[e]));
+        for (int e = 0; e < 8; ++e) r8[i][e] = from_f<T>(siluf_(to_f(v[e])) * to_f(uu[e]));
+      } else if (PRO == WPRO_NORM && a.norm_kind != 2) {
+        const float mean = a.stats[2 * m], rstd = a.stats[2 * m + 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r8[i][e] = from_f<T>((to_f(v[e]) - mean) * rstd * gm[e] + bt[e]);
       } else {
-        xr[i] = ld8<T>(X + m * a.ldx + k);
-        if (PRO == WPRO_NORM && a.norm_kind != 2)
-          xr[i] = norm8<T>(xr[i], a.stats[2 * m], a.stats[2 * m + 1], a.gamma + k, a.beta + k, a.norm_kind);
+        r8[i] = v;
       }
     }
   };
   auto store = [&](int buf) {
+    T* dst = isG ? &Gt[buf][0] : &Xt[buf][0];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ch = tid + 256 * i;
-      const int mr = ch >> 4, c0 = 8 * (ch & 15);
+    for (int e = 0; e < 8; ++e) {
+      x8_t<T> t;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Gt[buf][(c0 + e) * LDW + mr] = gr[i][e];
-        Xt[buf][(c0 + e) * LDW + mr] = xr[i][e];
-      }
+      for (int i = 0; i < 8; ++i) t[i] = r8[i][e];
+      st8<T>(dst + (cb + e) * LDW + rb, t);
     }
   };
 
@@ -296,7 +543,7 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a, int tiles_k,
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
 
-  const int64_t nsteps = (me - mb + WM - 1) / WM;
+  const int64_t nsteps = me > mb ? (me - mb + WM - 1) / WM : 0;
   if (nsteps > 0) {
     load(mb);
     store(0);
@@ -321,7 +568,9 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a, int tiles_k,
     __syncthreads();
   }
 
-  float* out = a.splits > 1 ? a.partial + (int64_t)split * N * K : a.dW;
+  // A dual output (dW | dW2) always goes through the partial buffer; the
+  // reduction pass splits the rows.
+  float* out = (a.splits > 1 || a.dW2 != nullptr) ? a.partial + (int64_t)split * N * K : a.dW;
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -335,12 +584,19 @@ __global__ __launch_bounds__(256, 2) void wgrad_kernel(WgradArgs a, int tiles_k,
 }
 
 __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
-                                                           float* __restrict__ out) {
+                                                           float* __restrict__ out, float* __restrict__ out2,
+                                                           int64_t nsplit_elems) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float s = 0.f;
   for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
-  out[i] = s;
+  if (out2 != nullptr && i >= nsplit_elems) out2[i - nsplit_elems] = s;
+  else out[i] = s;
+}
+
+template <typename T, int PRO, int GPRO>
+void wgrad_launch(const WgradArgs& a, dim3 grid, int tiles_k, int nt, int64_t chunk, hipStream_t st) {
+  hipLaunchKernelGGL((wgrad_kernel<T, PRO, GPRO>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk);
 }
 
 template <typename T>
@@ -350,18 +606,23 @@ hipError_t wgrad_t(const WgradArgs& a, hipStream_t st) {
   int64_t chunk = (a.M + a.splits - 1) / a.splits;
   chunk = (chunk + WM - 1) / WM * WM;
   dim3 grid(nt, a.splits);
+  const bool gz = a.Gz != nullptr;
   switch (a.pro) {
-    case WPRO_PLAIN: hipLaunchKernelGGL((wgrad_kernel<T, WPRO_PLAIN>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk); break;
-    case WPRO_NORM: hipLaunchKernelGGL((wgrad_kernel<T, WPRO_NORM>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk); break;
-    case WPRO_CONCAT: hipLaunchKernelGGL((wgrad_kernel<T, WPRO_CONCAT>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk); break;
-    case WPRO_GATE_TIED: hipLaunchKernelGGL((wgrad_kernel<T, WPRO_GATE_TIED>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk); break;
-    case WPRO_GATE_SEP: hipLaunchKernelGGL((wgrad_kernel<T, WPRO_GATE_SEP>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk); break;
+    case WPRO_PLAIN: gz ? wgrad_launch<T, WPRO_PLAIN, 1>(a, grid, tiles_k, nt, chunk, st)
+                        : wgrad_launch<T, WPRO_PLAIN, 0>(a, grid, tiles_k, nt, chunk, st); break;
+    case WPRO_NORM: wgrad_launch<T, WPRO_NORM, 0>(a, grid, tiles_k, nt, chunk, st); break;
+    case WPRO_CONCAT: gz ? wgrad_launch<T, WPRO_CONCAT, 1>(a, grid, tiles_k, nt, chunk, st)
+                         : wgrad_launch<T, WPRO_CONCAT, 0>(a, grid, tiles_k, nt, chunk, st); break;
+    case WPRO_GATE_TIED: wgrad_launch<T, WPRO_GATE_TIED, 0>(a, grid, tiles_k, nt, chunk, st); break;
+    case WPRO_GATE_SEP: wgrad_launch<T, WPRO_GATE_SEP, 0>(a, grid, tiles_k, nt, chunk, st); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.splits == 1) return e;
+  if (e != hipSuccess) return e;
   const int64_t n = (int64_t)a.N * a.K;
-  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.partial, a.splits, n, a.dW);
+  if (a.splits == 1 && a.dW2 == nullptr) return hipSuccess;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a.partial, a.splits, n,
+                     a.dW, a.dW2, (int64_t)a.nsplit * a.K);
   return hipGetLastError();
 }
 
@@ -384,15 +645,6 @@ __global__ __launch_bounds__(256) void transpose_kernel(const T* __restrict__ sr
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void dact_kernel(const T* __restrict__ dF, const T* __restrict__ Z, T* __restrict__ dZ,
-                                                   int64_t n, int act) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float g = to_f(dF[i]);
-  dZ[i] = from_f<T>(act == 0 ? g * dsiluf_(to_f(Z[i])) : g);
-}
-
 __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) x[i] = 0.f;
@@ -407,17 +659,14 @@ hipError_t launch_fill_zero(float* x, int64_t n, hipStream_t st) {
 }
 
 hipError_t launch_gemm_nt(const GemmArgs& a, bool bf16_data, hipStream_t st) {
-  return bf16_data ? gemm_pro<bf16>(a, st, a.N, nullptr, nullptr) : gemm_pro<float>(a, st, a.N, nullptr, nullptr);
-}
-
-hipError_t launch_gemm_nt_dual(const GemmArgs& a, int nsplit, const void* W2, void* Y2, bool bf16_data, hipStream_t st) {
-  return bf16_data ? gemm_pro<bf16>(a, st, nsplit, W2, Y2) : gemm_pro<float>(a, st, nsplit, W2, Y2);
+  if (a.K % 64 != 0) return hipErrorInvalidValue;
+  return bf16_data ? gemm_pro<bf16>(a, st) : gemm_pro<float>(a, st);
 }
 
 int wgrad_splits(int64_t M, int N, int K) {
   const int tiles = ((N + WN - 1) / WN) * ((K + WK - 1) / WK);
   int64_t s = (1024 + tiles - 1) / tiles;
-  const int64_t maxs = (M + 255) / 256;
+  const int64_t maxs = (M + 511) / 512;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
   return (int)s;
@@ -434,15 +683,5 @@ hipError_t launch_transpose(const void* src, int rows, int cols, void* dst, int 
     hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)src, rows, cols, (bf16*)dst, ldd, col0);
   else
     hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, st, (const float*)src, rows, cols, (float*)dst, ldd, col0);
-  return hipGetLastError();
-}
-
-hipError_t launch_dact(const void* dF, const void* Z, void* dZ, int64_t n, int act, bool bf16_data, hipStream_t st) {
-  if (n == 0) return hipSuccess;
-  const unsigned grid = (unsigned)((n + 255) / 256);
-  if (bf16_data)
-    hipLaunchKernelGGL(dact_kernel<bf16>, dim3(grid), dim3(256), 0, st, (const bf16*)dF, (const bf16*)Z, (bf16*)dZ, n, act);
-  else
-    hipLaunchKernelGGL(dact_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)dF, (const float*)Z, (float*)dZ, n, act);
   return hipGetLastError();
 }

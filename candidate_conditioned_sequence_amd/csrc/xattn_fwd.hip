@@ -32,6 +32,21 @@
 
 namespace {
 
+// exp2 argument s*c - ref.  The fp32 path rounds s*c first so that the row
+// holding the maximum gets exactly exp2(0) = 1 (a single-row history then
+// returns its value row bit for bit); bf16 rounds that difference away, so
+// the bf16 path uses one fused multiply-add.
+template <typename T>
+WHALE_DEV float scaled_arg(float s, float c, float ref) {
+  if constexpr (sizeof(T) == 4) {
+#pragma clang fp contract(off)
+    const float sc = s * c;     // rounded on its own: no fused multiply-add here
+    return sc - ref;
+  } else {
+    return fmaf(s, c, -ref);
+  }
+}
+
 constexpr int kNW = 4;            // waves per workgroup
 constexpr int kBN = 64;           // history rows per tile
 constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
@@ -183,7 +198,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
       for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(fmaf(s[kb][qb][r], c, -mref[qb]));
+          const float p = fast_exp2(scaled_arg<T>(s[kb][qb][r], c, mref[qb]));
           lsum[qb] += p;
           pf[kb][qb][r >> 3][r & 7] = from_f<T>(p);
         }

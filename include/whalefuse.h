@@ -50,7 +50,7 @@
  *     required pointer (WHALE_ERR_NULL), inconsistent sizes (WHALE_ERR_SHAPE,
  *     e.g. d % h != 0, M == 0), an unknown dtype (WHALE_ERR_DTYPE), a shape
  *     the kernels do not implement (WHALE_ERR_UNSUPPORTED: d_h not in
- *     {32, 64}, d above 512, H not a multiple of 64), or a workspace
+ *     {32, 64}, d not in {64, 128, 256, 512}, H not a multiple of 64), or a workspace
  *     smaller than the size query returns (WHALE_ERR_WORKSPACE).  A failed kernel launch returns WHALE_ERR_LAUNCH.
  *   - Results are bitwise reproducible for fixed inputs, dims and device:
  *     no atomics, every reduction runs in a fixed order.

@@ -186,20 +186,21 @@ def test_fusion_mlp_bwd(gpu, dtype, act):
     assert_close("dW_F", dWf, dWf_ref, dtype)
 
 
-@pytest.mark.parametrize("dtype,gate,norm", [("f32", O.GATE_SHARED, O.NORM_LAYER),
-                                             ("bf16", O.GATE_SHARED, O.NORM_LAYER),
-                                             ("bf16", O.GATE_SEPARATE, O.NORM_RMS),
-                                             ("f32", O.GATE_SEPARATE, O.NORM_NONE)])
-def test_swiglu_ffn_bwd(gpu, dtype, gate, norm):
-    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm}", flush=True)
-    M, d = 300, 128
+@pytest.mark.parametrize("dtype,gate,norm,d", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128),
+                                               ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256),
+                                               ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128),
+                                               ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64),
+                                               ("bf16", O.GATE_SHARED, O.NORM_LAYER, 512)])
+def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d):
+    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm} d={d}", flush=True)
+    M = 300
     H = 4 * d
     Fm, dY = draw(41, (M, d), dtype), draw(42, (M, d), dtype)
     Wu = weights(43, (2 if gate == O.GATE_SEPARATE else 1) * H, d, dtype)
     Wd = weights(44, d, H, dtype)
     g, bt = 1 + 0.2 * draw(45, (d,), "f32"), 0.2 * draw(46, (d,), "f32")
     ref = O.swiglu_ffn_bwd(Fm, norm, 1e-5, g, bt, Wu, gate, Wd, dY)
-    dm = wb.dims(1, M, 1, d, 2, 0, 0)
+    dm = wb.dims(1, M, 1, d, d // 64, 0, 0)
     tF, tWu, tWd = to_dev(Fm, dtype, gpu), to_dev(Wu, dtype, gpu), to_dev(Wd, dtype, gpu)
     tg, tb = f32_dev(g, gpu), f32_dev(bt, gpu)
     Y, U = torch.empty_like(tF), torch.empty((M, Wu.shape[0]), dtype=tF.dtype, device=gpu)
@@ -223,10 +224,13 @@ def test_swiglu_ffn_bwd(gpu, dtype, gate, norm):
         assert_close("db_f", db, ref["db_f"], dtype)
 
 
-@pytest.mark.parametrize("dtype,norm", [("f32", O.NORM_LAYER), ("bf16", O.NORM_LAYER), ("bf16", O.NORM_RMS)])
-def test_proj_qkv_bwd(gpu, dtype, norm):
-    print(f"\n[proj_qkv_bwd] {dtype} norm={norm}", flush=True)
-    B, C, n_q, d, h, L = 3, 5, 7, 128, 2, [0, 200, 77]
+@pytest.mark.parametrize("dtype,norm,d", [("f32", O.NORM_LAYER, 128), ("bf16", O.NORM_LAYER, 128),
+                                          ("bf16", O.NORM_RMS, 256), ("f32", O.NORM_LAYER, 64),
+                                          ("bf16", O.NORM_LAYER, 512), ("f32", O.NORM_NONE, 128)])
+def test_proj_qkv_bwd(gpu, dtype, norm, d):
+    print(f"\n[proj_qkv_bwd] {dtype} norm={norm} d={d}", flush=True)
+    B, C, n_q, L = 3, 5, 7, [0, 200, 77]
+    h = d // 64
     M, off = B * C * n_q, offsets(L)
     T = int(off[-1])
     Hw, Hs = draw(51, (M, d), dtype), draw(52, (T, d), dtype)
@@ -255,8 +259,9 @@ def test_proj_qkv_bwd(gpu, dtype, norm):
     assert_close("dH_s", dHs, ref["dH_s"], dtype)
     for name, got in zip(("dW_Q", "dW_K", "dW_V"), dW):
         assert_close(name, got, ref[name], dtype)
-    assert_close("dg_q", dgb[0], ref["dg_q"], dtype)
-    assert_close("dg_kv", dgb[2], ref["dg_kv"], dtype)
+    if norm != O.NORM_NONE:
+        assert_close("dg_q", dgb[0], ref["dg_q"], dtype)
+        assert_close("dg_kv", dgb[2], ref["dg_kv"], dtype)
     if norm == O.NORM_LAYER:
         assert_close("db_q", dgb[1], ref["db_q"], dtype)
         assert_close("db_kv", dgb[3], ref["db_kv"], dtype)
