@@ -71,6 +71,9 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run a plain device-to-device copy of 512 MiB (3 times), the reference kernel for "
+                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the module shards by request "
@@ -150,6 +153,13 @@ def main():
     import candidate_conditioned_sequence_amd.layer as layer_mod
     layer_mod.wb = wb
 
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step()

@@ -66,6 +66,46 @@ WHALE_DEV constexpr int acc_row(int r, int hh) { return 8 * (r >> 2) + 4 * hh + 
 
 WHALE_DEV f32x16 zero16() { f32x16 v; for (int i = 0; i < 16; ++i) v[i] = 0.f; return v; }
 
+// --------------------------------------------------------------- transposed operands
+// A operand of a 32x32x16 step taken column-wise from a row-major LDS tile
+// X[row][col] (row stride ld elements): lane l gets column c0 + l % 32 and, for
+// lane half hh = l / 32, the rows r0 + 4 hh + u (u < 4) and r0 + 8 + 4 hh + (u - 4)
+// (u >= 4) -- the row order of a 32x32 accumulator's column, so an accumulator
+// can be fed back as the matching B operand.
+//
+// bf16 uses the gfx950 transposing LDS read ds_read_b64_tr_b16: within each
+// 16-lane group, lane i supplies a pointer p_i to four consecutive 16-bit
+// elements and lane j receives p_{4k + j/4}[j % 4] for k = 0..3.  Lane i of
+// group g therefore points at row r0 + 4 (g / 2) + i / 4, column
+// c0 + 16 (g % 2) + 4 (i % 4); the second read is 8 rows further down.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+WHALE_DEV bf16x4 lds_tr4(const bf16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) bf16*)(p)));
+  return __builtin_bit_cast(bf16x4, v);
+}
+
+template <typename T> WHALE_DEV x8_t<T> lds_colA(const T* X, int ld, int r0, int c0, int lane);
+
+template <> WHALE_DEV bf16x8 lds_colA<bf16>(const bf16* X, int ld, int r0, int c0, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  const bf16* p = X + (r0 + 4 * (g >> 1) + (i >> 2)) * ld + c0 + 16 * (g & 1) + 4 * (i & 3);
+  return cat44<bf16>(lds_tr4(p), lds_tr4(p + 8 * ld));
+}
+
+template <> WHALE_DEV f32x8 lds_colA<float>(const float* X, int ld, int r0, int c0, int lane) {
+  const int hh = lane >> 5, c = c0 + (lane & 31);
+  f32x8 v;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v[u] = X[(r0 + 4 * hh + u) * ld + c];
+    v[u + 4] = X[(r0 + 8 + 4 * hh + u) * ld + c];
+  }
+  return v;
+}
+
 // --------------------------------------------------------------- misc
 // Workgroups are dispatched round-robin over the 8 XCDs (id % 8).  This
 // gives each XCD one contiguous range of logical ids so that workgroups

@@ -17,8 +17,9 @@
 //    the fp32 partials are summed in a fixed order by a second kernel.
 // Both kernels use the same register trick as the forward: the MFMA
 // accumulator of the score-like product is reused directly as the B operand
-// of the next product, with the A operand read from a transposed LDS tile in
-// the matching row order.  Deterministic: no atomics.
+// of the next product, with the A operand read column-wise from the same
+// row-major LDS tile (transposing LDS reads) in the matching row order.
+// Deterministic: no atomics.
 #include "common.h"
 #include "kernels.h"
 
@@ -54,10 +55,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
     const float* __restrict__ Dbuf, T* __restrict__ dQ, int d, int h, int QR, int nqb, float c, float scale,
     int nblocks) {
   constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = kNW * 32;
-  constexpr int KLD = DH + 8, VLD = BN + 4, CPR = DH / 8, NCH = BN * CPR / (kNW * 64);
+  constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (kNW * 64);
   __shared__ __attribute__((aligned(32))) T Ks[2][BN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][BN * KLD];
-  __shared__ __attribute__((aligned(32))) T Kt[2][DH * VLD];
 
   const int lid = xcd_remap(blockIdx.x, nblocks);
   const int qbi = lid % nqb;
@@ -108,8 +108,6 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       st8<T>(&Ks[buf][row * KLD + e0], kr[i]);
       st8<T>(&Vs[buf][row * KLD + e0], vr[i]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) Kt[buf][(e0 + u) * VLD + row] = kr[i][u];
     }
   };
 
@@ -142,10 +140,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const T* kp = &Kt[buf][(32 * e + l32) * VLD + 32 * kb + 16 * mm + 4 * hh];
-          mma32(acc[e], cat44<T>(ld4<T>(kp), ld4<T>(kp + 8)), dsf[kb][mm]);
-        }
+        for (int mm = 0; mm < 2; ++mm)
+          mma32(acc[e], lds_colA<T>(&Ks[buf][0], KLD, 32 * kb + 16 * mm, 32 * e, lane), dsf[kb][mm]);
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
   }
@@ -172,11 +168,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
     const float* __restrict__ Dbuf, T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ part,
     int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks) {
   constexpr int QT = 64, KS = DH / 16, NE = DH / 32;
-  constexpr int KLD = DH + 8, QLD = QT + 4, CPR = DH / 8, NCH = QT * CPR / (kNW * 64);
+  constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (kNW * 64);
   __shared__ __attribute__((aligned(32))) T Qs[2][QT * KLD];
   __shared__ __attribute__((aligned(32))) T Gs[2][QT * KLD];
-  __shared__ __attribute__((aligned(32))) T Qt[2][DH * QLD];
-  __shared__ __attribute__((aligned(32))) T Gt[2][DH * QLD];
   __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
   __shared__ __attribute__((aligned(16))) float D_s[2][QT];
 
@@ -237,11 +231,6 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       st8<T>(&Qs[buf][row * KLD + e0], qr[i]);
       st8<T>(&Gs[buf][row * KLD + e0], gr[i]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        Qt[buf][(e0 + u) * QLD + row] = qr[i][u];
-        Gt[buf][(e0 + u) * QLD + row] = gr[i][u];
-      }
     }
     if (tid < QT) { lse_s[buf][tid] = lr; D_s[buf][tid] = dr; }
   };
@@ -281,9 +270,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
       for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const int o = (32 * e + l32) * QLD + 32 * qb + 16 * mm + 4 * hh;
-          mma32(dv[e], cat44<T>(ld4<T>(&Gt[buf][o]), ld4<T>(&Gt[buf][o + 8])), pf[qb][mm]);
-          mma32(dk[e], cat44<T>(ld4<T>(&Qt[buf][o]), ld4<T>(&Qt[buf][o + 8])), dsf[qb][mm]);
+          mma32(dv[e], lds_colA<T>(&Gs[buf][0], KLD, 32 * qb + 16 * mm, 32 * e, lane), pf[qb][mm]);
+          mma32(dk[e], lds_colA<T>(&Qs[buf][0], KLD, 32 * qb + 16 * mm, 32 * e, lane), dsf[qb][mm]);
         }
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();

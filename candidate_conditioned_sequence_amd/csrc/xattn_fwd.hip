@@ -18,8 +18,8 @@
 //    lane plus one exchange between the two lane halves, and the
 //    probabilities P^T are already laid out as the B operand of the next
 //    product O^T += V^T P^T: no data movement between the two products.
-//    V is written to LDS transposed so that the A operand of that product
-//    (V^T rows, 8 history rows per lane) is two 4-element reads.
+//    V stays row-major in LDS; the A operand of that product (V^T rows, 8
+//    history rows per lane) comes from two transposing LDS reads.
 //  * Online softmax in base 2 with the scale folded in.  Lazy rescaling:
 //    the running reference max is only moved when a tile's max exceeds it by
 //    more than kTau (probabilities then stay below 2^kTau, harmless in fp32
@@ -53,8 +53,7 @@ constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
 
 template <typename T, int DH>
 struct FwdTile {
-  static constexpr int KLD = DH + 8;          // K tile row stride (elements)
-  static constexpr int VLD = kBN + 4;         // V^T tile row stride (elements)
+  static constexpr int KLD = DH + 8;          // K and V tile row stride (elements)
   static constexpr int CPR = DH / 8;          // 8-element chunks per row
   static constexpr int NCH = kBN * CPR / (kNW * 64);   // chunks per thread per tensor
   static_assert(NCH >= 1 && kBN * CPR % (kNW * 64) == 0, "tile/threads mismatch");
@@ -67,9 +66,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     int d, int h, int QR, int nqb, float c, int nblocks) {
   using TT = FwdTile<T, DH>;
   constexpr int NQ = QPW / 32, KS = DH / 16, NE = DH / 32, QB = kNW * QPW;
-  constexpr int KLD = TT::KLD, VLD = TT::VLD, CPR = TT::CPR, NCH = TT::NCH;
+  constexpr int KLD = TT::KLD, CPR = TT::CPR, NCH = TT::NCH;
   __shared__ __attribute__((aligned(32))) T Ks[2][kBN * KLD];
-  __shared__ __attribute__((aligned(32))) T Vt[2][DH * VLD];
+  __shared__ __attribute__((aligned(32))) T Vs[2][kBN * KLD];
 
   const int lid = xcd_remap(blockIdx.x, nblocks);
   const int qbi = lid % nqb;
@@ -122,8 +121,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
       const int ch = tid + i * kNW * 64;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       st8<T>(&Ks[buf][row * KLD + e0], kr[i]);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) Vt[buf][(e0 + u) * VLD + row] = vr[i][u];
+      st8<T>(&Vs[buf][row * KLD + e0], vr[i]);
     }
   };
 
@@ -190,17 +188,29 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
       }
     }
 
-    // P^T = exp2(s*c - ref), row sums kept per lane half, packed as B operands.
+    // P^T = exp2(s*c - ref), packed as B operands; row sums kept per lane
+    // half (bf16: summed from the rounded values the product uses).
     x8_t<T> pf[2][NQ][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = fast_exp2(scaled_arg<T>(s[kb][qb][r], c, mref[qb]));
-          lsum[qb] += p;
-          pf[kb][qb][r >> 3][r & 7] = from_f<T>(p);
+        for (int r = 0; r < 16; r += 2) {
+          const float p0 = fast_exp2(scaled_arg<T>(s[kb][qb][r], c, mref[qb]));
+          const float p1 = fast_exp2(scaled_arg<T>(s[kb][qb][r + 1], c, mref[qb]));
+          if constexpr (sizeof(T) == 2) {
+            f32x2 pp = {p0, p1};
+            const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
+            const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+            lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, lsum[qb], false);
+            pf[kb][qb][r >> 3][r & 7] = pk[0];
+            pf[kb][qb][r >> 3][(r & 7) + 1] = pk[1];
+          } else {
+            lsum[qb] += p0 + p1;
+            pf[kb][qb][r >> 3][r & 7] = from_f<T>(p0);
+            pf[kb][qb][r >> 3][(r & 7) + 1] = from_f<T>(p1);
+          }
         }
 
     // O^T[e][q] += V^T[e][key] P^T[key][q].  Operand element u of lane half
@@ -212,8 +222,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const T* vp = &Vt[buf][(32 * e + l32) * VLD + 32 * kb + 16 * mm + 4 * hh];
-          const x8_t<T> a = cat44<T>(ld4<T>(vp), ld4<T>(vp + 8));
+          const x8_t<T> a = lds_colA<T>(&Vs[buf][0], KLD, 32 * kb + 16 * mm, 32 * e, lane);
 #pragma unroll
           for (int qb = 0; qb < NQ; ++qb) mma32(oacc[e][qb], a, pf[kb][qb][mm]);
         }
