@@ -190,7 +190,7 @@ def main():
     # Roofline of the dominant call.  xattn_fwd is a single kernel launch.
     attn_ms = avg["xattn_fwd"]
     attn_tflops = f["attn_fwd"] / (attn_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": "xattn_fwd_kernel<bf16,64,64>", "achieved": round(attn_tflops, 1),
+    roof = {"bound": "mfma", "kernel": "xattn_fwd_kernel<bf16,64,64,4>", "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": None}
     res = {

@@ -47,11 +47,10 @@ WHALE_DEV float scaled_arg(float s, float c, float ref) {
   }
 }
 
-constexpr int kNW = 4;            // waves per workgroup
 constexpr int kBN = 64;           // history rows per tile
 constexpr float kTau = 8.0f;      // lazy-rescale threshold (log2 units)
 
-template <typename T, int DH>
+template <typename T, int DH, int kNW>
 struct FwdTile {
   static constexpr int KLD = DH + 8;          // K and V tile row stride (elements)
   static constexpr int CPR = DH / 8;          // 8-element chunks per row
@@ -59,14 +58,24 @@ struct FwdTile {
   static_assert(NCH >= 1 && kBN * CPR % (kNW * 64) == 0, "tile/threads mismatch");
 };
 
-template <typename T, int DH, int QPW>
+// kNW waves per workgroup, QPW queries per wave.
+//
+// Scores live in the log2 domain relative to a per-column reference ref:
+// t = c*s - ref with c = scale * log2(e), p = exp2(t).  For bf16 the factor
+// c is folded into the Q fragments once (Q*c rounded to bf16: a relative
+// error near 2^-9, below that of the bf16 probabilities) and -ref is the
+// accumulator input of the score MFMA, so the common path spends no VALU
+// instruction between the MFMA output and the exponential.  fp32 keeps Q
+// exact and forms t with a separate multiply and subtract.
+template <typename T, int DH, int QPW, int kNW>
 __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, T* __restrict__ A, float* __restrict__ lse,
     int d, int h, int QR, int nqb, float c, int nblocks) {
-  using TT = FwdTile<T, DH>;
+  using TT = FwdTile<T, DH, kNW>;
   constexpr int NQ = QPW / 32, KS = DH / 16, NE = DH / 32, QB = kNW * QPW;
   constexpr int KLD = TT::KLD, CPR = TT::CPR, NCH = TT::NCH;
+  constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Ks[2][kBN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][kBN * KLD];
 
@@ -87,17 +96,25 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     const int q = qbase + 32 * qb + l32;
     const T* src = Q + (qrow0 + q) * d + j * DH + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[qb][ks] = (q < QR) ? ld8<T>(src + 16 * ks) : zero8<T>();
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[qb][ks] = (q < QR) ? ld8<T>(src + 16 * ks) : zero8<T>();
+      if (kFold) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qf[qb][ks][u] = from_f<T>(to_f(qf[qb][ks][u]) * c);
+      }
+    }
   }
 
-  f32x16 oacc[NE][NQ];
+  f32x16 oacc[NE][NQ], bias[NQ];
 #pragma unroll
-  for (int e = 0; e < NE; ++e)
+  for (int qb = 0; qb < NQ; ++qb) {
+    bias[qb] = zero16();
 #pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) oacc[e][qb] = zero16();
+    for (int e = 0; e < NE; ++e) oacc[e][qb] = zero16();
+  }
   float mref[NQ], lsum[NQ];
 #pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = -INFINITY; lsum[qb] = 0.f; }
+  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = 0.f; lsum[qb] = 0.f; }
 
   const int ntiles = (L + kBN - 1) / kBN;
   const T* Kh = K + lo * d + j * DH;
@@ -136,18 +153,27 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     if (t + 1 < ntiles) load_tile(t + 1);
     const int nvalid = min(kBN, L - t * kBN);
 
-    // S^T[key][q] for two 32-row key blocks.
+    // Scores of two 32-row key blocks, accumulated onto -ref (bf16) or 0.
     f32x16 s[2][NQ];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int qb = 0; qb < NQ; ++qb) s[kb][qb] = zero16();
-#pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const x8_t<T> a = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
 #pragma unroll
-        for (int qb = 0; qb < NQ; ++qb) mma32(s[kb][qb], a, qf[qb][ks]);
+        for (int qb = 0; qb < NQ; ++qb) {
+          if (ks == 0) s[kb][qb] = bias[qb];
+          mma32(s[kb][qb], a, qf[qb][ks]);
+        }
       }
+    }
+    if (!kFold) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] = scaled_arg<T>(s[kb][qb][r], c, mref[qb]);
     }
     if (nvalid < kBN) {
 #pragma unroll
@@ -159,9 +185,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
             if (32 * kb + acc_row(r, hh) >= nvalid) s[kb][qb][r] = -INFINITY;
     }
 
-    // Tile max per query column, shared by both lane halves.
-    float mnew[NQ];
-    bool need = false;
+    // Tile max of t per query column (both lane halves).  The first tile
+    // always sets the reference; later ones move it only by more than kTau.
+    float tmax[NQ];
+    bool need = t == 0;
 #pragma unroll
     for (int qb = 0; qb < NQ; ++qb) {
       float mx = s[0][qb][0];
@@ -169,47 +196,61 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
-      mnew[qb] = fmaxf(mref[qb], mx);
-      need |= mnew[qb] > mref[qb] + kTau;
+      tmax[qb] = fmaxf(mx, __shfl_xor(mx, 32));
+      need |= tmax[qb] > kTau;
     }
     if (__ballot(need)) {
+      // Move the reference by the tile max: shift this tile's t, rescale O
+      // and the sums (alpha = 0 on the first tile, where both are zero).
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) {
-        if (mnew[qb] > mref[qb] + kTau) {
-          const float alpha = fast_exp2(mref[qb] - mnew[qb]);
-          mref[qb] = mnew[qb];
-          lsum[qb] *= alpha;
+        const float sh = (t == 0 || tmax[qb] > kTau) ? tmax[qb] : 0.f;
+        const float alpha = t == 0 ? 0.f : fast_exp2(-sh);
+        mref[qb] += sh;
+        lsum[qb] *= alpha;
 #pragma unroll
-          for (int e = 0; e < NE; ++e)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[e][qb][r] *= alpha;
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] -= sh;
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[e][qb][r] *= alpha;
+        if (kFold) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bias[qb][r] = -mref[qb];
         }
       }
     }
 
-    // P^T = exp2(s*c - ref), packed as B operands; row sums kept per lane
-    // half (bf16: summed from the rounded values the product uses).
+    // P^T = exp2(t), packed pairwise into the B operands; per-lane-half row
+    // sums (bf16: of the rounded values the product uses).
     x8_t<T> pf[2][NQ][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = fast_exp2(scaled_arg<T>(s[kb][qb][r], c, mref[qb]));
-          const float p1 = fast_exp2(scaled_arg<T>(s[kb][qb][r + 1], c, mref[qb]));
+        for (int mm = 0; mm < 2; ++mm) {
           if constexpr (sizeof(T) == 2) {
-            f32x2 pp = {p0, p1};
-            const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
-            const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-            lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, lsum[qb], false);
-            pf[kb][qb][r >> 3][r & 7] = pk[0];
-            pf[kb][qb][r >> 3][(r & 7) + 1] = pk[1];
+            u32x4 words;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const int r = 8 * mm + 2 * v;
+              f32x2 pp = {fast_exp2(s[kb][qb][r]), fast_exp2(s[kb][qb][r + 1])};
+              const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
+              const bf16x2 one = {(bf16)1.f, (bf16)1.f};
+              lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, lsum[qb], false);
+              words[v] = __builtin_bit_cast(unsigned, pk);
+            }
+            pf[kb][qb][mm] = __builtin_bit_cast(bf16x8, words);
           } else {
-            lsum[qb] += p0 + p1;
-            pf[kb][qb][r >> 3][r & 7] = from_f<T>(p0);
-            pf[kb][qb][r >> 3][(r & 7) + 1] = from_f<T>(p1);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const float p = fast_exp2(s[kb][qb][8 * mm + u]);
+              lsum[qb] += p;
+              pf[kb][qb][mm][u] = from_f<T>(p);
+            }
           }
         }
 
@@ -217,7 +258,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     // hh is history row 4*hh + u (u < 4) or 8 + 4*hh + (u - 4) of the
     // 16-row step, matching the accumulator rows of P^T.
 #pragma unroll
-    for (int e = 0; e < NE; ++e) {
+    for (int e = 0; e < NE; ++e)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -226,7 +267,6 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
 #pragma unroll
           for (int qb = 0; qb < NQ; ++qb) mma32(oacc[e][qb], a, pf[kb][qb][mm]);
         }
-    }
 
     if (t + 1 < ntiles) store_tile(buf ^ 1);
     __syncthreads();
@@ -255,14 +295,14 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
   }
 }
 
-template <typename T, int DH, int QPW>
+template <typename T, int DH, int QPW, int kNW>
 hipError_t launch_fwd_t(const XattnArgs& a, hipStream_t st) {
   constexpr int QB = kNW * QPW;
   const int nqb = (a.QR + QB - 1) / QB;
   const int64_t nblk = (int64_t)a.B * a.h * nqb;
   if (nblk == 0) return hipSuccess;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((xattn_fwd_kernel<T, DH, QPW>), dim3((unsigned)nblk), dim3(kNW * 64), 0, st,
+  hipLaunchKernelGGL((xattn_fwd_kernel<T, DH, QPW, kNW>), dim3((unsigned)nblk), dim3(kNW * 64), 0, st,
                      (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (T*)a.A, a.lse,
                      a.d, a.h, a.QR, nqb, c, (int)nblk);
   return hipGetLastError();
@@ -272,8 +312,8 @@ template <typename T>
 hipError_t launch_fwd_dh(const XattnArgs& a, hipStream_t st) {
   const bool wide = a.QR >= 1024;
   switch (a.dh) {
-    case 32: return wide ? launch_fwd_t<T, 32, 64>(a, st) : launch_fwd_t<T, 32, 32>(a, st);
-    case 64: return wide ? launch_fwd_t<T, 64, 64>(a, st) : launch_fwd_t<T, 64, 32>(a, st);
+    case 32: return wide ? launch_fwd_t<T, 32, 64, 4>(a, st) : launch_fwd_t<T, 32, 32, 4>(a, st);
+    case 64: return wide ? launch_fwd_t<T, 64, 64, 4>(a, st) : launch_fwd_t<T, 64, 32, 4>(a, st);
   }
   return hipErrorInvalidValue;
 }
