@@ -26,6 +26,14 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+
+# HBM traffic of one xattn_fwd_kernel<bf16,64,64,4> launch on this workload:
+# rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
+# the counter reads for a 512 MiB elementwise copy (x2.000 and x1.000).  Taken
+# from profiles/xattn_fwd_kernel_c3_L10k_hbm_traffic.md; must be re-measured
+# (or set to None) whenever that kernel changes.
+XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_kernel<bf16,64,64,4>",
+                     "fetch_kib": 709713, "fetch_scale": 2.000, "write_kib": 143495, "write_scale": 1.000}
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 
@@ -72,8 +80,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="first run a plain device-to-device copy of 512 MiB (3 times), the reference kernel for "
-                         "scaling the FETCH_SIZE / WRITE_SIZE counters")
+                    help="first run a plain elementwise copy (negation) of 512 MiB fp32, 3 times: the reference kernel "
+                         "for scaling the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the module shards by request "
@@ -154,10 +162,12 @@ def main():
     layer_mod.wb = wb
 
     if args.calibrate_copy:
-        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        # torch.neg over 2^27 fp32 values: one elementwise kernel that reads
+        # and writes exactly 512 MiB.
+        src = torch.ones(1 << 27, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
@@ -190,9 +200,17 @@ def main():
     # Roofline of the dominant call.  xattn_fwd is a single kernel launch.
     attn_ms = avg["xattn_fwd"]
     attn_tflops = f["attn_fwd"] / (attn_ms * 1e-3) / 1e12
-    roof = {"bound": "mfma", "kernel": "xattn_fwd_kernel<bf16,64,64,4>", "achieved": round(attn_tflops, 1),
+    kname = "xattn_fwd_kernel<bf16,64,64,4>"
+    tr = XATTN_FWD_TRAFFIC
+    traffic = None
+    if tr is not None and tr["kernel"] == kname:
+        traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]))
+    M, d = cfg.M, cfg.d
+    algo_bytes = 2 * (M * d + 2 * T * d + M * d) + 4 * M * cfg.h
+    roof = {"bound": "mfma", "kernel": kname, "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": None}
+            "traffic": traffic, "traffic_unit": "bytes per launch", "algorithmic_bytes": algo_bytes,
+            "algorithmic_flops": f["attn_fwd"]}
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
