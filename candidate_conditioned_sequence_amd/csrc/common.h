@@ -96,6 +96,30 @@ template <> WHALE_DEV bf16x8 lds_colA<bf16>(const bf16* X, int ld, int r0, int c
   return cat44<bf16>(lds_tr4(p), lds_tr4(p + 8 * ld));
 }
 
+// The same reads split into a per-lane element offset (computed once) and a
+// tile-uniform base X + r0*ld + c0.
+template <typename T> WHALE_DEV int lds_colA_lane(int ld, int lane);
+template <> WHALE_DEV int lds_colA_lane<bf16>(int ld, int lane) {
+  const int g = lane >> 4, i = lane & 15;
+  return (4 * (g >> 1) + (i >> 2)) * ld + 16 * (g & 1) + 4 * (i & 3);
+}
+template <> WHALE_DEV int lds_colA_lane<float>(int ld, int lane) {
+  return 4 * (lane >> 5) * ld + (lane & 31);
+}
+template <typename T> WHALE_DEV x8_t<T> lds_colA_at(const T* base, int ld, int off);
+template <> WHALE_DEV bf16x8 lds_colA_at<bf16>(const bf16* base, int ld, int off) {
+  return cat44<bf16>(lds_tr4(base + off), lds_tr4(base + off + 8 * ld));
+}
+template <> WHALE_DEV f32x8 lds_colA_at<float>(const float* base, int ld, int off) {
+  f32x8 v;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    v[u] = base[off + u * ld];
+    v[u + 4] = base[off + (8 + u) * ld];
+  }
+  return v;
+}
+
 template <> WHALE_DEV f32x8 lds_colA<float>(const float* X, int ld, int r0, int c0, int lane) {
   const int hh = lane >> 5, c = c0 + (lane & 31);
   f32x8 v;
@@ -123,6 +147,21 @@ WHALE_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 WHALE_DEV float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
 WHALE_DEV float siluf_(float z) { return z * sigmoidf_(z); }
 WHALE_DEV float dsiluf_(float z) { float s = sigmoidf_(z); return s * (1.f + z * (1.f - s)); }
+
+// Combine a value across the two lane halves (lanes l and l ^ 32) with one
+// v_permlane32_swap: both halves get the same result, formed in the same
+// order (low half's value first).
+WHALE_DEV f32x2 half_pair(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v), __builtin_bit_cast(unsigned, v),
+                                                  false, false);
+  return f32x2{__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1])};
+}
+// med3(a, b, +inf) = max(a, b) without the quieting moves fmaxf adds.
+WHALE_DEV float half_max(float v) {
+  const f32x2 p = half_pair(v);
+  return __builtin_amdgcn_fmed3f(p[0], p[1], INFINITY);
+}
+WHALE_DEV float half_sum(float v) { const f32x2 p = half_pair(v); return p[0] + p[1]; }
 
 WHALE_DEV float wave_sum(float v) {
 #pragma unroll

@@ -47,7 +47,42 @@ __global__ __launch_bounds__(256) void bwd_dot_kernel(const T* __restrict__ A, c
   D[i] = s;
 }
 
+// Probabilities and dS of one 32x32 score block, packed pairwise into two
+// B operands (bf16: v_cvt_pk; the pair order is the accumulator row order).
+template <typename T>
+WHALE_DEV void p_ds_pack(const f32x16& s, const f32x16& dp, x8_t<T> (&pf)[2], x8_t<T> (&dsf)[2]) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int mm = 0; mm < 2; ++mm) {
+      u32x4 pw, dw;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int r = 8 * mm + 2 * v;
+        const f32x2 pp = {fast_exp2(s[r]), fast_exp2(s[r + 1])};
+        const f32x2 dd = {pp[0] * dp[r], pp[1] * dp[r + 1]};
+        pw[v] = __builtin_bit_cast(unsigned, __builtin_convertvector(pp, bf16x2));
+        dw[v] = __builtin_bit_cast(unsigned, __builtin_convertvector(dd, bf16x2));
+      }
+      pf[mm] = __builtin_bit_cast(bf16x8, pw);
+      dsf[mm] = __builtin_bit_cast(bf16x8, dw);
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = fast_exp2(s[r]);
+      pf[r >> 3][r & 7] = p;
+      dsf[r >> 3][r & 7] = p * dp[r];
+    }
+  }
+}
+
 // ----------------------------------------------------------------- dQ
+// Scores in the log2 domain: t = c*s - lse2 with c = scale*log2(e).  For bf16
+// c is folded into the Q fragments once (rounded to bf16, as in the forward)
+// and -lse2 (one value per lane: this query) is the accumulator input of the
+// score MFMA; -D likewise starts the dP MFMA, so P = exp2(acc) and
+// dS = P * acc' need no other VALU work.  fp32 keeps Q exact and forms t with
+// one fused multiply-add.
 template <typename T, int DH>
 __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -56,6 +91,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
     int nblocks) {
   constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = kNW * 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (kNW * 64);
+  constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Ks[2][BN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][BN * KLD];
 
@@ -77,6 +113,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = qok ? ld8<T>(Q + off + 16 * ks) : zero8<T>();
       gf[ks] = qok ? ld8<T>(dA + off + 16 * ks) : zero8<T>();
+      if (kFold) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) qf[ks][u] = from_f<T>(to_f(qf[ks][u]) * c);
+      }
     }
   }
   const float lse2 = qok ? lse[(qrow0 + q) * h + j] * kLog2e : INFINITY;
@@ -89,16 +129,18 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
   const int ntiles = (L + BN - 1) / BN;
   const T* Kh = K + lo * d + j * DH;
   const T* Vh = V + lo * d + j * DH;
+  // Rows past the history are loaded as copies of its last row (no masked
+  // loads in the loop); their probabilities are set to 0 below.
   x8_t<T> kr[NCH], vr[NCH];
   auto load_tile = [&](int t) {
-    const int nvalid = min(BN, L - t * BN);
+    const int last = L - 1 - t * BN;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = tid + i * kNW * 64;
-      const int row = ch / CPR, e0 = 8 * (ch % CPR);
+      const int row = min(ch / CPR, last), e0 = 8 * (ch % CPR);
       const int64_t off = (int64_t)(t * BN + row) * d + e0;
-      kr[i] = row < nvalid ? ld8<T>(Kh + off) : zero8<T>();
-      vr[i] = row < nvalid ? ld8<T>(Vh + off) : zero8<T>();
+      kr[i] = ld8<T>(Kh + off);
+      vr[i] = ld8<T>(Vh + off);
     }
   };
   auto store_tile = [&](int buf) {
@@ -120,7 +162,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
     x8_t<T> dsf[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s, dp;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { s[r] = kFold ? -lse2 : 0.f; dp[r] = -Dq; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const x8_t<T> ka = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
@@ -128,12 +172,17 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
         mma32(s, ka, qf[ks]);
         mma32(dp, va, gf[ks]);
       }
+      if (!kFold) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = fast_exp2(fmaf(s[r], c, -lse2));
-        if (32 * kb + acc_row(r, hh) >= nvalid) p = 0.f;
-        dsf[kb][r >> 3][r & 7] = from_f<T>(p * (dp[r] - Dq));
+        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -lse2);
       }
+      if (nvalid < BN) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + acc_row(r, hh) >= nvalid) s[r] = -INFINITY;
+      }
+      x8_t<T> pf_unused[2];
+      p_ds_pack<T>(s, dp, pf_unused, dsf[kb]);   // P itself is not needed here
     }
 #pragma unroll
     for (int e = 0; e < NE; ++e)
@@ -161,6 +210,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
 }
 
 // ----------------------------------------------------------------- dK, dV
+// Lanes are keys and accumulator rows are queries, so -lse2 and -D vary with
+// the row: each query tile stores them negated in LDS and the 4-row groups a
+// lane needs are read straight into the score / dP accumulators as their
+// starting values.  bf16 folds c into the K fragments.  Query rows past the
+// split are loaded as copies of its last row with -lse2 = -inf, so P = 0 and
+// dS = 0 for them.
 template <typename T, int DH>
 __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -169,10 +224,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
     int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks) {
   constexpr int QT = 64, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (kNW * 64);
+  constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Qs[2][QT * KLD];
   __shared__ __attribute__((aligned(32))) T Gs[2][QT * KLD];
-  __shared__ __attribute__((aligned(16))) float lse_s[2][QT];
-  __shared__ __attribute__((aligned(16))) float D_s[2][QT];
+  __shared__ __attribute__((aligned(16))) float nl_s[2][QT];   // -lse2 (bf16) or lse2 (fp32)
+  __shared__ __attribute__((aligned(16))) float nd_s[2][QT];   // -D
 
   const int split = blockIdx.y;
   const int lid = xcd_remap(blockIdx.x, nblocks);
@@ -185,6 +241,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
   const int q_begin = split * qchunk;
   const int q_end = min(QR, q_begin + qchunk);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar
   const int key = kt * 128 + w * 32 + l32;
   const bool kok = key < L;
   const int64_t qrow0 = (int64_t)b * QR;
@@ -196,6 +253,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
     for (int ks = 0; ks < KS; ++ks) {
       kf[ks] = kok ? ld8<T>(K + off + 16 * ks) : zero8<T>();
       vf[ks] = kok ? ld8<T>(V + off + 16 * ks) : zero8<T>();
+      if (kFold) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) kf[ks][u] = from_f<T>(to_f(kf[ks][u]) * c);
+      }
     }
   }
   f32x16 dk[NE], dv[NE];
@@ -204,24 +265,28 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
 
   const int ntiles = q_end > q_begin ? (q_end - q_begin + QT - 1) / QT : 0;
   x8_t<T> qr[NCH], gr[NCH];
-  float lr = INFINITY, dr = 0.f;
+  float lr = 0.f, dr = 0.f;
   auto load_tile = [&](int t) {
     const int qt0 = q_begin + t * QT;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = tid + i * kNW * 64;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
-      const int qq = qt0 + row;
+      const int qq = min(qt0 + row, q_end - 1);
       const int64_t off = (qrow0 + qq) * d + j * DH + e0;
-      const bool ok = qq < q_end;
-      qr[i] = ok ? ld8<T>(Q + off) : zero8<T>();
-      gr[i] = ok ? ld8<T>(dA + off) : zero8<T>();
+      qr[i] = ld8<T>(Q + off);
+      gr[i] = ld8<T>(dA + off);
     }
-    if (tid < QT) {
-      const int qq = qt0 + tid;
+    // lane i of the first wave fetches query i's lse and D
+    if (wu == 0) {
+      const int qq = qt0 + lane;
+      const int qc = min(qq, q_end - 1);
+      const float l2 = lse[(qrow0 + qc) * h + j] * kLog2e;
+      const float dd = Dbuf[(qrow0 + qc) * h + j];
       const bool ok = qq < q_end;
-      lr = ok ? lse[(qrow0 + qq) * h + j] * kLog2e : INFINITY;
-      dr = ok ? Dbuf[(qrow0 + qq) * h + j] : 0.f;
+      if (kFold) lr = ok ? -l2 : -INFINITY;
+      else lr = ok ? l2 : INFINITY;
+      dr = ok ? -dd : 0.f;
     }
   };
   auto store_tile = [&](int buf) {
@@ -232,7 +297,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
       st8<T>(&Qs[buf][row * KLD + e0], qr[i]);
       st8<T>(&Gs[buf][row * KLD + e0], gr[i]);
     }
-    if (tid < QT) { lse_s[buf][tid] = lr; D_s[buf][tid] = dr; }
+    if (wu == 0) { nl_s[buf][lane] = lr; nd_s[buf][lane] = dr; }
   };
 
   if (ntiles > 0) { load_tile(0); store_tile(0); }
@@ -243,7 +308,22 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
     x8_t<T> pf[2][2], dsf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
-      f32x16 s = zero16(), dp = zero16();
+      f32x16 s, dp, l2blk;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&nl_s[buf][32 * qb + 8 * g + 4 * hh]);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&nd_s[buf][32 * qb + 8 * g + 4 * hh]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          dp[4 * g + u] = d4[u];
+          if (kFold) {
+            s[4 * g + u] = l4[u];
+          } else {
+            s[4 * g + u] = 0.f;
+            l2blk[4 * g + u] = l4[u];
+          }
+        }
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const x8_t<T> qa = ld8<T>(&Qs[buf][(32 * qb + l32) * KLD + 16 * ks + 8 * hh]);
@@ -251,18 +331,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
         mma32(s, qa, kf[ks]);
         mma32(dp, ga, vf[ks]);
       }
+      if (!kFold) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(&lse_s[buf][32 * qb + 8 * g + 4 * hh]);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(&D_s[buf][32 * qb + 8 * g + 4 * hh]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * g + u;
-          const float p = fast_exp2(fmaf(s[r], c, -l4[u]));
-          pf[qb][r >> 3][r & 7] = from_f<T>(p);
-          dsf[qb][r >> 3][r & 7] = from_f<T>(p * (dp[r] - d4[u]));
-        }
+        for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -l2blk[r]);
       }
+      p_ds_pack<T>(s, dp, pf[qb], dsf[qb]);
     }
 #pragma unroll
     for (int e = 0; e < NE; ++e)

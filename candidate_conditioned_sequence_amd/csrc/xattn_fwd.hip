@@ -25,8 +25,8 @@
 //    more than kTau (probabilities then stay below 2^kTau, harmless in fp32
 //    accumulation and bf16 operands); the result O / l is independent of the
 //    reference, and lse = ref + log2(l) is exact.
-//  * The ragged tail is masked (scores of rows past L_b set to -inf, their
-//    K/V never loaded and zero in LDS): no padding of the history.
+//  * The ragged tail is masked (scores of rows past L_b set to -inf): no
+//    padding of the history, and nothing past it is read.
 #include "common.h"
 #include "kernels.h"
 
@@ -120,16 +120,19 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
   const T* Kh = K + lo * d + j * DH;
   const T* Vh = V + lo * d + j * DH;
 
+  // Rows past the history are loaded as copies of its last row (unmasked
+  // loads: no EXEC writes between MFMAs): their scores are set to -inf, so
+  // their probabilities are exactly 0 and they add nothing.
   x8_t<T> kr[NCH], vr[NCH];
   auto load_tile = [&](int t) {
     const int nvalid = min(kBN, L - t * kBN);
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = tid + i * kNW * 64;
-      const int row = ch / CPR, e0 = 8 * (ch % CPR);
+      const int row = min(ch / CPR, nvalid - 1), e0 = 8 * (ch % CPR);
       const int64_t off = (int64_t)(t * kBN + row) * d + e0;
-      kr[i] = row < nvalid ? ld8<T>(Kh + off) : zero8<T>();
-      vr[i] = row < nvalid ? ld8<T>(Vh + off) : zero8<T>();
+      kr[i] = ld8<T>(Kh + off);
+      vr[i] = ld8<T>(Vh + off);
     }
   };
   auto store_tile = [&](int buf) {
@@ -196,7 +199,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      tmax[qb] = fmaxf(mx, __shfl_xor(mx, 32));
+      tmax[qb] = half_max(mx);
       need |= tmax[qb] > kTau;
     }
     if (__ballot(need)) {
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
 #pragma unroll
   for (int qb = 0; qb < NQ; ++qb) {
     const int q = qbase + 32 * qb + l32;
-    const float ltot = lsum[qb] + __shfl_xor(lsum[qb], 32);
+    const float ltot = half_sum(lsum[qb]);
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (q < QR) {
       T* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
