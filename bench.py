@@ -200,7 +200,7 @@ def main():
     # Roofline of the dominant call.  xattn_fwd is a single kernel launch.
     attn_ms = avg["xattn_fwd"]
     attn_tflops = f["attn_fwd"] / (attn_ms * 1e-3) / 1e12
-    kname = "xattn_fwd_kernel<bf16,64,64,4>"
+    kname = "xattn_fwd_pp_kernel<64>"
     tr = XATTN_FWD_TRAFFIC
     traffic = None
     if tr is not None and tr["kernel"] == kname:

@@ -88,6 +88,18 @@ WHALE_DEV bf16x4 lds_tr4(const bf16* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
+// LDS reads from a 32-bit LDS byte address (one base register plus an
+// immediate offset per read).
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+WHALE_DEV uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+WHALE_DEV bf16x8 lds_ld8(uint32_t a) { return *(const lds_bf16x8*)(uintptr_t)a; }
+WHALE_DEV bf16x4 lds_tr4_at(uint32_t a) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)a);
+  return __builtin_bit_cast(bf16x4, v);
+}
+
 template <typename T> WHALE_DEV x8_t<T> lds_colA(const T* X, int ld, int r0, int c0, int lane);
 
 template <> WHALE_DEV bf16x8 lds_colA<bf16>(const bf16* X, int ld, int r0, int c0, int lane) {

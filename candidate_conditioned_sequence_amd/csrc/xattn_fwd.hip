@@ -157,19 +157,29 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     const int nvalid = min(kBN, L - t * kBN);
 
     // Scores of two 32-row key blocks, accumulated onto -ref (bf16) or 0.
+    // All K operands are read first (one LDS wait), then the 16 MFMAs are
+    // issued at raised wave priority, so the other wave's softmax fills in.
+    __builtin_amdgcn_s_setprio(1);
     f32x16 s[2][NQ];
+    x8_t<T> ka[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const x8_t<T> a = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
 #pragma unroll
         for (int qb = 0; qb < NQ; ++qb) {
           if (ks == 0) s[kb][qb] = bias[qb];
-          mma32(s[kb][qb], a, qf[qb][ks]);
+          mma32(s[kb][qb], ka[kb][ks], qf[qb][ks]);
         }
       }
     }
+    __builtin_amdgcn_sched_group_barrier(0x0100, 2 * KS, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS * NQ, 0);
+    __builtin_amdgcn_s_setprio(0);
     if (!kFold) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -227,7 +237,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     }
 
     // P^T = exp2(t), packed pairwise into the B operands; per-lane-half row
-    // sums (bf16: of the rounded values the product uses).
+    // sums of the fp32 values with plain adds (a v_dot2 on the packed pairs
+    // would share the matrix core with the other wave's MFMAs).
     x8_t<T> pf[2][NQ][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -242,8 +253,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
               const int r = 8 * mm + 2 * v;
               f32x2 pp = {fast_exp2(s[kb][qb][r]), fast_exp2(s[kb][qb][r + 1])};
               const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
-              const bf16x2 one = {(bf16)1.f, (bf16)1.f};
-              lsum[qb] = __builtin_amdgcn_fdot2_f32_bf16(pk, one, lsum[qb], false);
+              lsum[qb] += pp[0];
+              lsum[qb] += pp[1];
               words[v] = __builtin_bit_cast(unsigned, pk);
             }
             pf[kb][qb][mm] = __builtin_bit_cast(bf16x8, words);
@@ -261,9 +272,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     // hh is history row 4*hh + u (u < 4) or 8 + 4*hh + (u - 4) of the
     // 16-row step, matching the accumulator rows of P^T.
 #pragma unroll
-    for (int e = 0; e < NE; ++e)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int e = 0; e < NE; ++e)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
           const x8_t<T> a = lds_colA<T>(&Vs[buf][0], KLD, 32 * kb + 16 * mm, 32 * e, lane);
@@ -298,6 +309,270 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
   }
 }
 
+// ------------------------------------------------------------ ping-pong
+// bf16 kernel for many queries per request.  A workgroup of 8 waves serves
+// 512 queries of one (request, head): waves 0-3 form group A and 4-7 group B,
+// so every SIMD holds one wave of each.  Every wave runs the same loop:
+//   MFMA(u): scores of tile u and the PV product of tile u-1 (32 MFMAs and the
+//            LDS reads feeding them), barrier,
+//   VALU(u): tile traffic, max, rare rescale, exponentials, packing and row
+//            sums of tile u, barrier,
+// and group B starts one barrier late (A ends one barrier later), so between
+// two barriers one wave of each SIMD feeds the matrix core while the other
+// does the softmax.  Row sums use plain fp32 adds: a packed bf16 dot
+// instruction would occupy the matrix core the other wave is using.
+//
+// Tiles of 64 history rows rotate through 3 LDS buffers.  In its VALU(v)
+// phase group A stores K of tile v+1 and starts loading K of tile v+2; group
+// B does the same for V (its VALU(v) is one phase later, and V of a tile is
+// first read one tile later than K).  Each buffer is reused only after both
+// groups' last read of it, with barriers in between.  The phase barrier waits
+// only for this wave's LDS traffic (lgkmcnt), so the global loads stay in
+// flight across it.
+constexpr int kNBUF = 3;               // LDS tiles resident at once
+constexpr int kPPQ = 64;              // queries per wave
+constexpr int kPPW = 8;               // waves per workgroup
+constexpr int kPPQB = kPPQ * kPPW;    // queries per workgroup
+
+WHALE_DEV void phase_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);        // lgkmcnt(0); vmcnt and expcnt untouched
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int DH>
+__global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+    const int64_t* __restrict__ offsets, bf16* __restrict__ A, float* __restrict__ lse,
+    int d, int h, int QR, int nqb, float c, int nblocks) {
+  constexpr int NQ = kPPQ / 32, KS = DH / 16, NE = DH / 32;
+  constexpr int KLD = DH + 8, CPR = DH / 8;
+  constexpr int NCH = kBN * CPR / (4 * 64);      // chunks per thread of one tensor (4 waves per tensor)
+  static_assert(NCH >= 1 && kBN * CPR % (4 * 64) == 0, "tile/threads mismatch");
+  constexpr uint32_t kBufBytes = kBN * KLD * 2;
+  __shared__ __attribute__((aligned(32))) bf16 Ks[kNBUF][kBN * KLD];
+  __shared__ __attribute__((aligned(32))) bf16 Vs[kNBUF][kBN * KLD];
+
+  const int lid = xcd_remap(blockIdx.x, nblocks);
+  const int qbi = lid % nqb;
+  const int bj = lid / nqb;
+  const int j = bj % h, b = bj / h;
+  const int64_t lo = offsets[b];
+  const int L = (int)(offsets[b + 1] - lo);
+  const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int grp = wv >> 2;                                // 0 = A, 1 = B
+  const int gtid = tid & 255;                             // thread index within the group
+  const int64_t qrow0 = (int64_t)b * QR;
+  const int qbase = qbi * kPPQB + wv * kPPQ;
+
+  bf16x8 qf[NQ][KS];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const int q = qbase + 32 * qb + l32;
+    const bf16* src = Q + (qrow0 + q) * d + j * DH + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[qb][ks] = (q < QR) ? ld8<bf16>(src + 16 * ks) : zero8<bf16>();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qf[qb][ks][u] = (bf16)((float)qf[qb][ks][u] * c);
+    }
+  }
+
+  f32x16 oacc[NE][NQ], s[2][NQ];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+    for (int e = 0; e < NE; ++e) oacc[e][qb] = zero16();
+  float mref[NQ], lsum[NQ];
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = 0.f; lsum[qb] = 0.f; }
+  bf16x8 pf[2][NQ][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) { pf[kb][qb][0] = zero8<bf16>(); pf[kb][qb][1] = zero8<bf16>(); }
+
+  const int ntiles = (L + kBN - 1) / kBN;
+  // LDS byte addresses: per-lane part + uniform buffer offset + constants.
+  const uint32_t kbase = lds_addr(&Ks[0][0]) + 2 * (l32 * KLD + 8 * hh);
+  const uint32_t vbase = lds_addr(&Vs[0][0]) + 2 * lds_colA_lane<bf16>(KLD, lane);
+
+  // Group A moves K tiles, group B V tiles.  Rows past the history are copies
+  // of its last row (unmasked loads); their scores are set to -inf.
+  const bf16* Gsrc = (grp == 0 ? K : V) + lo * d + j * DH;
+  bf16* Gdst = grp == 0 ? &Ks[0][0] : &Vs[0][0];
+  bf16x8 xr[NCH];
+  auto load_tile = [&](int t) {
+    const int last = L - 1 - t * kBN;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = gtid + i * 256;
+      const int row = min(ch / CPR, last), e0 = 8 * (ch % CPR);
+      xr[i] = ld8<bf16>(Gsrc + (int64_t)(t * kBN + row) * d + e0);
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = gtid + i * 256;
+      const int row = ch / CPR, e0 = 8 * (ch % CPR);
+      st8<bf16>(Gdst + buf * (kBN * KLD) + row * KLD + e0, xr[i]);
+    }
+  };
+
+  // MFMA step u: scores of tile u onto -ref, and O += V P of tile u-1.  For
+  // u = ntiles the scores read a resident buffer and are never used; for
+  // u = 0 the product is skipped.
+  auto mfma_step = [&](int u) {
+    __builtin_amdgcn_s_setprio(1);
+    const uint32_t kaddr = kbase + (uint32_t)(u % kNBUF) * kBufBytes;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      bf16x8 ka[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_ld8(kaddr + 2 * (32 * kb * KLD + 16 * ks));
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb) {
+          if (ks == 0) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kb][qb][r] = -mref[qb];
+          }
+          mma32(s[kb][qb], ka[ks], qf[qb][ks]);
+        }
+    }
+    if (u >= 1) {
+      const uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kBufBytes;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int mm = 0; mm < 2; ++mm) {
+            const uint32_t o = vaddr + 2 * ((32 * kb + 16 * mm) * KLD + 32 * e);
+            const bf16x8 a = cat44<bf16>(lds_tr4_at(o), lds_tr4_at(o + 2 * 8 * KLD));
+#pragma unroll
+            for (int qb = 0; qb < NQ; ++qb) mma32(oacc[e][qb], a, pf[kb][qb][mm]);
+          }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // VALU step u: tile traffic, then the softmax of tile u's scores into pf
+  // (row sums into lsum).
+  auto valu_step = [&](int u) {
+    if (u + 1 < ntiles) store_tile((u + 1) % kNBUF);
+    if (u + 2 < ntiles) load_tile(u + 2);
+    const int nvalid = min(kBN, L - u * kBN);
+    if (nvalid < kBN) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + acc_row(r, hh) >= nvalid) s[kb][qb][r] = -INFINITY;
+    }
+    float tmax[NQ];
+    bool need = u == 0;
+#pragma unroll
+    for (int qb = 0; qb < NQ; ++qb) {
+      float mx = s[0][qb][0];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      tmax[qb] = half_max(mx);
+      need |= tmax[qb] > kTau;
+    }
+    if (__ballot(need)) {
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) {
+        const float sh = (u == 0 || tmax[qb] > kTau) ? tmax[qb] : 0.f;
+        const float alpha = u == 0 ? 0.f : fast_exp2(-sh);
+        mref[qb] += sh;
+        lsum[qb] *= alpha;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][qb][r] -= sh;
+#pragma unroll
+        for (int e = 0; e < NE; ++e)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[e][qb][r] *= alpha;
+      }
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          u32x4 words;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int r = 8 * mm + 2 * v;
+            const f32x2 pp = {fast_exp2(s[kb][qb][r]), fast_exp2(s[kb][qb][r + 1])};
+            lsum[qb] += pp[0];
+            lsum[qb] += pp[1];
+            words[v] = __builtin_bit_cast(unsigned, __builtin_convertvector(pp, bf16x2));
+          }
+          pf[kb][qb][mm] = __builtin_bit_cast(bf16x8, words);
+        }
+  };
+
+  // Prologue: tile 0 of both tensors into buffer 0 (each group its tensor),
+  // tile 1 of this group's tensor into registers.
+  if (ntiles > 0) { load_tile(0); store_tile(0); }
+  if (ntiles > 1) load_tile(1);
+  phase_barrier();
+
+  if (grp == 1) phase_barrier();
+  for (int u = 0; u <= ntiles; ++u) {
+    mfma_step(u);
+    phase_barrier();
+    if (u < ntiles) valu_step(u);
+    phase_barrier();
+  }
+  if (grp == 0) phase_barrier();
+
+#pragma unroll
+  for (int qb = 0; qb < NQ; ++qb) {
+    const int q = qbase + 32 * qb + l32;
+    const float ltot = half_sum(lsum[qb]);
+    const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+    if (q < QR) {
+      bf16* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 o;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = (bf16)(oacc[e][qb][4 * g + u] * inv);
+          st4<bf16>(dst + 32 * e + 8 * g, o);
+        }
+      if (lse != nullptr && hh == 0)
+        lse[(qrow0 + q) * h + j] = ltot > 0.f ? (mref[qb] + log2f(ltot)) * kLn2 : -INFINITY;
+    }
+  }
+}
+
+template <int DH>
+hipError_t launch_fwd_pp(const XattnArgs& a, hipStream_t st) {
+  const int nqb = (a.QR + kPPQB - 1) / kPPQB;
+  const int64_t nblk = (int64_t)a.B * a.h * nqb;
+  if (nblk == 0) return hipSuccess;
+  const float c = a.scale * kLog2e;
+  hipLaunchKernelGGL((xattn_fwd_pp_kernel<DH>), dim3((unsigned)nblk), dim3(kPPW * 64), 0, st,
+                     (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.offsets, (bf16*)a.A, a.lse,
+                     a.d, a.h, a.QR, nqb, c, (int)nblk);
+  return hipGetLastError();
+}
+
 template <typename T, int DH, int QPW, int kNW>
 hipError_t launch_fwd_t(const XattnArgs& a, hipStream_t st) {
   constexpr int QB = kNW * QPW;
@@ -314,6 +589,9 @@ hipError_t launch_fwd_t(const XattnArgs& a, hipStream_t st) {
 template <typename T>
 hipError_t launch_fwd_dh(const XattnArgs& a, hipStream_t st) {
   const bool wide = a.QR >= 1024;
+  if constexpr (sizeof(T) == 2) {
+    if (wide && a.dh == 64) return launch_fwd_pp<64>(a, st);
+  }
   switch (a.dh) {
     case 32: return wide ? launch_fwd_t<T, 32, 64, 4>(a, st) : launch_fwd_t<T, 32, 32, 4>(a, st);
     case 64: return wide ? launch_fwd_t<T, 64, 64, 4>(a, st) : launch_fwd_t<T, 64, 32, 4>(a, st);

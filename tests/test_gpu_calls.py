@@ -39,6 +39,10 @@ XATTN_CASES = [
     ("bf16", 256, 4, 64, 32, [1000, 333]),
     ("bf16", 512, 8, 8, 16, [97, 640]),
     ("f32", 128, 2, 40, 8, [300, 5]),
+    # C*n_q >= 1024 with d_h = 64: the 8-wave ping-pong kernel (partial last
+    # query block, every ragged length class)
+    ("bf16", 256, 4, 40, 30, [0, 1, 63, 64, 65, 257, 130]),
+    ("bf16", 512, 8, 32, 32, [700, 1]),
 ]
 
 

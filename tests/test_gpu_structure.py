@@ -38,9 +38,10 @@ def _fwd(gpu, dtype, Q, K, V, L, C, n_q, h, extra_rows=0, poison=None):
     return A.cpu(), lse.cpu()
 
 
-@pytest.mark.parametrize("dtype,d,h", [("bf16", 256, 4), ("f32", 64, 2), ("bf16", 128, 4)])
-def test_single_key_returns_value_row_bitwise(gpu, dtype, d, h):
-    C, n_q, L = 3, 5, [1, 1, 0, 1]
+@pytest.mark.parametrize("dtype,d,h,C,n_q", [("bf16", 256, 4, 3, 5), ("f32", 64, 2, 3, 5), ("bf16", 128, 4, 3, 5),
+                                             ("bf16", 256, 4, 40, 30)])
+def test_single_key_returns_value_row_bitwise(gpu, dtype, d, h, C, n_q):
+    L = [1, 1, 0, 1]
     M = len(L) * C * n_q
     Q, K, V = _draw(1, (M, d), dtype), _draw(2, (3, d), dtype), _draw(3, (3, d), dtype)
     A, lse = _fwd(gpu, dtype, Q, K, V, L, C, n_q, h)
@@ -52,12 +53,13 @@ def test_single_key_returns_value_row_bitwise(gpu, dtype, d, h):
     assert torch.all(A[2 * per:3 * per] == 0) and torch.all(torch.isneginf(lse[2 * per:3 * per]))
 
 
-@pytest.mark.parametrize("hot", [0, 63, 64, 700, 1299])
-def test_one_hot_saturated_picks_exact_row(gpu, hot):
+@pytest.mark.parametrize("hot,C,n_q", [(0, 4, 8), (63, 4, 8), (64, 4, 8), (700, 4, 8), (1299, 4, 8),
+                                       (0, 32, 32), (64, 32, 32), (1299, 32, 32)])
+def test_one_hot_saturated_picks_exact_row(gpu, hot, C, n_q):
     # Score gap of 512 natural-log units: every other weight underflows to 0,
     # in any history tile.  V rows hold small integers (exact in bf16) naming
     # the row, so the exact value proves the indexing.
-    dtype, d, h, C, n_q, L = "bf16", 128, 2, 4, 8, [1300]
+    dtype, d, h, L = "bf16", 128, 2, [1300]
     M = C * n_q
     Q = np.zeros((M, d), np.float32)
     Q[:, 0] = 64.0
@@ -71,8 +73,9 @@ def test_one_hot_saturated_picks_exact_row(gpu, hot):
     assert torch.equal(A.float(), torch.from_numpy(np.repeat(V[hot:hot + 1], M, 0)))
 
 
-def test_memory_past_the_history_is_never_read(gpu):
-    dtype, d, h, C, n_q, L = "bf16", 256, 4, 5, 7, [77, 0, 130]
+@pytest.mark.parametrize("C,n_q", [(5, 7), (40, 30)])
+def test_memory_past_the_history_is_never_read(gpu, C, n_q):
+    dtype, d, h, L = "bf16", 256, 4, [77, 0, 130]
     M = len(L) * C * n_q
     Q, K, V = _draw(7, (M, d), dtype), _draw(8, (sum(L), d), dtype), _draw(9, (sum(L), d), dtype)
     A0, l0 = _fwd(gpu, dtype, Q, K, V, L, C, n_q, h)
