@@ -473,67 +473,78 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
   const T* X = (const T*)a.X;
   const T* X2 = (const T*)a.X2;
 
-  // Threads 0..127 load 8x8 blocks of G, threads 128..255 of X.  Block b:
-  // rows 8 (b % 8) .. +8 of the m-step, columns 8 (b / 8) .. +8 of the tile.
-  const bool isG = tid < 128;
-  const int b = tid & 127, rb = 8 * (b & 7), cb = 8 * (b >> 3);
-  const int col = (isG ? n0 : k0) + cb;
-  const bool cok = col < (isG ? N : K);
-  const T* src = nullptr;     // column base of this thread's 8 columns
-  const T* srcz = nullptr;    // second operand of the prologue
-  int ld = 0;
-  if (cok) {
-    if (isG) {
-      if (G2 != nullptr && col >= a.nsplit) { src = G2 + (col - a.nsplit); }
-      else src = G + col;
-      ld = a.ldg;
-      if (GPRO == 1) srcz = Gz + col;
-    } else if (PRO == WPRO_CONCAT && col >= a.ksplit) {
-      src = X2 + (col - a.ksplit); ld = a.ldx2;
-    } else {
-      src = X + col; ld = a.ldx;
-      if (PRO == WPRO_GATE_SEP) srcz = X + a.gate_H + col;
+  // Every thread moves half of one 8x8 block of G and half of the matching
+  // block of X (4 rows of 8 columns each), so the prologue work on X (norm,
+  // gate) and on G (activation derivative) is spread over all four waves.
+  // Block bk: rows 8 (bk % 8) .. +8 of the m-step, columns 8 (bk / 8) .. +8 of
+  // the tile; this thread takes rows 4*half .. +4 of it.
+  const int bk = tid >> 1, half = tid & 1;
+  const int rb = 8 * (bk & 7) + 4 * half, cb = 8 * (bk >> 3);
+  const int gcol = n0 + cb, xcol = k0 + cb;
+  const T* gsrc = nullptr;    // column base of this thread's 8 G columns
+  const T* gsrcz = nullptr;   // activation input for the G prologue
+  const T* xsrc = nullptr;    // column base of this thread's 8 X columns
+  const T* xsrcz = nullptr;   // second operand of the X prologue
+  int xld = a.ldx;
+  if (gcol < N) {
+    gsrc = (G2 != nullptr && gcol >= a.nsplit) ? G2 + (gcol - a.nsplit) : G + gcol;
+    if (GPRO == 1) gsrcz = Gz + gcol;
+  }
+  if (xcol < K) {
+    if (PRO == WPRO_CONCAT && xcol >= a.ksplit) { xsrc = X2 + (xcol - a.ksplit); xld = a.ldx2; }
+    else {
+      xsrc = X + xcol;
+      if (PRO == WPRO_GATE_SEP) xsrcz = X + a.gate_H + xcol;
     }
   }
   float gm[8], bt[8];
-  if (!isG && PRO == WPRO_NORM && cok) {
+  if (PRO == WPRO_NORM && xsrc != nullptr) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) { gm[u] = a.gamma[col + u]; bt[u] = a.norm_kind == 0 ? a.beta[col + u] : 0.f; }
+    for (int u = 0; u < 8; ++u) { gm[u] = a.gamma[xcol + u]; bt[u] = a.norm_kind == 0 ? a.beta[xcol + u] : 0.f; }
   }
 
-  x8_t<T> r8[8];
+  x8_t<T> gr[4], xr[4];
   auto load = [&](int64_t mbase) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < 4; ++i) {
       const int64_t m = mbase + rb + i;
-      if (src == nullptr || m >= me) { r8[i] = zero8<T>(); continue; }
-      const x8_t<T> v = ld8<T>(src + m * ld);
-      if (isG) {
-        r8[i] = GPRO == 1 ? dact8<T>(v, ld8<T>(srcz + m * ld)) : v;
-      } else if (PRO == WPRO_GATE_TIED) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { const float uf = to_f(v[e]); r8[i][e] = from_f<T>(siluf_(uf) * uf); }
-      } else if (PRO == WPRO_GATE_SEP) {
-        const x8_t<T> uu = ld8<T>(srcz + m * ld);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r8[i][e] = from_f<T>(siluf_(to_f(v[e])) * to_f(uu[e]));
-      } else if (PRO == WPRO_NORM && a.norm_kind != 2) {
-        const float mean = a.stats[2 * m], rstd = a.stats[2 * m + 1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r8[i][e] = from_f<T>((to_f(v[e]) - mean) * rstd * gm[e] + bt[e]);
+      const bool mok = m < me;
+      if (gsrc != nullptr && mok) {
+        const x8_t<T> v = ld8<T>(gsrc + m * a.ldg);
+        gr[i] = GPRO == 1 ? dact8<T>(v, ld8<T>(gsrcz + m * a.ldg)) : v;
       } else {
-        r8[i] = v;
+        gr[i] = zero8<T>();
+      }
+      if (xsrc != nullptr && mok) {
+        const x8_t<T> v = ld8<T>(xsrc + m * xld);
+        if (PRO == WPRO_GATE_TIED) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) { const float uf = to_f(v[e]); xr[i][e] = from_f<T>(siluf_(uf) * uf); }
+        } else if (PRO == WPRO_GATE_SEP) {
+          const x8_t<T> uu = ld8<T>(xsrcz + m * xld);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[i][e] = from_f<T>(siluf_(to_f(v[e])) * to_f(uu[e]));
+        } else if (PRO == WPRO_NORM && a.norm_kind != 2) {
+          const float mean = a.stats[2 * m], rstd = a.stats[2 * m + 1];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) xr[i][e] = from_f<T>((to_f(v[e]) - mean) * rstd * gm[e] + bt[e]);
+        } else {
+          xr[i] = v;
+        }
+      } else {
+        xr[i] = zero8<T>();
       }
     }
   };
+  // Transposed into [column][m]: 4 consecutive m of one column per write.
   auto store = [&](int buf) {
-    T* dst = isG ? &Gt[buf][0] : &Xt[buf][0];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      x8_t<T> t;
+      x4_t<T> tg, tx;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) t[i] = r8[i][e];
-      st8<T>(dst + (cb + e) * LDW + rb, t);
+      for (int i = 0; i < 4; ++i) { tg[i] = gr[i][e]; tx[i] = xr[i][e]; }
+      st4<T>(&Gt[buf][(cb + e) * LDW + rb], tg);
+      st4<T>(&Xt[buf][(cb + e) * LDW + rb], tx);
     }
   };
 
