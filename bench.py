@@ -27,13 +27,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of one xattn_fwd_kernel<bf16,64,64,4> launch on this workload:
+# HBM traffic of one xattn_fwd_pp_kernel<64> launch on this workload:
 # rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
 # the counter reads for a 512 MiB elementwise copy (x2.000 and x1.000).  Taken
-# from profiles/xattn_fwd_kernel_c3_L10k_hbm_traffic.md; must be re-measured
+# from profiles/xattn_fwd_pp_kernel_c3_L10k_hbm_traffic.md; must be re-measured
 # (or set to None) whenever that kernel changes.
-XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_kernel<bf16,64,64,4>",
-                     "fetch_kib": 709713, "fetch_scale": 2.000, "write_kib": 143495, "write_scale": 1.000}
+XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_pp_kernel<64>",
+                     "fetch_kib": 705614, "fetch_scale": 2.000, "write_kib": 136159, "write_scale": 1.000}
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 
