@@ -216,6 +216,7 @@ size_t whale_swiglu_ffn_workspace_size(const whale_dims_t* dims, whale_dtype_t d
   (void)gate;
   Carve c(nullptr);
   c.take((size_t)s.M * H * esz(dtype));      // G
+  c.take((size_t)s.M * s.d * esz(dtype));    // X_f = Norm_f(F)
   return c.used;
 }
 
@@ -238,12 +239,19 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   const bool bf = dtype == WHALE_BF16;
   Carve c(workspace);
   void* G = c.take((size_t)s.M * H * esz(dtype));
-  if (norm != WHALE_NORM_NONE) WHALE_TRY(launch_norm_stats(F, stats_f, s.M, s.d, (int)norm, eps, bf, stream));
+  void* Xf = c.take((size_t)s.M * s.d * esz(dtype));
+  // X_f = Norm_f(F) once (statistics saved for the backward), so that the
+  // up projection does not renormalise F for every block of its H columns.
+  const void* Xin = F;
+  if (norm != WHALE_NORM_NONE) {
+    WHALE_TRY(launch_norm_apply(F, nullptr, stats_f, g_f, b_f, Xf, s.M, s.d, (int)norm, eps, bf, stream));
+    Xin = Xf;
+  }
   GemmArgs a = gemm_defaults();
-  a.X = F; a.ldx = s.d; a.stats = stats_f; a.gamma = g_f; a.beta = b_f; a.norm_kind = (int)norm;
+  a.X = Xin; a.ldx = s.d;
   a.W = W_U; a.ldw = s.d; a.Y = G; a.ldy = H; a.Z = U_saved;
   a.M = s.M; a.K = s.d;
-  a.pro = norm == WHALE_NORM_NONE ? PRO_PLAIN : PRO_NORM;
+  a.pro = PRO_PLAIN;
   if (gate == WHALE_GATE_SHARED) { a.N = H; a.epi = EPI_GATE_TIED; a.ldz = H; }
   else { a.N = 2 * H; a.epi = EPI_GATE_SEP; a.ldz = 2 * H; }
   WHALE_TRY(launch_gemm_nt(a, bf, stream));
@@ -294,6 +302,7 @@ size_t whale_fusion_mlp_bwd_workspace_size(const whale_dims_t* dims, whale_dtype
   Carve c(nullptr);
   c.take((size_t)2 * s.d * s.d * esz(dtype));        // W_F^T [2d, d]
   c.take(wgrad_partial_bytes(s.M, s.d, 2 * s.d));
+  c.take((size_t)s.M * s.d * esz(dtype));            // dZ
   return c.used;
 }
 
@@ -313,17 +322,23 @@ whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   Carve c(workspace);
   void* WFt = c.take((size_t)2 * d * d * esz(dtype));
   float* part = (float*)c.take(wgrad_partial_bytes(s.M, d, 2 * d));
-  // dW_F = dZ^T [A, H_w], dZ = dF * act'(Z) formed in the loader.
-  Wg w(dF, d, A, d, WPRO_CONCAT, s.M, d, 2 * d, dW_F, part);
+  void* dZw = c.take((size_t)s.M * d * esz(dtype));
+  // dZ = dF * act'(Z) once; both products below read it.
+  const void* dZ = dF;
+  if (silu) {
+    WHALE_TRY(launch_dact(dF, Z_saved, dZw, (int64_t)s.M * d, bf, stream));
+    dZ = dZw;
+  }
+  // dW_F = dZ^T [A, H_w]
+  Wg w(dZ, d, A, d, WPRO_CONCAT, s.M, d, 2 * d, dW_F, part);
   w.concat(H_w, d, d);
-  if (silu) w.gz(Z_saved);
   WHALE_TRY(w.run(bf, stream));
   // [dA | dH_w - dF] = dZ W_F: one GEMM against W_F^T [2d, d]; columns >= d get the residual dF.
   WHALE_TRY(launch_transpose(W_F, d, 2 * d, WFt, d, 0, bf, stream));
   GemmArgs g = gemm_defaults();
-  g.X = dF; g.ldx = d; g.X2 = Z_saved; g.ldx2 = d;
+  g.X = dZ; g.ldx = d;
   g.W = WFt; g.ldw = d; g.Y = dA; g.Y2 = dH_w; g.ldy = d; g.nsplit = d; g.R = dF; g.ldr = d;
-  g.M = s.M; g.N = 2 * d; g.K = d; g.pro = silu ? PRO_DACT : PRO_PLAIN; g.epi = EPI_DUAL_RESID2;
+  g.M = s.M; g.N = 2 * d; g.K = d; g.pro = PRO_PLAIN; g.epi = EPI_DUAL_RESID2;
   return ret(launch_gemm_nt(g, bf, stream));
 }
 
@@ -340,6 +355,7 @@ size_t whale_swiglu_ffn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype
   c.take(p1 > p2 ? p1 : p2);
   c.take(norm_part_bytes(s.M, s.d));
   c.take((size_t)colsum_scratch_floats(s.d) * 4);
+  c.take((size_t)s.M * s.d * esz(dtype));            // X_f
   return c.used;
 }
 
@@ -369,6 +385,7 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   float* part = (float*)c.take(p1 > p2 ? p1 : p2);
   float* npart = (float*)c.take(norm_part_bytes(s.M, d));
   float* cscr = (float*)c.take((size_t)colsum_scratch_floats(d) * 4);
+  void* Xf = c.take((size_t)s.M * d * esz(dtype));
 
   // dW_D = dY^T G, with G recomputed from U in the loader.
   Wg w1(dY, d, U_saved, Hu, sep ? WPRO_GATE_SEP : WPRO_GATE_TIED, s.M, d, H, dW_D, part);
@@ -379,9 +396,14 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   g.X = dY; g.ldx = d; g.W = WDt; g.ldw = d; g.Y = dU; g.ldy = Hu; g.Z = (void*)U_saved; g.ldz = Hu;
   g.M = s.M; g.N = H; g.K = d; g.pro = PRO_PLAIN; g.epi = sep ? EPI_DGATE_SEP : EPI_DGATE_TIED;
   WHALE_TRY(launch_gemm_nt(g, bf, stream));
-  // dW_U = dU^T Norm_f(F)
-  Wg w2(dU, Hu, F, d, WPRO_NORM, s.M, Hu, d, dW_U, part);
-  WHALE_TRY(w2.norm(stats_f, g_f, b_f, nk).run(bf, stream));
+  // dW_U = dU^T X_f, X_f = Norm_f(F) formed once from the saved statistics
+  const void* Xin = F;
+  if (norm != WHALE_NORM_NONE) {
+    WHALE_TRY(launch_norm_apply(F, stats_f, nullptr, g_f, b_f, Xf, s.M, d, nk, eps, bf, stream));
+    Xin = Xf;
+  }
+  Wg w2(dU, Hu, Xin, d, WPRO_PLAIN, s.M, Hu, d, dW_U, part);
+  WHALE_TRY(w2.run(bf, stream));
   // dF = dY + Norm_f backward(dU W_U), one kernel.
   WHALE_TRY(launch_transpose(W_U, Hu, d, WUt, Hu, 0, bf, stream));     // [d, Hu]
   WHALE_TRY(norm_bwd_gemm(dU, Hu, nullptr, 0, WUt, Hu, Hu, F, stats_f, g_f, nk, dY, dF, npart, s.M, d, bf, stream));
@@ -403,6 +425,8 @@ size_t whale_proj_qkv_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t
   c.take(norm_part_bytes(s.M, s.d));
   c.take(norm_part_bytes(s.T, s.d));
   c.take((size_t)colsum_scratch_floats(s.d) * 4);
+  c.take((size_t)s.M * s.d * esz(dtype));            // X_q
+  c.take((size_t)s.T * s.d * esz(dtype));            // X_s
   return c.used;
 }
 
@@ -435,14 +459,26 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
   float* npq = (float*)c.take(norm_part_bytes(s.M, d));
   float* npk = (float*)c.take(norm_part_bytes(s.T, d));
   float* cscr = (float*)c.take((size_t)colsum_scratch_floats(d) * 4);
+  void* Xq = c.take((size_t)s.M * d * esz(dtype));
+  void* Xs = c.take((size_t)s.T * d * esz(dtype));
 
-  // Weight gradients with the normalised inputs recomputed in the loader;
-  // dW_K and dW_V share one pass over H_s.
-  Wg wq(dQ, d, H_w, d, WPRO_NORM, s.M, d, d, dW_Q, part);
-  WHALE_TRY(wq.norm(stats_q, g_q, b_q, nk).run(bf, stream));
+  // Weight gradients against the normalised inputs, formed once from the
+  // saved statistics; dW_K and dW_V share one pass over X_s.
+  const void* Xqin = H_w;
+  const void* Xsin = H_s;
+  if (norm != WHALE_NORM_NONE) {
+    WHALE_TRY(launch_norm_apply(H_w, stats_q, nullptr, g_q, b_q, Xq, s.M, d, nk, eps, bf, stream));
+    Xqin = Xq;
+    if (s.T > 0) {
+      WHALE_TRY(launch_norm_apply(H_s, stats_kv, nullptr, g_kv, b_kv, Xs, s.T, d, nk, eps, bf, stream));
+      Xsin = Xs;
+    }
+  }
+  Wg wq(dQ, d, Xqin, d, WPRO_PLAIN, s.M, d, d, dW_Q, part);
+  WHALE_TRY(wq.run(bf, stream));
   if (s.T > 0) {
-    Wg wkv(dK, d, H_s, d, WPRO_NORM, s.T, 2 * d, d, dW_K, part);
-    WHALE_TRY(wkv.norm(stats_kv, g_kv, b_kv, nk).dual(dV, d, dW_V).run(bf, stream));
+    Wg wkv(dK, d, Xsin, d, WPRO_PLAIN, s.T, 2 * d, d, dW_K, part);
+    WHALE_TRY(wkv.dual(dV, d, dW_V).run(bf, stream));
   } else {
     WHALE_TRY(launch_fill_zero(dW_K, (int64_t)d * d, stream));
     WHALE_TRY(launch_fill_zero(dW_V, (int64_t)d * d, stream));

@@ -28,6 +28,14 @@ int xattn_bwd_splits(int B, int h, int QR, int max_L, int dh);
 // ---------------------------------------------------------------- norms
 // Row statistics (mean, rstd) of x [rows, n]; mean = 0 for RMSNorm.
 // kind: 0 LayerNorm, 1 RMSNorm.
+// y = Norm(x) (gamma, beta applied; beta ignored for RMSNorm).  stats_in
+// given: use those statistics; else compute them (and write stats_out if
+// given).  kind: 0 LayerNorm, 1 RMSNorm.
+hipError_t launch_norm_apply(const void* x, const float* stats_in, float* stats_out, const float* gamma,
+                             const float* beta, void* y, int64_t rows, int n, int kind, float eps, bool bf16_data,
+                             hipStream_t st);
+// dZ = dF * SiLU'(Z) over n elements (n % 8 == 0).
+hipError_t launch_dact(const void* dF, const void* Z, void* dZ, int64_t n, bool bf16_data, hipStream_t st);
 hipError_t launch_norm_stats(const void* x, float* stats, int64_t rows, int n, int kind, float eps,
                              bool bf16_data, hipStream_t st);
 // Column sums of per-tile partials part [nblk, 2, n] (row 0: dgamma terms,

@@ -16,38 +16,120 @@
 
 namespace {
 
-// A group of n/8 lanes owns one row, each lane 8 contiguous elements.
-template <typename T>
-__global__ __launch_bounds__(256) void norm_stats_kernel(const T* __restrict__ x, float* __restrict__ stats,
-                                                         int64_t rows, int n, int kind, float eps) {
-  const int lpr = n / 8;                   // power of two, 8..64
-  const int rpw = 64 / lpr;                // rows per wave
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row = ((int64_t)blockIdx.x * 4 + w) * rpw + lane / lpr;
-  const int cl = lane % lpr;
-  const bool ok = row < rows;
-  float v[8];
-  if (ok) {
-    const x8_t<T> r = ld8<T>(x + row * n + 8 * cl);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = to_f(r[u]);
-  } else {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = 0.f;
-  }
+// A group of n/8 lanes owns one row, each lane 8 contiguous elements; every
+// group handles kRows rows (loads for all of them issued first), so a block
+// of 4 waves covers 4 * (64 / (n/8)) * kRows rows.
+constexpr int kRows = 4;
+
+// Row statistics of one row held as 8 values per lane of a group of lpr lanes.
+WHALE_DEV void row_stats(const float* v, int lpr, int n, int kind, float eps, float& mean, float& rstd) {
   float s = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) s += v[u];
   for (int o = 1; o < lpr; o <<= 1) s += __shfl_xor(s, o);
-  const float mean = kind == 0 ? s / n : 0.f;
+  mean = kind == 0 ? s / n : 0.f;
   float q = 0.f;
 #pragma unroll
   for (int u = 0; u < 8; ++u) { const float dl = v[u] - mean; q += dl * dl; }
   for (int o = 1; o < lpr; o <<= 1) q += __shfl_xor(q, o);
-  if (ok && cl == 0) {
-    stats[2 * row] = mean;
-    stats[2 * row + 1] = 1.f / sqrtf(q / n + eps);
+  rstd = 1.f / sqrtf(q / n + eps);
+}
+
+template <typename T>
+WHALE_DEV void load_rows(const T* __restrict__ x, int64_t row0, int64_t rstep, int64_t rows, int n, int cl,
+                         float (&v)[kRows][8]) {
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int64_t row = row0 + k * rstep;
+    if (row < rows) {
+      const x8_t<T> r = ld8<T>(x + row * n + 8 * cl);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[k][u] = to_f(r[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[k][u] = 0.f;
+    }
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void norm_stats_kernel(const T* __restrict__ x, float* __restrict__ stats,
+                                                         int64_t rows, int n, int kind, float eps) {
+  const int lpr = n / 8;                   // power of two, 8..64
+  const int rpw = 64 / lpr;                // rows per wave and pass
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rstep = 4 * rpw;           // rows per block and pass
+  const int64_t row0 = (int64_t)blockIdx.x * rstep * kRows + w * rpw + lane / lpr;
+  const int cl = lane % lpr;
+  float v[kRows][8];
+  load_rows<T>(x, row0, rstep, rows, n, cl, v);
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int64_t row = row0 + k * rstep;
+    float mean, rstd;
+    row_stats(v[k], lpr, n, kind, eps, mean, rstd);
+    if (row < rows && cl == 0) {
+      stats[2 * row] = mean;
+      stats[2 * row + 1] = rstd;
+    }
+  }
+}
+
+// Normalised rows y = (x - mean) * rstd * gamma + beta (beta = 0 for RMSNorm)
+// for the GEMMs that consume them, with the statistics computed here
+// (stats_in == nullptr, written to stats_out if given) or read from a
+// previous pass.  Same layout as norm_stats_kernel; HBM-bound.
+template <typename T>
+__global__ __launch_bounds__(256) void norm_apply_kernel(const T* __restrict__ x, const float* __restrict__ stats_in,
+                                                         float* __restrict__ stats_out, const float* __restrict__ gamma,
+                                                         const float* __restrict__ beta, T* __restrict__ y,
+                                                         int64_t rows, int n, int kind, float eps) {
+  const int lpr = n / 8;
+  const int rpw = 64 / lpr;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t rstep = 4 * rpw;
+  const int64_t row0 = (int64_t)blockIdx.x * rstep * kRows + w * rpw + lane / lpr;
+  const int cl = lane % lpr;
+  float gm[8], bt[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    gm[u] = gamma[8 * cl + u];
+    bt[u] = 0.f;
+    if (kind == 0) bt[u] = beta[8 * cl + u];          // beta may be null for RMSNorm
+  }
+  float v[kRows][8];
+  load_rows<T>(x, row0, rstep, rows, n, cl, v);
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    const int64_t row = row0 + k * rstep;
+    const bool ok = row < rows;
+    float mean, rstd;
+    if (stats_in != nullptr) {
+      mean = ok ? stats_in[2 * row] : 0.f;
+      rstd = ok ? stats_in[2 * row + 1] : 0.f;
+    } else {
+      row_stats(v[k], lpr, n, kind, eps, mean, rstd);
+      if (ok && cl == 0 && stats_out != nullptr) { stats_out[2 * row] = mean; stats_out[2 * row + 1] = rstd; }
+    }
+    if (!ok) continue;
+    x8_t<T> o;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) o[u] = from_f<T>((v[k][u] - mean) * rstd * gm[u] + bt[u]);
+    st8<T>(y + row * n + 8 * cl, o);
+  }
+}
+
+// dZ = dF * SiLU'(Z), elementwise (8 per thread).
+template <typename T>
+__global__ __launch_bounds__(256) void dact_kernel(const T* __restrict__ dF, const T* __restrict__ Z, T* __restrict__ dZ,
+                                                   int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const x8_t<T> g = ld8<T>(dF + 8 * i), z = ld8<T>(Z + 8 * i);
+  x8_t<T> o;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) o[u] = from_f<T>(to_f(g[u]) * dsiluf_(to_f(z[u])));
+  st8<T>(dZ + 8 * i, o);
 }
 
 // Level 1: block (column group cg of 64 columns, row split s) sums rows
@@ -85,12 +167,39 @@ constexpr int kColsumSplits = 64;
 hipError_t launch_norm_stats(const void* x, float* stats, int64_t rows, int n, int kind, float eps,
                              bool bf16_data, hipStream_t st) {
   if (rows == 0) return hipSuccess;
-  const int rpb = 4 * (64 / (n / 8));      // rows per block
+  const int rpb = 4 * (64 / (n / 8)) * kRows;   // rows per block
   const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
   if (bf16_data)
     hipLaunchKernelGGL(norm_stats_kernel<bf16>, dim3(grid), dim3(256), 0, st, (const bf16*)x, stats, rows, n, kind, eps);
   else
     hipLaunchKernelGGL(norm_stats_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)x, stats, rows, n, kind, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_apply(const void* x, const float* stats_in, float* stats_out, const float* gamma,
+                             const float* beta, void* y, int64_t rows, int n, int kind, float eps, bool bf16_data,
+                             hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int rpb = 4 * (64 / (n / 8)) * kRows;
+  const unsigned grid = (unsigned)((rows + rpb - 1) / rpb);
+  if (bf16_data)
+    hipLaunchKernelGGL(norm_apply_kernel<bf16>, dim3(grid), dim3(256), 0, st, (const bf16*)x, stats_in, stats_out,
+                       gamma, beta, (bf16*)y, rows, n, kind, eps);
+  else
+    hipLaunchKernelGGL(norm_apply_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)x, stats_in, stats_out,
+                       gamma, beta, (float*)y, rows, n, kind, eps);
+  return hipGetLastError();
+}
+
+hipError_t launch_dact(const void* dF, const void* Z, void* dZ, int64_t n, bool bf16_data, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const int64_t n8 = n / 8;
+  const unsigned grid = (unsigned)((n8 + 255) / 256);
+  if (bf16_data)
+    hipLaunchKernelGGL(dact_kernel<bf16>, dim3(grid), dim3(256), 0, st, (const bf16*)dF, (const bf16*)Z, (bf16*)dZ, n8);
+  else
+    hipLaunchKernelGGL(dact_kernel<float>, dim3(grid), dim3(256), 0, st, (const float*)dF, (const float*)Z,
+                       (float*)dZ, n8);
   return hipGetLastError();
 }
 

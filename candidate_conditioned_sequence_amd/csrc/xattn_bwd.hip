@@ -165,13 +165,23 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
       f32x16 s, dp;
 #pragma unroll
       for (int r = 0; r < 16; ++r) { s[r] = kFold ? -lse2 : 0.f; dp[r] = -Dq; }
+      // all operand reads of this key block first (one LDS wait), then the
+      // MFMAs at raised priority
+      x8_t<T> ka[KS], va[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const x8_t<T> ka = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
-        const x8_t<T> va = ld8<T>(&Vs[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
-        mma32(s, ka, qf[ks]);
-        mma32(dp, va, gf[ks]);
+        ka[ks] = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
+        va[ks] = ld8<T>(&Vs[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
       }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        mma32(s, ka[ks], qf[ks]);
+        mma32(dp, va[ks], gf[ks]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x0100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS, 0);
+      __builtin_amdgcn_s_setprio(0);
       if (!kFold) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -lse2);
@@ -324,13 +334,21 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
           }
         }
       }
+      x8_t<T> qa[KS], ga[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const x8_t<T> qa = ld8<T>(&Qs[buf][(32 * qb + l32) * KLD + 16 * ks + 8 * hh]);
-        const x8_t<T> ga = ld8<T>(&Gs[buf][(32 * qb + l32) * KLD + 16 * ks + 8 * hh]);
-        mma32(s, qa, kf[ks]);
-        mma32(dp, ga, vf[ks]);
+        qa[ks] = ld8<T>(&Qs[buf][(32 * qb + l32) * KLD + 16 * ks + 8 * hh]);
+        ga[ks] = ld8<T>(&Gs[buf][(32 * qb + l32) * KLD + 16 * ks + 8 * hh]);
       }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        mma32(s, qa[ks], kf[ks]);
+        mma32(dp, ga[ks], vf[ks]);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x0100, 2 * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS, 0);
+      __builtin_amdgcn_s_setprio(0);
       if (!kFold) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -l2blk[r]);
