@@ -48,7 +48,7 @@ _D = ctypes.POINTER(WhaleDims)
 _SIGS = {
     "whale_status_string": (ctypes.c_char_p, [_I]),
     "whale_version": (ctypes.c_char_p, []),
-    "whale_proj_qkv": (_I, [_D, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "whale_proj_qkv": (_I, [_D, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "whale_jagged_xattn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_fusion_mlp": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P]),
     "whale_swiglu_ffn_workspace_size": (_S, [_D, _I, _I, ctypes.c_int32]),
@@ -62,7 +62,7 @@ _SIGS = {
                                   _P, _P, _P, _S, _P]),
     "whale_proj_qkv_bwd_workspace_size": (_S, [_D, _I]),
     "whale_proj_qkv_bwd": (_I, [_D, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
-                                _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
+                                _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
 }
 
 _lib = None
@@ -129,10 +129,10 @@ def status_string(code):
 
 
 def whale_proj_qkv(d_, H_w, H_s, norm, eps, g_q, b_q, g_kv, b_kv, W_Q, W_K, W_V, Q, K, V, stats_q, stats_kv,
-                   stream=None):
+                   X_q=None, X_s=None, stream=None):
     rc = load().whale_proj_qkv(ctypes.byref(d_), _dtype_code(H_w), _ptr(H_w), _ptr(H_s), norm, eps, _ptr(g_q),
                                _ptr(b_q), _ptr(g_kv), _ptr(b_kv), _ptr(W_Q), _ptr(W_K), _ptr(W_V), _ptr(Q), _ptr(K),
-                               _ptr(V), _ptr(stats_q), _ptr(stats_kv), _stream(stream))
+                               _ptr(V), _ptr(stats_q), _ptr(stats_kv), _ptr(X_q), _ptr(X_s), _stream(stream))
     _check("whale_proj_qkv", rc)
 
 
@@ -203,10 +203,12 @@ def whale_proj_qkv_bwd_workspace_size(d_, dtype_code):
 
 
 def whale_proj_qkv_bwd(d_, H_w, H_s, norm, eps, g_q, b_q, g_kv, b_kv, stats_q, stats_kv, W_Q, W_K, W_V, dQ, dK, dV,
-                       dH_w_in, dH_w, dH_s, dW_Q, dW_K, dW_V, dg_q, db_q, dg_kv, db_kv, workspace, stream=None):
+                       dH_w_in, dH_w, dH_s, dW_Q, dW_K, dW_V, dg_q, db_q, dg_kv, db_kv, workspace, X_q=None, X_s=None,
+                       stream=None):
     ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load().whale_proj_qkv_bwd(ctypes.byref(d_), _dtype_code(H_w), _ptr(H_w), _ptr(H_s), norm, eps, _ptr(g_q),
-                                   _ptr(b_q), _ptr(g_kv), _ptr(b_kv), _ptr(stats_q), _ptr(stats_kv), _ptr(W_Q),
+                                   _ptr(b_q), _ptr(g_kv), _ptr(b_kv), _ptr(stats_q), _ptr(stats_kv), _ptr(X_q),
+                                   _ptr(X_s), _ptr(W_Q),
                                    _ptr(W_K), _ptr(W_V), _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dH_w_in), _ptr(dH_w),
                                    _ptr(dH_s), _ptr(dW_Q), _ptr(dW_K), _ptr(dW_V), _ptr(dg_q), _ptr(db_q),
                                    _ptr(dg_kv), _ptr(db_kv), _ptr(workspace), ws, _stream(stream))

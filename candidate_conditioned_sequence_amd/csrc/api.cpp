@@ -147,7 +147,7 @@ const char* whale_version(void) { return "0.1.0"; }
 whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, const void* H_w, const void* H_s,
                               whale_norm_t norm, float eps, const float* g_q, const float* b_q, const float* g_kv,
                               const float* b_kv, const void* W_Q, const void* W_K, const void* W_V, void* Q, void* K,
-                              void* V, float* stats_q, float* stats_kv, hipStream_t stream) {
+                              void* V, float* stats_q, float* stats_kv, void* X_q, void* X_s, hipStream_t stream) {
   Shape s;
   whale_status_t rc = check_dims(dims, dtype, &s);
   if (rc != WHALE_OK) return rc;
@@ -158,19 +158,26 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
   if (norm != WHALE_NORM_NONE && (!stats_q || (s.T > 0 && !stats_kv))) return WHALE_ERR_NULL;
   const bool bf = dtype == WHALE_BF16;
   const int nk = (int)norm;
-  if (norm != WHALE_NORM_NONE) {
-    WHALE_TRY(launch_norm_stats(H_w, stats_q, s.M, s.d, nk, eps, bf, stream));
-    WHALE_TRY(launch_norm_stats(H_s, stats_kv, s.T, s.d, nk, eps, bf, stream));
+  const bool nrm = norm != WHALE_NORM_NONE;
+  // Each input is normalised either once into X_q / X_s (statistics computed
+  // in the same pass) or, without them, per tile in the GEMM prologue.
+  const bool mq = nrm && X_q != nullptr, ms = nrm && X_s != nullptr && s.T > 0;
+  if (nrm) {
+    if (mq) WHALE_TRY(launch_norm_apply(H_w, nullptr, stats_q, g_q, b_q, X_q, s.M, s.d, nk, eps, bf, stream));
+    else WHALE_TRY(launch_norm_stats(H_w, stats_q, s.M, s.d, nk, eps, bf, stream));
+    if (ms) WHALE_TRY(launch_norm_apply(H_s, nullptr, stats_kv, g_kv, b_kv, X_s, s.T, s.d, nk, eps, bf, stream));
+    else WHALE_TRY(launch_norm_stats(H_s, stats_kv, s.T, s.d, nk, eps, bf, stream));
   }
   GemmArgs a = gemm_defaults();
-  a.X = H_w; a.ldx = s.d; a.stats = stats_q; a.gamma = g_q; a.beta = b_q; a.norm_kind = nk;
+  a.X = mq ? X_q : H_w; a.ldx = s.d; a.stats = stats_q; a.gamma = g_q; a.beta = b_q; a.norm_kind = nk;
   a.W = W_Q; a.ldw = s.d; a.Y = Q; a.ldy = s.d; a.M = s.M; a.N = s.d; a.K = s.d;
-  a.pro = norm == WHALE_NORM_NONE ? PRO_PLAIN : PRO_NORM; a.epi = EPI_STORE;
+  a.pro = (nrm && !mq) ? PRO_NORM : PRO_PLAIN; a.epi = EPI_STORE;
   WHALE_TRY(launch_gemm_nt(a, bf, stream));
   if (s.T > 0) {
-    // K and V in one pass over H_s: weight rows [0, d) from W_K, [d, 2d) from W_V.
+    // K and V in one pass over the history rows: weight rows [0, d) from W_K, [d, 2d) from W_V.
     GemmArgs b = a;
-    b.X = H_s; b.stats = stats_kv; b.gamma = g_kv; b.beta = b_kv;
+    b.X = ms ? X_s : H_s; b.stats = stats_kv; b.gamma = g_kv; b.beta = b_kv;
+    b.pro = (nrm && !ms) ? PRO_NORM : PRO_PLAIN;
     b.W = W_K; b.W2 = W_V; b.nsplit = s.d; b.Y = K; b.Y2 = V; b.M = s.T; b.N = 2 * s.d;
     WHALE_TRY(launch_gemm_nt(b, bf, stream));
   }
@@ -432,7 +439,8 @@ size_t whale_proj_qkv_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t
 
 whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* H_w, const void* H_s,
                                   whale_norm_t norm, float eps, const float* g_q, const float* b_q, const float* g_kv,
-                                  const float* b_kv, const float* stats_q, const float* stats_kv, const void* W_Q,
+                                  const float* b_kv, const float* stats_q, const float* stats_kv, const void* X_q_in,
+                                  const void* X_s_in, const void* W_Q,
                                   const void* W_K, const void* W_V, const void* dQ, const void* dK, const void* dV,
                                   const void* dH_w_in, void* dH_w, void* dH_s, float* dW_Q, float* dW_K, float* dW_V,
                                   float* dg_q, float* db_q, float* dg_kv, float* db_kv, void* workspace,
@@ -467,11 +475,19 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
   const void* Xqin = H_w;
   const void* Xsin = H_s;
   if (norm != WHALE_NORM_NONE) {
-    WHALE_TRY(launch_norm_apply(H_w, stats_q, nullptr, g_q, b_q, Xq, s.M, d, nk, eps, bf, stream));
-    Xqin = Xq;
+    if (X_q_in) {
+      Xqin = X_q_in;
+    } else {
+      WHALE_TRY(launch_norm_apply(H_w, stats_q, nullptr, g_q, b_q, Xq, s.M, d, nk, eps, bf, stream));
+      Xqin = Xq;
+    }
     if (s.T > 0) {
-      WHALE_TRY(launch_norm_apply(H_s, stats_kv, nullptr, g_kv, b_kv, Xs, s.T, d, nk, eps, bf, stream));
-      Xsin = Xs;
+      if (X_s_in) {
+        Xsin = X_s_in;
+      } else {
+        WHALE_TRY(launch_norm_apply(H_s, stats_kv, nullptr, g_kv, b_kv, Xs, s.T, d, nk, eps, bf, stream));
+        Xsin = Xs;
+      }
     }
   }
   Wg wq(dQ, d, Xqin, d, WPRO_PLAIN, s.M, d, d, dW_Q, part);

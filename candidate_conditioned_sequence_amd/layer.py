@@ -44,14 +44,19 @@ class FusionLayer:
         Q, K, V = _empty((M, d), dt, dev), _empty((T, d), dt, dev), _empty((T, d), dt, dev)
         sq = _empty((M, 2), torch.float32, dev) if nn else None
         skv = _empty((T, 2), torch.float32, dev) if nn else None
+        # The normalised inputs are written once (the projections then read them
+        # and the backward reuses them); without them the projections normalise
+        # per tile.
+        Xq = _empty((M, d), dt, dev) if nn else None
+        Xs = _empty((T, d), dt, dev) if nn else None
         wb.whale_proj_qkv(dm, H_w, H_s, self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"], p["W_Q"],
-                          p["W_K"], p["W_V"], Q, K, V, sq, skv, stream)
+                          p["W_K"], p["W_V"], Q, K, V, sq, skv, Xq, Xs, stream)
         A, lse = _empty((M, d), dt, dev), _empty((M, self.h), torch.float32, dev)
         wb.whale_jagged_xattn_fwd(dm, Q, K, V, offsets, self.scale, A, lse, stream)
         F = _empty((M, d), dt, dev)
         Z = _empty((M, d), dt, dev) if (save and self.act == wb.ACT_SILU) else None
         wb.whale_fusion_mlp(dm, A, H_w, p["W_F"], self.act, F, Z, stream)
-        out = dict(Q=Q, K=K, V=V, A=A, lse=lse, F=F, Z=Z, stats_q=sq, stats_kv=skv)
+        out = dict(Q=Q, K=K, V=V, A=A, lse=lse, F=F, Z=Z, stats_q=sq, stats_kv=skv, X_q=Xq, X_s=Xs)
         if self.ffn:
             H = self.H
             Hu = 2 * H if self.gate == wb.GATE_SEPARATE else H
@@ -106,6 +111,6 @@ class FusionLayer:
         wb.whale_proj_qkv_bwd(dm, c["H_w"], c["H_s"], self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"],
                               c["stats_q"], c["stats_kv"], p["W_Q"], p["W_K"], p["W_V"], dQ, dK, dV, dHw_mlp,
                               g["dH_w"], g["dH_s"], g["dW_Q"], g["dW_K"], g["dW_V"], g["dg_q"], g["db_q"], g["dg_kv"],
-                              g["db_kv"], ws, stream)
+                              g["db_kv"], ws, c.get("X_q"), c.get("X_s"), stream)
         g.update(dA=dA, dQ=dQ, dK=dK, dV=dV, dF=dF)
         return g

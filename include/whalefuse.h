@@ -109,6 +109,12 @@ const char* whale_version(void);
  * ignored).  g_q/b_q and g_kv/b_kv are fp32 [d].  stats_q [M,2] and
  * stats_kv [T,2] receive the row statistics; both are required unless norm
  * is none (whale_proj_qkv_bwd consumes them).  T may be 0.
+ *
+ * X_q [M,d] and X_s [T,d] (data dtype, may be NULL; unused for norm none)
+ * receive the normalised inputs Norm_q(H_w) and Norm_kv(H_s).  Given, they
+ * are written once and the projections read them; NULL, the projections
+ * normalise their input tiles on the fly.  Passing them on to
+ * whale_proj_qkv_bwd saves the backward from forming them again.
  */
 whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype,
                               const void* H_w, const void* H_s,
@@ -117,7 +123,8 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype,
                               const float* g_kv, const float* b_kv,
                               const void* W_Q, const void* W_K, const void* W_V,
                               void* Q, void* K, void* V,
-                              float* stats_q, float* stats_kv, hipStream_t stream);
+                              float* stats_q, float* stats_kv,
+                              void* X_q, void* X_s, hipStream_t stream);
 
 /*
  * a3, Eq. (4): jagged softmax cross-attention.  For request b, head j and
@@ -229,6 +236,8 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
  * total), dH_s = Norm_kv backward(dX_s); norm parameter gradients fp32 [d].
  * stats_q / stats_kv come from the forward (may be NULL only for norm none;
  * the norm parameter gradients are then not written and may be NULL).
+ * X_q / X_s: the forward's normalised inputs if it wrote them, else NULL
+ * (they are then formed again in the workspace).
  */
 size_t whale_proj_qkv_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype);
 whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
@@ -237,6 +246,7 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
                                   const float* g_q, const float* b_q,
                                   const float* g_kv, const float* b_kv,
                                   const float* stats_q, const float* stats_kv,
+                                  const void* X_q, const void* X_s,
                                   const void* W_Q, const void* W_K, const void* W_V,
                                   const void* dQ, const void* dK, const void* dV,
                                   const void* dH_w_in,

@@ -69,10 +69,14 @@ def test_xattn_fwd(gpu, case):
     assert_close("lse", got[fin], lse_ref[fin], dtype, factor=0.1)
 
 
-@pytest.mark.parametrize("dtype,norm", [("f32", O.NORM_LAYER), ("bf16", O.NORM_LAYER), ("bf16", O.NORM_RMS),
-                                        ("f32", O.NORM_NONE)])
-def test_proj_qkv(gpu, dtype, norm):
-    print(f"\n[proj_qkv] {dtype} norm={norm}", flush=True)
+@pytest.mark.parametrize("dtype,norm,keep", [("f32", O.NORM_LAYER, False), ("bf16", O.NORM_LAYER, False),
+                                             ("bf16", O.NORM_RMS, False), ("f32", O.NORM_NONE, False),
+                                             ("f32", O.NORM_LAYER, True), ("bf16", O.NORM_LAYER, True),
+                                             ("bf16", O.NORM_RMS, True)])
+def test_proj_qkv(gpu, dtype, norm, keep):
+    """keep: the normalised inputs are written out once (X_q, X_s) and the
+    projections read them; otherwise the projections normalise per tile."""
+    print(f"\n[proj_qkv] {dtype} norm={norm} keep={keep}", flush=True)
     B, C, n_q, d, h, L = 3, 5, 7, 128, 2, [0, 200, 77]
     M, off = B * C * n_q, offsets(L)
     T = int(off[-1])
@@ -84,12 +88,16 @@ def test_proj_qkv(gpu, dtype, norm):
     dm = wb.dims(B, C, n_q, d, h, max(L), T)
     Q, K, V = (torch.empty((n, d), dtype=to_dev(Hw[:1], dtype, gpu).dtype, device=gpu) for n in (M, T, T))
     sq, skv = torch.empty((M, 2), device=gpu), torch.empty((T, 2), device=gpu)
+    Xq, Xs = (torch.empty_like(Q), torch.empty_like(K)) if keep else (None, None)
     wb.whale_proj_qkv(dm, to_dev(Hw, dtype, gpu), to_dev(Hs, dtype, gpu), norm, 1e-5, f32_dev(g[0], gpu),
                       f32_dev(bt[0], gpu), f32_dev(g[1], gpu), f32_dev(bt[1], gpu), to_dev(Wq, dtype, gpu),
-                      to_dev(Wk, dtype, gpu), to_dev(Wv, dtype, gpu), Q, K, V, sq, skv)
+                      to_dev(Wk, dtype, gpu), to_dev(Wv, dtype, gpu), Q, K, V, sq, skv, Xq, Xs)
     torch.cuda.synchronize()
     for name, got, ref in (("Q", Q, Qr), ("K", K, Kr), ("V", V, Vr)):
         assert_close(name, got, ref, dtype)
+    if keep:
+        assert_close("X_q", Xq, O.norm_fwd(Hw, norm, g[0], bt[0], 1e-5)[0], dtype)
+        assert_close("X_s", Xs, O.norm_fwd(Hs, norm, g[1], bt[1], 1e-5)[0], dtype)
 
 
 @pytest.mark.parametrize("dtype,act", [("f32", O.ACT_SILU), ("bf16", O.ACT_SILU), ("bf16", O.ACT_NONE)])
@@ -228,11 +236,13 @@ def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d):
         assert_close("db_f", db, ref["db_f"], dtype)
 
 
-@pytest.mark.parametrize("dtype,norm,d", [("f32", O.NORM_LAYER, 128), ("bf16", O.NORM_LAYER, 128),
-                                          ("bf16", O.NORM_RMS, 256), ("f32", O.NORM_LAYER, 64),
-                                          ("bf16", O.NORM_LAYER, 512), ("f32", O.NORM_NONE, 128)])
-def test_proj_qkv_bwd(gpu, dtype, norm, d):
-    print(f"\n[proj_qkv_bwd] {dtype} norm={norm} d={d}", flush=True)
+@pytest.mark.parametrize("dtype,norm,d,keep", [("f32", O.NORM_LAYER, 128, False), ("bf16", O.NORM_LAYER, 128, False),
+                                               ("bf16", O.NORM_RMS, 256, False), ("f32", O.NORM_LAYER, 64, False),
+                                               ("bf16", O.NORM_LAYER, 512, False), ("f32", O.NORM_NONE, 128, False),
+                                               ("bf16", O.NORM_LAYER, 256, True), ("f32", O.NORM_RMS, 128, True)])
+def test_proj_qkv_bwd(gpu, dtype, norm, d, keep):
+    """keep: the forward's normalised inputs are handed to the backward."""
+    print(f"\n[proj_qkv_bwd] {dtype} norm={norm} d={d} keep={keep}", flush=True)
     B, C, n_q, L = 3, 5, 7, [0, 200, 77]
     h = d // 64
     M, off = B * C * n_q, offsets(L)
@@ -250,14 +260,15 @@ def test_proj_qkv_bwd(gpu, dtype, norm, d):
     tg = [f32_dev(x, gpu) for x in (g[0], bt[0], g[1], bt[1])]
     Q, K, V = torch.empty_like(tHw), torch.empty_like(tHs), torch.empty_like(tHs)
     sq, skv = torch.empty((M, 2), device=gpu), torch.empty((T, 2), device=gpu)
-    wb.whale_proj_qkv(dm, tHw, tHs, norm, 1e-5, *tg, *tW, Q, K, V, sq, skv)
+    Xq, Xs = (torch.empty_like(tHw), torch.empty_like(tHs)) if keep else (None, None)
+    wb.whale_proj_qkv(dm, tHw, tHs, norm, 1e-5, *tg, *tW, Q, K, V, sq, skv, Xq, Xs)
     dHw, dHs = torch.empty_like(tHw), torch.empty_like(tHs)
     dW = [torch.empty((d, d), device=gpu) for _ in range(3)]
     dgb = [torch.empty(d, device=gpu) for _ in range(4)]
     ws = torch.empty(wb.whale_proj_qkv_bwd_workspace_size(dm, wb._dtype_code(tHw)), dtype=torch.uint8, device=gpu)
     wb.whale_proj_qkv_bwd(dm, tHw, tHs, norm, 1e-5, *tg, sq, skv, *tW, to_dev(dQ, dtype, gpu),
                           to_dev(dK, dtype, gpu), to_dev(dV, dtype, gpu), to_dev(extra, dtype, gpu), dHw, dHs, *dW,
-                          *dgb, ws)
+                          *dgb, ws, Xq, Xs)
     torch.cuda.synchronize()
     assert_close("dH_w", dHw, ref["dH_w"] + extra, dtype)
     assert_close("dH_s", dHs, ref["dH_s"], dtype)

@@ -63,7 +63,7 @@ def test_host_validation_rejects_before_launch():
                                 fake, 16, None) == 5
     # LayerNorm without its statistics buffer
     assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 0, 1e-5, fake, fake, fake, fake, fake, fake, fake, fake,
-                              fake, fake, None, fake, None) == 1
+                              fake, fake, None, fake, None, None, None) == 1
 
 
 def test_workspace_sizes_are_host_only_and_monotone():
