@@ -112,9 +112,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
 #pragma unroll
     for (int e = 0; e < NE; ++e) oacc[e][qb] = zero16();
   }
-  float mref[NQ], lsum[NQ];
+  // Row sums in four partial chains per query block; chain v takes the v-th
+  // pair of every 8-value group, in the same order as the ping-pong kernel,
+  // so the two kernels give the same bits.
+  float mref[NQ], lsum[NQ][4];
 #pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = 0.f; lsum[qb] = 0.f; }
+  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = 0.f; for (int v = 0; v < 4; ++v) lsum[qb][v] = 0.f; }
 
   const int ntiles = (L + kBN - 1) / kBN;
   const T* Kh = K + lo * d + j * DH;
@@ -220,7 +223,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
         const float sh = (t == 0 || tmax[qb] > kTau) ? tmax[qb] : 0.f;
         const float alpha = t == 0 ? 0.f : fast_exp2(-sh);
         mref[qb] += sh;
-        lsum[qb] *= alpha;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lsum[qb][v] *= alpha;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -253,8 +257,8 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
               const int r = 8 * mm + 2 * v;
               f32x2 pp = {fast_exp2(s[kb][qb][r]), fast_exp2(s[kb][qb][r + 1])};
               const bf16x2 pk = __builtin_convertvector(pp, bf16x2);
-              lsum[qb] += pp[0];
-              lsum[qb] += pp[1];
+              lsum[qb][v] += pp[0];
+              lsum[qb][v] += pp[1];
               words[v] = __builtin_bit_cast(unsigned, pk);
             }
             pf[kb][qb][mm] = __builtin_bit_cast(bf16x8, words);
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
               const float p = fast_exp2(s[kb][qb][8 * mm + u]);
-              lsum[qb] += p;
+              lsum[qb][u >> 1] += p;
               pf[kb][qb][mm][u] = from_f<T>(p);
             }
           }
@@ -290,7 +294,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
 #pragma unroll
   for (int qb = 0; qb < NQ; ++qb) {
     const int q = qbase + 32 * qb + l32;
-    const float ltot = half_sum(lsum[qb]);
+    const float ltot = half_sum((lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]));
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (q < QR) {
       T* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
@@ -385,9 +389,10 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
     for (int e = 0; e < NE; ++e) oacc[e][qb] = zero16();
-  float mref[NQ], lsum[NQ];
+  // Row sums in four partial chains per query block (summed after the loop).
+  float mref[NQ], lsum[NQ][4];
 #pragma unroll
-  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = 0.f; lsum[qb] = 0.f; }
+  for (int qb = 0; qb < NQ; ++qb) { mref[qb] = 0.f; for (int v = 0; v < 4; ++v) lsum[qb][v] = 0.f; }
   bf16x8 pf[2][NQ][2];
 #pragma unroll
   for (int kb = 0; kb < 2; ++kb)
@@ -403,69 +408,88 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   // of its last row (unmasked loads); their scores are set to -inf.
   const bf16* Gsrc = (grp == 0 ? K : V) + lo * d + j * DH;
   bf16* Gdst = grp == 0 ? &Ks[0][0] : &Vs[0][0];
-  bf16x8 xr[NCH];
-  auto load_tile = [&](int t) {
+  // Two register stages: tile t is staged in xr[t & 1].  It is loaded by this
+  // group's MFMA step t-2, between its score MFMAs (loads issued there cost
+  // the matrix cores less than a burst of loads at the start of a VALU
+  // step), and written to LDS by VALU step t-1.
+  bf16x8 xr[2][NCH];
+  auto load_tile = [&](int t, bf16x8 (&xs)[NCH]) {
     const int last = L - 1 - t * kBN;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = gtid + i * 256;
       const int row = min(ch / CPR, last), e0 = 8 * (ch % CPR);
-      xr[i] = ld8<bf16>(Gsrc + (int64_t)(t * kBN + row) * d + e0);
+      xs[i] = ld8<bf16>(Gsrc + (int64_t)(t * kBN + row) * d + e0);
     }
   };
-  auto store_tile = [&](int buf) {
+  auto store_tile = [&](int buf, const bf16x8 (&xs)[NCH]) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = gtid + i * 256;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
-      st8<bf16>(Gdst + buf * (kBN * KLD) + row * KLD + e0, xr[i]);
+      st8<bf16>(Gdst + buf * (kBN * KLD) + row * KLD + e0, xs[i]);
     }
   };
 
   // MFMA step u: scores of tile u onto -ref, and O += V P of tile u-1.  For
   // u = ntiles the scores read a resident buffer and are never used; for
   // u = 0 the product is skipped.
-  auto mfma_step = [&](int u) {
+  auto mfma_step = [&](int u, bf16x8 (&xl)[NCH]) {
     __builtin_amdgcn_s_setprio(1);
+    // This group's share of tile u+2 goes out between the score MFMAs (the
+    // last two steps reload the last tile, which is never stored).
+    load_tile(min(u + 2, ntiles - 1), xl);
     const uint32_t kaddr = kbase + (uint32_t)(u % kNBUF) * kBufBytes;
+    // Four independent score chains (kb, qb) interleaved: each accumulator
+    // recurs every fourth MFMA.
+    bf16x8 ka[2][KS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      bf16x8 ka[KS];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[ks] = lds_ld8(kaddr + 2 * (32 * kb * KLD + 16 * ks));
+      for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = lds_ld8(kaddr + 2 * (32 * kb * KLD + 16 * ks));
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int qb = 0; qb < NQ; ++qb) {
-          if (ks == 0) {
+      for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][qb][r] = -mref[qb];
-          }
-          mma32(s[kb][qb], ka[ks], qf[qb][ks]);
-        }
-    }
-    if (u >= 1) {
-      const uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kBufBytes;
+        for (int r = 0; r < 16; ++r) s[kb][qb][r] = -mref[qb];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < NE; ++e)
+        for (int qb = 0; qb < NQ; ++qb) mma32(s[kb][qb], ka[kb][ks], qf[qb][ks]);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 4, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x0008, 8, 0);
+    if (u >= 1) {
+      const uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kBufBytes;
+      // Four independent output chains (e, qb) interleaved.
 #pragma unroll
-          for (int mm = 0; mm < 2; ++mm) {
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          bf16x8 a[NE];
+#pragma unroll
+          for (int e = 0; e < NE; ++e) {
             const uint32_t o = vaddr + 2 * ((32 * kb + 16 * mm) * KLD + 32 * e);
-            const bf16x8 a = cat44<bf16>(lds_tr4_at(o), lds_tr4_at(o + 2 * 8 * KLD));
-#pragma unroll
-            for (int qb = 0; qb < NQ; ++qb) mma32(oacc[e][qb], a, pf[kb][qb][mm]);
+            a[e] = cat44<bf16>(lds_tr4_at(o), lds_tr4_at(o + 2 * 8 * KLD));
           }
+#pragma unroll
+          for (int e = 0; e < NE; ++e)
+#pragma unroll
+            for (int qb = 0; qb < NQ; ++qb) mma32(oacc[e][qb], a[e], pf[kb][qb][mm]);
+        }
     }
     __builtin_amdgcn_s_setprio(0);
   };
 
-  // VALU step u: tile traffic, then the softmax of tile u's scores into pf
-  // (row sums into lsum).
-  auto valu_step = [&](int u) {
-    if (u + 1 < ntiles) store_tile((u + 1) % kNBUF);
-    if (u + 2 < ntiles) load_tile(u + 2);
+  // VALU step u: tile u+1 into LDS, then the softmax of tile u's scores into
+  // pf (row sums into lsum).
+  auto valu_step = [&](int u, bf16x8 (&xs)[NCH]) {
+    if (u + 1 < ntiles) store_tile((u + 1) % kNBUF, xs);
     const int nvalid = min(kBN, L - u * kBN);
     if (nvalid < kBN) {
 #pragma unroll
@@ -480,12 +504,15 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     bool need = u == 0;
 #pragma unroll
     for (int qb = 0; qb < NQ; ++qb) {
-      float mx = s[0][qb][0];
+      // four independent max chains, then combined
+      float m4[4];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int v = 0; v < 4; ++v) m4[v] = s[v >> 1][qb][8 * (v & 1)];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][qb][r]);
-      tmax[qb] = half_max(mx);
+      for (int v = 0; v < 4; ++v)
+#pragma unroll
+        for (int r = 1; r < 8; ++r) m4[v] = fmaxf(m4[v], s[v >> 1][qb][8 * (v & 1) + r]);
+      tmax[qb] = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
       need |= tmax[qb] > kTau;
     }
     if (__ballot(need)) {
@@ -494,7 +521,8 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
         const float sh = (u == 0 || tmax[qb] > kTau) ? tmax[qb] : 0.f;
         const float alpha = u == 0 ? 0.f : fast_exp2(-sh);
         mref[qb] += sh;
-        lsum[qb] *= alpha;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) lsum[qb][v] *= alpha;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -516,8 +544,8 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
           for (int v = 0; v < 4; ++v) {
             const int r = 8 * mm + 2 * v;
             const f32x2 pp = {fast_exp2(s[kb][qb][r]), fast_exp2(s[kb][qb][r + 1])};
-            lsum[qb] += pp[0];
-            lsum[qb] += pp[1];
+            lsum[qb][v] += pp[0];
+            lsum[qb][v] += pp[1];
             words[v] = __builtin_bit_cast(unsigned, __builtin_convertvector(pp, bf16x2));
           }
           pf[kb][qb][mm] = __builtin_bit_cast(bf16x8, words);
@@ -526,23 +554,31 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
 
   // Prologue: tile 0 of both tensors into buffer 0 (each group its tensor),
   // tile 1 of this group's tensor into registers.
-  if (ntiles > 0) { load_tile(0); store_tile(0); }
-  if (ntiles > 1) load_tile(1);
+  if (ntiles > 0) { load_tile(0, xr[0]); store_tile(0, xr[0]); }
+  if (ntiles > 1) load_tile(1, xr[1]);
+
   phase_barrier();
 
   if (grp == 1) phase_barrier();
-  for (int u = 0; u <= ntiles; ++u) {
-    mfma_step(u);
+  if (ntiles > 0)
+  for (int u = 0; u <= ntiles; u += 2) {
+    mfma_step(u, xr[0]);
     phase_barrier();
-    if (u < ntiles) valu_step(u);
+    if (u < ntiles) valu_step(u, xr[1]);
     phase_barrier();
+    if (u + 1 <= ntiles) {
+      mfma_step(u + 1, xr[1]);
+      phase_barrier();
+      if (u + 1 < ntiles) valu_step(u + 1, xr[0]);
+      phase_barrier();
+    }
   }
   if (grp == 0) phase_barrier();
 
 #pragma unroll
   for (int qb = 0; qb < NQ; ++qb) {
     const int q = qbase + 32 * qb + l32;
-    const float ltot = half_sum(lsum[qb]);
+    const float ltot = half_sum((lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]));
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
     if (q < QR) {
       bf16* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
