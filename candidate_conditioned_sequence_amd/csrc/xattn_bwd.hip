@@ -157,7 +157,9 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    // The next tile's loads go out between the first score MFMAs; the last
+    // step reloads its own tile and stores it into the idle buffer.
+    const int tnext = min(t + 1, ntiles - 1);
     const int nvalid = min(BN, L - t * BN);
     x8_t<T> dsf[2][2];
 #pragma unroll
@@ -174,13 +176,23 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
         va[ks] = ld8<T>(&Vs[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
       }
       __builtin_amdgcn_s_setprio(1);
+      if (kb == 0) load_tile(tnext);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         mma32(s, ka[ks], qf[ks]);
         mma32(dp, va[ks], gf[ks]);
       }
       __builtin_amdgcn_sched_group_barrier(0x0100, 2 * KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS, 0);
+      if (kb == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * NCH; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS - 2 * NCH, 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS, 0);
+      }
       __builtin_amdgcn_s_setprio(0);
       if (!kFold) {
 #pragma unroll
@@ -201,7 +213,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
           mma32(acc[e], lds_colA<T>(&Ks[buf][0], KLD, 32 * kb + 16 * mm, 32 * e, lane), dsf[kb][mm]);
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    store_tile(buf ^ 1);
     __syncthreads();
   }
 
@@ -275,7 +287,10 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
 
   const int ntiles = q_end > q_begin ? (q_end - q_begin + QT - 1) / QT : 0;
   x8_t<T> qr[NCH], gr[NCH];
-  float lr = 0.f, dr = 0.f;
+  float lraw = 0.f, draw = 0.f;   // raw lse and D of query lane
+  int lq = 0;
+  // Raw loads only: the arithmetic on the loaded values waits until the
+  // values are stored, so no wait on the loads sits at the top of a step.
   auto load_tile = [&](int t) {
     const int qt0 = q_begin + t * QT;
 #pragma unroll
@@ -287,17 +302,11 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
       qr[i] = ld8<T>(Q + off);
       gr[i] = ld8<T>(dA + off);
     }
-    // lane i of the first wave fetches query i's lse and D
-    if (wu == 0) {
-      const int qq = qt0 + lane;
-      const int qc = min(qq, q_end - 1);
-      const float l2 = lse[(qrow0 + qc) * h + j] * kLog2e;
-      const float dd = Dbuf[(qrow0 + qc) * h + j];
-      const bool ok = qq < q_end;
-      if (kFold) lr = ok ? -l2 : -INFINITY;
-      else lr = ok ? l2 : INFINITY;
-      dr = ok ? -dd : 0.f;
-    }
+    // lane i of every wave fetches query i's lse and D
+    lq = qt0 + lane;
+    const int qc = min(lq, q_end - 1);
+    lraw = lse[(qrow0 + qc) * h + j];
+    draw = Dbuf[(qrow0 + qc) * h + j];
   };
   auto store_tile = [&](int buf) {
 #pragma unroll
@@ -307,14 +316,24 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
       st8<T>(&Qs[buf][row * KLD + e0], qr[i]);
       st8<T>(&Gs[buf][row * KLD + e0], gr[i]);
     }
-    if (wu == 0) { nl_s[buf][lane] = lr; nd_s[buf][lane] = dr; }
+    // Every wave writes the same 64 values (no branch for the loads to sink
+    // into).
+    {
+      const float l2 = lraw * kLog2e;
+      const bool ok = lq < q_end;
+      nl_s[buf][lane] = kFold ? (ok ? -l2 : -INFINITY) : (ok ? l2 : INFINITY);
+      nd_s[buf][lane] = ok ? -draw : 0.f;
+    }
   };
 
   if (ntiles > 0) { load_tile(0); store_tile(0); }
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+    // The next tile's loads go out between the first score MFMAs.  The last
+    // step reloads its own tile and stores it into the idle buffer, which is
+    // never read again: the loads, MFMAs and stores stay one straight block.
+    const int tnext = min(t + 1, ntiles - 1);
     x8_t<T> pf[2][2], dsf[2][2];
 #pragma unroll
     for (int qb = 0; qb < 2; ++qb) {
@@ -341,13 +360,23 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
         ga[ks] = ld8<T>(&Gs[buf][(32 * qb + l32) * KLD + 16 * ks + 8 * hh]);
       }
       __builtin_amdgcn_s_setprio(1);
+      if (qb == 0) load_tile(tnext);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         mma32(s, qa[ks], kf[ks]);
         mma32(dp, ga[ks], vf[ks]);
       }
       __builtin_amdgcn_sched_group_barrier(0x0100, 2 * KS, 0);
-      __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS, 0);
+      if (qb == 0) {
+#pragma unroll
+        for (int i = 0; i < 2 * NCH + 2; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS - (2 * NCH + 2), 0);
+      } else {
+        __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS, 0);
+      }
       __builtin_amdgcn_s_setprio(0);
       if (!kFold) {
 #pragma unroll
@@ -364,7 +393,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
           mma32(dv[e], lds_colA<T>(&Gs[buf][0], KLD, 32 * qb + 16 * mm, 32 * e, lane), pf[qb][mm]);
           mma32(dk[e], lds_colA<T>(&Qs[buf][0], KLD, 32 * qb + 16 * mm, 32 * e, lane), dsf[qb][mm]);
         }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+    store_tile(buf ^ 1);
     __syncthreads();
   }
 
