@@ -126,28 +126,30 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
       const int ch = tid + NT * i;
-      const int64_t m = m0 + ch / CPR;
-      const bool ok = m < M && ch < BM * CPR;
+      // Rows past M (and chunks past the tile) read row M-1: their products
+      // land in output rows or columns the epilogues never write, and the
+      // loads stay unmasked.
+      const int64_t m = min(m0 + ch / CPR, M - 1);
       amean[i] = 0.f;
       arstd[i] = 1.f;
-      if (PRO == PRO_NORM && ok && a.norm_kind != 2) { amean[i] = a.stats[2 * m]; arstd[i] = a.stats[2 * m + 1]; }
-      aptr[i] = ok ? X + m * a.ldx + 8 * (ch % CPR) : nullptr;
-      aptr2[i] = (ok && X2) ? X2 + m * a.ldx2 + 8 * (ch % CPR) : nullptr;
+      if (PRO == PRO_NORM && a.norm_kind != 2) { amean[i] = a.stats[2 * m]; arstd[i] = a.stats[2 * m + 1]; }
+      aptr[i] = X + m * a.ldx + 8 * (ch % CPR);
+      aptr2[i] = X2 ? X2 + m * a.ldx2 + 8 * (ch % CPR) : aptr[i];
     }
 #pragma unroll
     for (int i = 0; i < BCH; ++i) {
       const int ch = tid + NT * i;
       const int tr = ch / CPR;
-      const T* p = nullptr;
+      const T* p;
       if (EPI == EPI_GATE_SEP) {
         // tile rows [64 v, 64 v + 32) gate rows, [64 v + 32, 64 v + 64) up rows, same output columns
-        const int n = n0 / 2 + (tr >> 6) * 32 + (tr & 31);
-        if (n < Hs) p = W + (int64_t)(((tr >> 5) & 1) ? Hs + n : n) * a.ldw;
+        const int n = min(n0 / 2 + (tr >> 6) * 32 + (tr & 31), Hs - 1);
+        p = W + (int64_t)(((tr >> 5) & 1) ? Hs + n : n) * a.ldw;
       } else {
-        const int n = n0 + tr;
-        if (n < N) p = (W2 != nullptr && n >= a.nsplit) ? W2 + (int64_t)(n - a.nsplit) * a.ldw : W + (int64_t)n * a.ldw;
+        const int n = min(n0 + tr, N - 1);
+        p = (W2 != nullptr && n >= a.nsplit) ? W2 + (int64_t)(n - a.nsplit) * a.ldw : W + (int64_t)n * a.ldw;
       }
-      bptr[i] = p ? p + 8 * (ch % CPR) : nullptr;
+      bptr[i] = p + 8 * (ch % CPR);
     }
   };
   // Raw loads of one K step into a slot; the prologue math (norm, dZ) is
@@ -155,12 +157,11 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
   auto load = [&](int slot, int k0) {
 #pragma unroll
     for (int i = 0; i < ACH; ++i) {
-      if (aptr[i] == nullptr) { ar[slot][i] = zero8<T>(); continue; }
-      if (PRO == PRO_CONCAT && k0 >= a.ksplit) ar[slot][i] = ld8<T>(aptr2[i] + (k0 - a.ksplit));
-      else ar[slot][i] = ld8<T>(aptr[i] + k0);
+      const bool second = PRO == PRO_CONCAT && k0 >= a.ksplit;
+      ar[slot][i] = ld8<T>(second ? aptr2[i] + (k0 - a.ksplit) : aptr[i] + k0);
     }
 #pragma unroll
-    for (int i = 0; i < BCH; ++i) br[slot][i] = bptr[i] ? ld8<T>(bptr[i] + k0) : zero8<T>();
+    for (int i = 0; i < BCH; ++i) br[slot][i] = ld8<T>(bptr[i] + k0);
   };
   auto store = [&](int slot, int buf, int k0) {
 #pragma unroll
@@ -168,13 +169,11 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
       const int ch = tid + NT * i;
       if (ch >= BM * CPR) continue;
       x8_t<T> v = ar[slot][i];
-      if (aptr[i] != nullptr) {
-        if (PRO == PRO_DACT) {
-          v = dact8<T>(v, ld8<T>(aptr2[i] + k0));
-        } else if (PRO == PRO_NORM && a.norm_kind != 2) {
-          const int k = k0 + 8 * (ch % CPR);
-          v = norm8<T>(v, amean[i], arstd[i], &sgb[k], &sgb[512 + k], 0);
-        }
+      if (PRO == PRO_DACT) {
+        v = dact8<T>(v, ld8<T>(aptr2[i] + k0));
+      } else if (PRO == PRO_NORM && a.norm_kind != 2) {
+        const int k = k0 + 8 * (ch % CPR);
+        v = norm8<T>(v, amean[i], arstd[i], &sgb[k], &sgb[512 + k], 0);
       }
       st8<T>(&As[buf * BM * LDT + (ch / CPR) * LDT + 8 * (ch % CPR)], v);
     }
@@ -213,10 +212,12 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
         const int kt = kt0 + u;
         if (kt < nk) {
           const int buf = kt & 1;
-          // slot u (K step kt) is in LDS now: refill it with K step kt + PIPE
-          if (kt + PIPE < nk) load(u, (kt + PIPE) * BK);
           const T* At = As + buf * BM * LDT;
           const T* Bt = Bs + buf * BN * LDT;
+          __builtin_amdgcn_s_setprio(1);
+          // slot u (K step kt) is in LDS now: refill it with K step kt + PIPE
+          // (the last steps reload the last K step)
+          load(u, min(kt + PIPE, nk - 1) * BK);
 #pragma unroll
           for (int ks = 0; ks < BK / 16; ++ks) {
             x8_t<T> af[2], bf[2];
@@ -229,7 +230,20 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
 #pragma unroll
               for (int jj = 0; jj < 2; ++jj) mma32(acc[i][jj], af[i], bf[jj]);
           }
-          if (kt + 1 < nk) store((u + 1) % PIPE, buf ^ 1, (kt + 1) * BK);
+          if constexpr (sizeof(T) == 2) {
+            constexpr int NV = ACH + BCH;
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+              __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+                if (4 * ks + m < NV) __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+              }
+            }
+          }
+          __builtin_amdgcn_s_setprio(0);
+          store((u + 1) % PIPE, buf ^ 1, min(kt + 1, nk - 1) * BK);
           __syncthreads();
         }
       }
