@@ -434,7 +434,7 @@ hipError_t gemm_go(const GemmArgs& a, hipStream_t st) {
 template <typename T, int PRO>
 hipError_t gemm_epi(const GemmArgs& a, hipStream_t st) {
   switch (a.epi) {
-    case EPI_STORE: return gemm_go<T, PRO, EPI_STORE, 128, 128, 64>(a, st);
+    case EPI_STORE: return gemm_go<T, PRO, EPI_STORE, 128, sizeof(T) == 2 ? 256 : 128, 64>(a, st);
     case EPI_RESID: return gemm_go<T, PRO, EPI_RESID, 128, 128, 64>(a, st);
     case EPI_SILU_RESID: return gemm_go<T, PRO, EPI_SILU_RESID, 128, 128, 64>(a, st);
     case EPI_GATE_TIED: return gemm_go<T, PRO, EPI_GATE_TIED, 128, 128, 64>(a, st);
