@@ -1,16 +1,15 @@
-// Row normalisation statistics and the column reduction of the norm
-// parameter gradients.
+// Row normalisation (statistics, and the normalised rows for the GEMMs that
+// consume them), the SiLU derivative product of the fusion MLP backward, and
+// the column reduction of the norm parameter gradients.
 //
 // The pages normalise the Wukong output before the query projection, the
 // HSTU output before the key/value projections, and the fused stream before
 // the FFN (pith.science verdict record, pith_extraction.key_machinery;
 // gist.science Technical Summary §2.1, pre-norm SwiGLU FFN).  LayerNorm uses
 // the biased variance with eps inside the root; RMSNorm the mean square.  The
-// affine gamma/beta is applied in the GEMM prologue that consumes each row and
-// the norm backward runs in the epilogue of the GEMM that produces dX, so
-// these kernels only produce (mean, rstd) per row and reduce the per-tile
-// dgamma/dbeta partials.  Both are HBM-bound: 16-byte loads, every byte read
-// once.
+// norm backward runs in the epilogue of the GEMM that produces dX; the
+// kernels here reduce its per-tile dgamma/dbeta partials.  All are HBM-bound:
+// 16-byte loads, every byte read once.
 #include "common.h"
 #include "kernels.h"
 
@@ -21,35 +20,47 @@ namespace {
 // of 4 waves covers 4 * (64 / (n/8)) * kRows rows.
 constexpr int kRows = 4;
 
-// Row statistics of one row held as 8 values per lane of a group of lpr lanes.
-WHALE_DEV void row_stats(const float* v, int lpr, int n, int kind, float eps, float& mean, float& rstd) {
-  float s = 0.f;
+// Row statistics of kRows rows, each held as 8 values per lane of a group of
+// lpr lanes; the cross-lane sums of all rows advance together, so their
+// shuffles are in flight at the same time.
+WHALE_DEV void row_stats(const float (&v)[kRows][8], int lpr, int n, int kind, float eps, float (&mean)[kRows],
+                         float (&rstd)[kRows]) {
+  float s[kRows], q[kRows];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) s += v[u];
-  for (int o = 1; o < lpr; o <<= 1) s += __shfl_xor(s, o);
-  mean = kind == 0 ? s / n : 0.f;
-  float q = 0.f;
+  for (int k = 0; k < kRows; ++k) {
+    s[k] = 0.f;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) { const float dl = v[u] - mean; q += dl * dl; }
-  for (int o = 1; o < lpr; o <<= 1) q += __shfl_xor(q, o);
-  rstd = 1.f / sqrtf(q / n + eps);
+    for (int u = 0; u < 8; ++u) s[k] += v[k][u];
+  }
+  for (int o = 1; o < lpr; o <<= 1)
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) s[k] += __shfl_xor(s[k], o);
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) {
+    mean[k] = kind == 0 ? s[k] / n : 0.f;
+    q[k] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) { const float dl = v[k][u] - mean[k]; q[k] += dl * dl; }
+  }
+  for (int o = 1; o < lpr; o <<= 1)
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) q[k] += __shfl_xor(q[k], o);
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) rstd[k] = 1.f / sqrtf(q[k] / n + eps);
 }
 
+// Rows past the end read the last row (unmasked loads, all in flight at
+// once); their results are never stored.
 template <typename T>
 WHALE_DEV void load_rows(const T* __restrict__ x, int64_t row0, int64_t rstep, int64_t rows, int n, int cl,
                          float (&v)[kRows][8]) {
+  x8_t<T> r[kRows];
 #pragma unroll
-  for (int k = 0; k < kRows; ++k) {
-    const int64_t row = row0 + k * rstep;
-    if (row < rows) {
-      const x8_t<T> r = ld8<T>(x + row * n + 8 * cl);
+  for (int k = 0; k < kRows; ++k) r[k] = ld8<T>(x + min(row0 + k * rstep, rows - 1) * n + 8 * cl);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[k][u] = to_f(r[u]);
-    } else {
+  for (int k = 0; k < kRows; ++k)
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[k][u] = 0.f;
-    }
-  }
+    for (int u = 0; u < 8; ++u) v[k][u] = to_f(r[k][u]);
 }
 
 template <typename T>
@@ -61,16 +72,15 @@ __global__ __launch_bounds__(256) void norm_stats_kernel(const T* __restrict__ x
   const int64_t rstep = 4 * rpw;           // rows per block and pass
   const int64_t row0 = (int64_t)blockIdx.x * rstep * kRows + w * rpw + lane / lpr;
   const int cl = lane % lpr;
-  float v[kRows][8];
+  float v[kRows][8], mean[kRows], rstd[kRows];
   load_rows<T>(x, row0, rstep, rows, n, cl, v);
+  row_stats(v, lpr, n, kind, eps, mean, rstd);
 #pragma unroll
   for (int k = 0; k < kRows; ++k) {
     const int64_t row = row0 + k * rstep;
-    float mean, rstd;
-    row_stats(v[k], lpr, n, kind, eps, mean, rstd);
     if (row < rows && cl == 0) {
-      stats[2 * row] = mean;
-      stats[2 * row + 1] = rstd;
+      stats[2 * row] = mean[k];
+      stats[2 * row + 1] = rstd[k];
     }
   }
 }
@@ -97,24 +107,29 @@ __global__ __launch_bounds__(256) void norm_apply_kernel(const T* __restrict__ x
     bt[u] = 0.f;
     if (kind == 0) bt[u] = beta[8 * cl + u];          // beta may be null for RMSNorm
   }
-  float v[kRows][8];
+  float v[kRows][8], mean[kRows], rstd[kRows];
   load_rows<T>(x, row0, rstep, rows, n, cl, v);
+  if (stats_in != nullptr) {
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const int64_t row = min(row0 + k * rstep, rows - 1);
+      mean[k] = stats_in[2 * row];
+      rstd[k] = stats_in[2 * row + 1];
+    }
+  } else {
+    row_stats(v, lpr, n, kind, eps, mean, rstd);
+  }
 #pragma unroll
   for (int k = 0; k < kRows; ++k) {
     const int64_t row = row0 + k * rstep;
-    const bool ok = row < rows;
-    float mean, rstd;
-    if (stats_in != nullptr) {
-      mean = ok ? stats_in[2 * row] : 0.f;
-      rstd = ok ? stats_in[2 * row + 1] : 0.f;
-    } else {
-      row_stats(v[k], lpr, n, kind, eps, mean, rstd);
-      if (ok && cl == 0 && stats_out != nullptr) { stats_out[2 * row] = mean; stats_out[2 * row + 1] = rstd; }
+    if (row >= rows) continue;
+    if (stats_in == nullptr && cl == 0 && stats_out != nullptr) {
+      stats_out[2 * row] = mean[k];
+      stats_out[2 * row + 1] = rstd[k];
     }
-    if (!ok) continue;
     x8_t<T> o;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) o[u] = from_f<T>((v[k][u] - mean) * rstd * gm[u] + bt[u]);
+    for (int u = 0; u < 8; ++u) o[u] = from_f<T>((v[k][u] - mean[k]) * rstd[k] * gm[u] + bt[u]);
     st8<T>(y + row * n + 8 * cl, o);
   }
 }
