@@ -183,11 +183,11 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
       st8<T>(&Bs[buf * BN * LDT + (ch / CPR) * LDT + 8 * (ch % CPR)], br[slot][i]);
     }
   };
+  // (With a single K step the second slot refetches it; it is never read.)
   auto prefetch_tile = [&](int t) {
     setup(t);
 #pragma unroll
-    for (int u = 0; u < PIPE; ++u)
-      if (u * BK < a.K) load(u, u * BK);
+    for (int u = 0; u < PIPE; ++u) load(u, min(u * BK, a.K - BK));
   };
 
   const int nk = K / BK;
@@ -248,9 +248,43 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
         }
       }
     }
-    // The next tile's first K steps go in flight during this epilogue.
-    if (tile + gx < t_hi) prefetch_tile(tile + gx);
+    // Epilogue inputs (residual R, saved pre-activation Z) of every pass are
+    // loaded now, from clamped rows and columns (unused where out of range),
+    // ahead of the next tile's operand loads: waiting for them later does not
+    // wait for those.
+    constexpr int OUTC = (EPI == EPI_GATE_SEP) ? BN / 2 : BN;   // output columns per tile
+    constexpr int CH = SROWS * OUTC / 8;                         // 8-column chunks per pass
+    constexpr int CPT = (CH + NT - 1) / NT;
+    constexpr int NP = BM / SROWS;
+    // (The separate-gate backward needs two inputs per chunk; preloading both
+    // would not fit in registers, so it loads them where they are used.)
+    constexpr int NL = (EPI == EPI_RESID || EPI == EPI_SILU_RESID || EPI == EPI_DUAL_RESID2 || EPI == EPI_DGATE_TIED) ? 1 : 0;
+    x8_t<T> pre[NP][CPT][1];
+    if constexpr (NL > 0 && EPI != EPI_NORM_BWD) {
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          const int c = min(tid + i * NT, CH - 1);
+          const int row = c / (OUTC / 8), col = 8 * (c % (OUTC / 8));
+          const int64_t m = min(m0 + p * SROWS + row, M - 1);
+          const int n = min(n0 + col, N - 1);
+          if (EPI == EPI_DUAL_RESID2) {
+            pre[p][i][0] = ld8<T>(R + m * a.ldr + max(n - a.nsplit, 0));
+          } else if (EPI == EPI_DGATE_TIED) {
+            pre[p][i][0] = ld8<T>(Z + m * a.ldz + n);
+          } else {
+            pre[p][i][0] = ld8<T>(R + m * a.ldr + n);
+          }
+        }
+    }
 
+    // The next tile's first K steps go in flight during this epilogue (the
+    // last tile refetches its own, unused: an unconditional prefetch lets the
+    // waits above count exactly).
+    prefetch_tile(tile + gx < t_hi ? tile + gx : tile);
+
+#pragma unroll
     for (int pass = 0; pass < BM / SROWS; ++pass) {
       // Stage rows [pass*SROWS, (pass+1)*SROWS) of the tile (fp32).
       if (SROWS == BM || wm == pass) {
@@ -328,9 +362,10 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
         }
       } else {
         // Generic epilogue: 8-column chunks, coalesced 16-byte accesses.
-        constexpr int OUTC = (EPI == EPI_GATE_SEP) ? BN / 2 : BN;   // output columns per tile
-        constexpr int CH = SROWS * OUTC / 8;
-        for (int c = tid; c < CH; c += NT) {
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) {
+          const int c = tid + i * NT;
+          if (c >= CH) continue;
           const int row = c / (OUTC / 8), col = 8 * (c % (OUTC / 8));
           const int64_t m = r0 + row;
           if (m >= M) continue;
@@ -353,28 +388,27 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
           if (n >= N) continue;
 #pragma unroll
           for (int u = 0; u < 8; ++u) v[u] = stg[row * SLD + col + u];
+          float p8[8];
+          if constexpr (NL > 0) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) p8[u] = to_f(pre[pass][i][0][u]);
+          }
           if (EPI == EPI_STORE) {
             if (a.Y2 != nullptr && n >= a.nsplit) st8f<YT>((YT*)a.Y2 + m * a.ldy + (n - a.nsplit), v);
             else st8f<YT>(Y + m * a.ldy + n, v);
           } else if (EPI == EPI_RESID) {
-            float r8[8];
-            ld8f<T>(R + m * a.ldr + n, r8);
-            for (int u = 0; u < 8; ++u) r8[u] += v[u];
-            st8f<YT>(Y + m * a.ldy + n, r8);
+            for (int u = 0; u < 8; ++u) p8[u] += v[u];
+            st8f<YT>(Y + m * a.ldy + n, p8);
           } else if (EPI == EPI_DUAL_RESID2) {
             if (n < a.nsplit) {
               st8f<YT>(Y + m * a.ldy + n, v);
             } else {
-              float r8[8];
-              ld8f<T>(R + m * a.ldr + (n - a.nsplit), r8);
-              for (int u = 0; u < 8; ++u) r8[u] += v[u];
-              st8f<YT>((YT*)a.Y2 + m * a.ldy + (n - a.nsplit), r8);
+              for (int u = 0; u < 8; ++u) p8[u] += v[u];
+              st8f<YT>((YT*)a.Y2 + m * a.ldy + (n - a.nsplit), p8);
             }
           } else if (EPI == EPI_SILU_RESID) {
-            float r8[8];
-            ld8f<T>(R + m * a.ldr + n, r8);
-            for (int u = 0; u < 8; ++u) r8[u] += siluf_(v[u]);
-            st8f<YT>(Y + m * a.ldy + n, r8);
+            for (int u = 0; u < 8; ++u) p8[u] += siluf_(v[u]);
+            st8f<YT>(Y + m * a.ldy + n, p8);
             if (Z) st8f<T>(Z + m * a.ldz + n, v);
           } else if (EPI == EPI_GATE_TIED) {
             float g8[8];
@@ -382,9 +416,7 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
             st8f<YT>(Y + m * a.ldy + n, g8);
             if (Z) st8f<T>(Z + m * a.ldz + n, v);
           } else if (EPI == EPI_DGATE_TIED) {
-            float u8[8];
-            ld8f<T>(Z + m * a.ldz + n, u8);
-            for (int u = 0; u < 8; ++u) v[u] *= dsiluf_(u8[u]) * u8[u] + siluf_(u8[u]);
+            for (int u = 0; u < 8; ++u) v[u] *= dsiluf_(p8[u]) * p8[u] + siluf_(p8[u]);
             st8f<YT>(Y + m * a.ldy + n, v);
           } else if (EPI == EPI_DGATE_SEP) {
             float ug[8], uu[8], o1[8], o2[8];
