@@ -156,7 +156,10 @@ WHALE_DEV int xcd_remap(int id, int n) {
 }
 
 WHALE_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-WHALE_DEV float sigmoidf_(float z) { return 1.f / (1.f + __expf(-z)); }
+// Logistic sigmoid with the hardware reciprocal (about 1 ulp): the IEEE
+// division sequence would cost ten instructions per element in the gate and
+// activation prologues / epilogues.  1 + e^-z = inf gives 0, as it should.
+WHALE_DEV float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 WHALE_DEV float siluf_(float z) { return z * sigmoidf_(z); }
 WHALE_DEV float dsiluf_(float z) { float s = sigmoidf_(z); return s * (1.f + z * (1.f - s)); }
 

@@ -526,64 +526,74 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
   // the tile; this thread takes rows 4*half .. +4 of it.
   const int bk = tid >> 1, half = tid & 1;
   const int rb = 8 * (bk & 7) + 4 * half, cb = 8 * (bk >> 3);
-  const int gcol = n0 + cb, xcol = k0 + cb;
-  const T* gsrc = nullptr;    // column base of this thread's 8 G columns
-  const T* gsrcz = nullptr;   // activation input for the G prologue
-  const T* xsrc = nullptr;    // column base of this thread's 8 X columns
-  const T* xsrcz = nullptr;   // second operand of the X prologue
+  // Columns past N / K read the last 8-column group (their sums are never
+  // written); rows past the chunk read its last row and are zeroed when
+  // stored, so every load is unmasked and all of them are in flight at once.
+  const int gcol = min(n0 + cb, N - 8), xcol = min(k0 + cb, K - 8);
+  const T* gsrc = (G2 != nullptr && gcol >= a.nsplit) ? G2 + (gcol - a.nsplit) : G + gcol;
+  const T* gsrcz = GPRO == 1 ? Gz + gcol : gsrc;   // activation input for the G prologue
+  const T* xsrc;                                   // column base of this thread's 8 X columns
+  const T* xsrcz = nullptr;                        // second operand of the X prologue
   int xld = a.ldx;
-  if (gcol < N) {
-    gsrc = (G2 != nullptr && gcol >= a.nsplit) ? G2 + (gcol - a.nsplit) : G + gcol;
-    if (GPRO == 1) gsrcz = Gz + gcol;
-  }
-  if (xcol < K) {
-    if (PRO == WPRO_CONCAT && xcol >= a.ksplit) { xsrc = X2 + (xcol - a.ksplit); xld = a.ldx2; }
-    else {
-      xsrc = X + xcol;
-      if (PRO == WPRO_GATE_SEP) xsrcz = X + a.gate_H + xcol;
-    }
+  if (PRO == WPRO_CONCAT && xcol >= a.ksplit) { xsrc = X2 + (xcol - a.ksplit); xld = a.ldx2; }
+  else {
+    xsrc = X + xcol;
+    if (PRO == WPRO_GATE_SEP) xsrcz = X + a.gate_H + xcol;
   }
   float gm[8], bt[8];
-  if (PRO == WPRO_NORM && xsrc != nullptr) {
+  if (PRO == WPRO_NORM) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) { gm[u] = a.gamma[xcol + u]; bt[u] = a.norm_kind == 0 ? a.beta[xcol + u] : 0.f; }
   }
 
-  x8_t<T> gr[4], xr[4];
+  // Raw loads of one m-step; the prologues run when the step is stored.
+  x8_t<T> gr[4], gz[4], xr[4], xz[4];
+  float mn[4], rs[4];
+  int64_t mrow0 = 0;
   auto load = [&](int64_t mbase) {
+    mrow0 = mbase;
+    int64_t mr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mr[i] = mbase + rb + i;
+    if (mbase + WM > me) {   // only a chunk's last step can run past it
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mr[i] = min(mr[i], me - 1);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t m = mbase + rb + i;
-      const bool mok = m < me;
-      if (gsrc != nullptr && mok) {
-        const x8_t<T> v = ld8<T>(gsrc + m * a.ldg);
-        gr[i] = GPRO == 1 ? dact8<T>(v, ld8<T>(gsrcz + m * a.ldg)) : v;
-      } else {
-        gr[i] = zero8<T>();
-      }
-      if (xsrc != nullptr && mok) {
-        const x8_t<T> v = ld8<T>(xsrc + m * xld);
-        if (PRO == WPRO_GATE_TIED) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) { const float uf = to_f(v[e]); xr[i][e] = from_f<T>(siluf_(uf) * uf); }
-        } else if (PRO == WPRO_GATE_SEP) {
-          const x8_t<T> uu = ld8<T>(xsrcz + m * xld);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xr[i][e] = from_f<T>(siluf_(to_f(v[e])) * to_f(uu[e]));
-        } else if (PRO == WPRO_NORM && a.norm_kind != 2) {
-          const float mean = a.stats[2 * m], rstd = a.stats[2 * m + 1];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) xr[i][e] = from_f<T>((to_f(v[e]) - mean) * rstd * gm[e] + bt[e]);
-        } else {
-          xr[i] = v;
-        }
-      } else {
-        xr[i] = zero8<T>();
-      }
+      const int64_t m = mr[i];
+      gr[i] = ld8<T>(gsrc + m * a.ldg);
+      if (GPRO == 1) gz[i] = ld8<T>(gsrcz + m * a.ldg);
+      xr[i] = ld8<T>(xsrc + m * xld);
+      if (PRO == WPRO_GATE_SEP) xz[i] = ld8<T>(xsrcz + m * xld);
+      if (PRO == WPRO_NORM && a.norm_kind != 2) { mn[i] = a.stats[2 * m]; rs[i] = a.stats[2 * m + 1]; }
     }
   };
-  // Transposed into [column][m]: 4 consecutive m of one column per write.
+  // Prologues, zeros for rows past the chunk, then transposed into
+  // [column][m]: 4 consecutive m of one column per write.
   auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x8_t<T> g = GPRO == 1 ? dact8<T>(gr[i], gz[i]) : gr[i];
+      x8_t<T> x = xr[i];
+      if (PRO == WPRO_GATE_TIED) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { const float uf = to_f(x[e]); x[e] = from_f<T>(siluf_(uf) * uf); }
+      } else if (PRO == WPRO_GATE_SEP) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = from_f<T>(siluf_(to_f(x[e])) * to_f(xz[i][e]));
+      } else if (PRO == WPRO_NORM && a.norm_kind != 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = from_f<T>((to_f(x[e]) - mn[i]) * rs[i] * gm[e] + bt[e]);
+      }
+      gr[i] = g;
+      xr[i] = x;
+    }
+    if (mrow0 + WM > me) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (mrow0 + rb + i >= me) { gr[i] = zero8<T>(); xr[i] = zero8<T>(); }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x4_t<T> tg, tx;
@@ -730,6 +740,7 @@ int wgrad_splits(int64_t M, int N, int K) {
 }
 
 hipError_t launch_wgrad(const WgradArgs& a, bool bf16_data, hipStream_t st) {
+  if (a.N < 8 || a.K < 8 || a.N % 8 != 0 || a.K % 8 != 0) return hipErrorInvalidValue;   // whole 8-column groups
   return bf16_data ? wgrad_t<bf16>(a, st) : wgrad_t<float>(a, st);
 }
 
