@@ -300,49 +300,69 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
       const int64_t r0 = m0 + pass * SROWS;
 
       if (EPI == EPI_NORM_BWD) {
-        // The tile spans whole rows (BN >= N).  A group of N/8 lanes owns a row.
-        constexpr int LPRmax = BN / 8;
-        const int LPR = N / 8;                      // lanes per row (power of two, <= 64)
-        const int rpp = 64 / LPR;                   // rows per wave pass
+        // The tile spans whole rows (N == BN).  A group of BN/8 lanes owns a
+        // row; each thread handles NIT rows of the pass, NB at a time.  The
+        // inputs of a batch (x, R, the row statistics) are loaded first, the
+        // row sums of its NB rows advance together, then a second sweep
+        // writes the outputs.
+        constexpr int LPR = BN / 8;                 // lanes per row (power of two, <= 64)
+        constexpr int RPP = 64 / LPR;               // rows per wave pass
+        constexpr int NIT = SROWS / ((NT / 64) * RPP);
+        constexpr int NB = NIT < (BN >= 256 ? 4 : 2) ? NIT : (BN >= 256 ? 4 : 2);   // registers
+        const int rpp = RPP;
         const int sub = lane / LPR, cl = lane % LPR;
         const int c0 = 8 * cl;
         float pg[8], pb[8], gmm[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) { pg[u] = 0.f; pb[u] = 0.f; gmm[u] = a.norm_kind == 2 ? 1.f : a.gamma[c0 + u]; }
         const float invn = 1.f / N;
-        for (int rb = w * rpp; rb < SROWS; rb += (NT / 64) * rpp) {
-          const int row = rb + sub;
-          const int64_t m = r0 + row;
-          const bool ok = m < M;
-          float dxn[8], xh[8];
-          float mean = 0.f, rstd = 1.f;
-          if (ok && a.norm_kind != 2) { mean = a.stats[2 * m]; rstd = a.stats[2 * m + 1]; }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) dxn[u] = stg[row * SLD + c0 + u];
-          if (ok) ld8f<T>((const T*)a.nx + m * N + c0, xh);
-          else for (int u = 0; u < 8; ++u) xh[u] = 0.f;
-          float s1 = 0.f, s2 = 0.f;
+        for (int i0 = 0; i0 < NIT; i0 += NB) {
+          x8_t<T> xin[NB], rin[NB];
+          float mean[NB], rstd[NB], s1[NB], s2[NB];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            xh[u] = (xh[u] - mean) * rstd;
-            const float gd = ok ? dxn[u] * gmm[u] : 0.f;
-            s1 += gd;
-            s2 += gd * xh[u];
-            if (ok) { pg[u] += dxn[u] * xh[u]; pb[u] += dxn[u]; }
+          for (int j = 0; j < NB; ++j) {
+            const int row = (w + (i0 + j) * (NT / 64)) * RPP + sub;
+            const int64_t m = min(r0 + row, M - 1);
+            xin[j] = ld8<T>((const T*)a.nx + m * N + c0);
+            rin[j] = R ? ld8<T>(R + m * a.ldr + c0) : zero8<T>();
+            mean[j] = 0.f;
+            rstd[j] = 1.f;
+            if (a.norm_kind != 2) { mean[j] = a.stats[2 * m]; rstd[j] = a.stats[2 * m + 1]; }
           }
 #pragma unroll
-          for (int o = 1; o < LPRmax; o <<= 1)
-            if (o < LPR) { s1 += __shfl_xor(s1, o); s2 += __shfl_xor(s2, o); }
-          s1 *= invn;
-          s2 *= invn;
-          if (a.norm_kind != 0) s1 = 0.f;
-          if (ok) {
-            float o8[8];
-            if (R) ld8f<T>(R + m * a.ldr + c0, o8);
-            else for (int u = 0; u < 8; ++u) o8[u] = 0.f;
+          for (int j = 0; j < NB; ++j) {
+            const int row = (w + (i0 + j) * (NT / 64)) * RPP + sub;
+            const bool ok = r0 + row < M;
+            s1[j] = 0.f;
+            s2[j] = 0.f;
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-              o8[u] += a.norm_kind == 2 ? dxn[u] : rstd * (dxn[u] * gmm[u] - s1 - xh[u] * s2);
+            for (int u = 0; u < 8; ++u) {
+              const float xh = (to_f(xin[j][u]) - mean[j]) * rstd[j];
+              const float gd = ok ? stg[row * SLD + c0 + u] * gmm[u] : 0.f;
+              s1[j] += gd;
+              s2[j] += gd * xh;
+            }
+          }
+#pragma unroll
+          for (int o = 1; o < LPR; o <<= 1)
+#pragma unroll
+            for (int j = 0; j < NB; ++j) { s1[j] += __shfl_xor(s1[j], o); s2[j] += __shfl_xor(s2[j], o); }
+#pragma unroll
+          for (int j = 0; j < NB; ++j) {
+            const int row = (w + (i0 + j) * (NT / 64)) * RPP + sub;
+            const int64_t m = r0 + row;
+            if (m >= M) continue;
+            const float c1 = a.norm_kind != 0 ? 0.f : s1[j] * invn, c2 = s2[j] * invn;
+            float o8[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+              const float dxn = stg[row * SLD + c0 + u];
+              const float xh = (to_f(xin[j][u]) - mean[j]) * rstd[j];
+              pg[u] += dxn * xh;
+              pb[u] += dxn;
+              o8[u] = to_f(rin[j][u]) + (a.norm_kind == 2 ? dxn : rstd[j] * (dxn * gmm[u] - c1 - xh * c2));
+            }
             st8f<YT>(Y + m * a.ldy + c0, o8);
           }
         }
@@ -475,8 +495,9 @@ hipError_t gemm_epi(const GemmArgs& a, hipStream_t st) {
     case EPI_DGATE_SEP: return gemm_go<T, PRO, EPI_DGATE_SEP, 128, 128, 32>(a, st);
     case EPI_DUAL_RESID2: return gemm_go<T, PRO, EPI_DUAL_RESID2, 128, 128, 32>(a, st);
     case EPI_NORM_BWD:
-      // Row-complete tiles (BN >= N); the K step shrinks with the tile so
+      // Row-complete tiles (BN == N); the K step shrinks with the tile so
       // that the double-buffered tiles fit in LDS.
+      if (a.N != 64 && a.N != 128 && a.N != 256 && a.N != 512) return hipErrorInvalidValue;
       if (a.N <= 64) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 64, 32>(a, st);
       if (a.N <= 128) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 128, 32>(a, st);
       if (a.N <= 256) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 256, 32>(a, st);
