@@ -354,9 +354,12 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   constexpr int KLD = DH + 8, CPR = DH / 8;
   constexpr int NCH = kBN * CPR / (4 * 64);      // chunks per thread of one tensor (4 waves per tensor)
   static_assert(NCH >= 1 && kBN * CPR % (4 * 64) == 0, "tile/threads mismatch");
-  constexpr uint32_t kBufBytes = kBN * KLD * 2;
+  // V rows are 192 bytes apart: the four rows that 32 lanes of a transposing
+  // read touch then fall in four different 16-bank groups.
+  constexpr int VLD = DH + 32;
+  constexpr uint32_t kBufBytes = kBN * KLD * 2, kVBufBytes = kBN * VLD * 2;
   __shared__ __attribute__((aligned(32))) bf16 Ks[kNBUF][kBN * KLD];
-  __shared__ __attribute__((aligned(32))) bf16 Vs[kNBUF][kBN * KLD];
+  __shared__ __attribute__((aligned(32))) bf16 Vs[kNBUF][kBN * VLD];
 
   const int lid = xcd_remap(blockIdx.x, nblocks);
   const int qbi = lid % nqb;
@@ -402,12 +405,13 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   const int ntiles = (L + kBN - 1) / kBN;
   // LDS byte addresses: per-lane part + uniform buffer offset + constants.
   const uint32_t kbase = lds_addr(&Ks[0][0]) + 2 * (l32 * KLD + 8 * hh);
-  const uint32_t vbase = lds_addr(&Vs[0][0]) + 2 * lds_colA_lane<bf16>(KLD, lane);
+  const uint32_t vbase = lds_addr(&Vs[0][0]) + 2 * lds_colA_lane<bf16>(VLD, lane);
 
   // Group A moves K tiles, group B V tiles.  Rows past the history are copies
   // of its last row (unmasked loads); their scores are set to -inf.
   const bf16* Gsrc = (grp == 0 ? K : V) + lo * d + j * DH;
   bf16* Gdst = grp == 0 ? &Ks[0][0] : &Vs[0][0];
+  const int gld = grp == 0 ? KLD : VLD;
   // Two register stages: tile t is staged in xr[t & 1].  It is loaded by this
   // group's MFMA step t-2, between its score MFMAs (loads issued there cost
   // the matrix cores less than a burst of loads at the start of a VALU
@@ -427,7 +431,7 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     for (int i = 0; i < NCH; ++i) {
       const int ch = gtid + i * 256;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
-      st8<bf16>(Gdst + buf * (kBN * KLD) + row * KLD + e0, xs[i]);
+      st8<bf16>(Gdst + buf * (kBN * gld) + row * gld + e0, xs[i]);
     }
   };
 
@@ -465,7 +469,7 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x0008, 8, 0);
     if (u >= 1) {
-      const uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kBufBytes;
+      const uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kVBufBytes;
       // Four independent output chains (e, qb) interleaved.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -474,8 +478,8 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
           bf16x8 a[NE];
 #pragma unroll
           for (int e = 0; e < NE; ++e) {
-            const uint32_t o = vaddr + 2 * ((32 * kb + 16 * mm) * KLD + 32 * e);
-            a[e] = cat44<bf16>(lds_tr4_at(o), lds_tr4_at(o + 2 * 8 * KLD));
+            const uint32_t o = vaddr + 2 * ((32 * kb + 16 * mm) * VLD + 32 * e);
+            a[e] = cat44<bf16>(lds_tr4_at(o), lds_tr4_at(o + 2 * 8 * VLD));
           }
 #pragma unroll
           for (int e = 0; e < NE; ++e)
