@@ -676,8 +676,21 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
                                                            int64_t nsplit_elems) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
-  float s = 0.f;
-  for (int k = 0; k < splits; ++k) s += part[(int64_t)k * n + i];
+  // Eight partial sums (slice k goes to sum k % 8), eight loads in flight,
+  // combined in a fixed tree: deterministic.
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  int k = 0;
+  for (; k + 8 <= splits; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = part[(int64_t)(k + u) * n + i];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc[u] += v[u];
+  }
+  for (; k < splits; ++k) acc[k & 7] += part[(int64_t)k * n + i];
+  const float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
   if (out2 != nullptr && i >= nsplit_elems) out2[i - nsplit_elems] = s;
   else out[i] = s;
 }

@@ -155,9 +155,21 @@ __global__ __launch_bounds__(256) void colsum1_kernel(const float* __restrict__ 
   const int cg = blockIdx.x, s = blockIdx.y;
   const int ph = threadIdx.x >> 6, c = cg * 64 + (threadIdx.x & 63);
   const int64_t r0 = (int64_t)s * R / S, r1 = (int64_t)(s + 1) * R / S;
-  float acc = 0.f;
-  if (c < n2)
-    for (int64_t r = r0 + ph; r < r1; r += 4) acc += part[r * n2 + c];
+  // Four partial sums per thread (rows r, r+4, r+8, r+12 of each group of
+  // 16), four loads in flight, combined in a fixed order.
+  float a4[4] = {0.f, 0.f, 0.f, 0.f};
+  if (c < n2) {
+    int64_t r = r0 + ph;
+    for (; r + 12 < r1; r += 16) {
+      float v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = part[(r + 4 * u) * n2 + c];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) a4[u] += v[u];
+    }
+    for (int u = 0; r < r1; r += 4, ++u) a4[u & 3] += part[r * n2 + c];
+  }
+  const float acc = (a4[0] + a4[1]) + (a4[2] + a4[3]);
   red[ph][threadIdx.x & 63] = acc;
   __syncthreads();
   if (ph == 0 && c < n2) out[(int64_t)s * n2 + c] = ((red[0][threadIdx.x] + red[1][threadIdx.x]) + red[2][threadIdx.x]) +
@@ -169,8 +181,20 @@ __global__ __launch_bounds__(256) void colsum2_kernel(const float* __restrict__ 
                                                       float* __restrict__ dgamma, float* __restrict__ dbeta) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= 2 * n) return;
-  float acc = 0.f;
-  for (int s = 0; s < S; ++s) acc += p2[(int64_t)s * 2 * n + c];
+  // Eight partial sums (row s goes to sum s % 8), combined in a fixed order.
+  float a8[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) a8[u] = 0.f;
+  int s = 0;
+  for (; s + 8 <= S; s += 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p2[(int64_t)(s + u) * 2 * n + c];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a8[u] += v[u];
+  }
+  for (; s < S; ++s) a8[s & 7] += p2[(int64_t)s * 2 * n + c];
+  const float acc = ((a8[0] + a8[1]) + (a8[2] + a8[3])) + ((a8[4] + a8[5]) + (a8[6] + a8[7]));
   if (c < n) { if (dgamma) dgamma[c] = acc; }
   else if (dbeta) dbeta[c - n] = acc;
 }
