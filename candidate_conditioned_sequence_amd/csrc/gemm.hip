@@ -525,9 +525,11 @@ template <typename T, int PRO, int GPRO>
 __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, int ntiles, int64_t chunk) {
   __shared__ __attribute__((aligned(32))) T Gt[2][WN * LDW];   // [n][m]
   __shared__ __attribute__((aligned(32))) T Xt[2][WK * LDW];   // [k][m]
-  const int split = blockIdx.y;
-  const int lid = xcd_remap(blockIdx.x, ntiles);
-  const int tk = lid % tiles_k, tnn = lid / tiles_k;
+  // One logical id per (slice, tile); consecutive ids share an XCD, so the
+  // tiles of one slice, which read the same rows of G and X, meet in its L2.
+  const int lid = xcd_remap(blockIdx.x, gridDim.x);
+  const int split = lid / ntiles, tl = lid % ntiles;
+  const int tk = tl % tiles_k, tnn = tl / tiles_k;
   const int n0 = tnn * WN, k0 = tk * WK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wm = w >> 1, wn = w & 1;
@@ -567,12 +569,15 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
     for (int u = 0; u < 8; ++u) { gm[u] = a.gamma[xcol + u]; bt[u] = a.norm_kind == 0 ? a.beta[xcol + u] : 0.f; }
   }
 
-  // Raw loads of one m-step; the prologues run when the step is stored.
-  x8_t<T> gr[4], gz[4], xr[4], xz[4];
-  float mn[4], rs[4];
-  int64_t mrow0 = 0;
-  auto load = [&](int64_t mbase) {
-    mrow0 = mbase;
+  // Raw loads of one m-step into a register stage; the prologues run when
+  // the stage is stored.
+  struct Stage {
+    x8_t<T> gr[4], gz[4], xr[4], xz[4];
+    float mn[4], rs[4];
+    int64_t mrow0;
+  };
+  auto load = [&](Stage& S, int64_t mbase) {
+    S.mrow0 = mbase;
     int64_t mr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) mr[i] = mbase + rb + i;
@@ -583,43 +588,43 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t m = mr[i];
-      gr[i] = ld8<T>(gsrc + m * a.ldg);
-      if (GPRO == 1) gz[i] = ld8<T>(gsrcz + m * a.ldg);
-      xr[i] = ld8<T>(xsrc + m * xld);
-      if (PRO == WPRO_GATE_SEP) xz[i] = ld8<T>(xsrcz + m * xld);
-      if (PRO == WPRO_NORM && a.norm_kind != 2) { mn[i] = a.stats[2 * m]; rs[i] = a.stats[2 * m + 1]; }
+      S.gr[i] = ld8<T>(gsrc + m * a.ldg);
+      if (GPRO == 1) S.gz[i] = ld8<T>(gsrcz + m * a.ldg);
+      S.xr[i] = ld8<T>(xsrc + m * xld);
+      if (PRO == WPRO_GATE_SEP) S.xz[i] = ld8<T>(xsrcz + m * xld);
+      if (PRO == WPRO_NORM && a.norm_kind != 2) { S.mn[i] = a.stats[2 * m]; S.rs[i] = a.stats[2 * m + 1]; }
     }
   };
   // Prologues, zeros for rows past the chunk, then transposed into
   // [column][m]: 4 consecutive m of one column per write.
-  auto store = [&](int buf) {
+  auto store = [&](Stage& S, int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      x8_t<T> g = GPRO == 1 ? dact8<T>(gr[i], gz[i]) : gr[i];
-      x8_t<T> x = xr[i];
+      x8_t<T> g = GPRO == 1 ? dact8<T>(S.gr[i], S.gz[i]) : S.gr[i];
+      x8_t<T> x = S.xr[i];
       if (PRO == WPRO_GATE_TIED) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) { const float uf = to_f(x[e]); x[e] = from_f<T>(siluf_(uf) * uf); }
       } else if (PRO == WPRO_GATE_SEP) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = from_f<T>(siluf_(to_f(x[e])) * to_f(xz[i][e]));
+        for (int e = 0; e < 8; ++e) x[e] = from_f<T>(siluf_(to_f(x[e])) * to_f(S.xz[i][e]));
       } else if (PRO == WPRO_NORM && a.norm_kind != 2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = from_f<T>((to_f(x[e]) - mn[i]) * rs[i] * gm[e] + bt[e]);
+        for (int e = 0; e < 8; ++e) x[e] = from_f<T>((to_f(x[e]) - S.mn[i]) * S.rs[i] * gm[e] + bt[e]);
       }
-      gr[i] = g;
-      xr[i] = x;
+      S.gr[i] = g;
+      S.xr[i] = x;
     }
-    if (mrow0 + WM > me) {
+    if (S.mrow0 + WM > me) {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (mrow0 + rb + i >= me) { gr[i] = zero8<T>(); xr[i] = zero8<T>(); }
+        if (S.mrow0 + rb + i >= me) { S.gr[i] = zero8<T>(); S.xr[i] = zero8<T>(); }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       x4_t<T> tg, tx;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { tg[i] = gr[i][e]; tx[i] = xr[i][e]; }
+      for (int i = 0; i < 4; ++i) { tg[i] = S.gr[i][e]; tx[i] = S.xr[i][e]; }
       st4<T>(&Gt[buf][(cb + e) * LDW + rb], tg);
       st4<T>(&Xt[buf][(cb + e) * LDW + rb], tx);
     }
@@ -632,14 +637,11 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
     for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
 
   const int64_t nsteps = me > mb ? (me - mb + WM - 1) / WM : 0;
-  if (nsteps > 0) {
-    load(mb);
-    store(0);
-  }
-  __syncthreads();
-  for (int64_t s = 0; s < nsteps; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < nsteps) load(mb + (s + 1) * WM);
+  // MFMAs of one step on LDS buffer buf, with the loads of step `next` into
+  // stage L issued between them (the last steps reload the last step).
+  auto step = [&](int buf, Stage& L, int64_t next) {
+    __builtin_amdgcn_s_setprio(1);
+    load(L, mb + min(next, nsteps - 1) * WM);
 #pragma unroll
     for (int ks = 0; ks < WM / 16; ++ks) {
       x8_t<T> af[2], bf[2];
@@ -652,9 +654,41 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) mma32(acc[i][jj], af[i], bf[jj]);
     }
-    if (s + 1 < nsteps) store(buf ^ 1);
+    if constexpr (sizeof(T) == 2) {
+      constexpr int NV = 4 * (2 + (GPRO == 1) + (PRO == WPRO_GATE_SEP));
+#pragma unroll
+      for (int ks = 0; ks < WM / 16; ++ks) {
+        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+#pragma unroll
+        for (int mq = 0; mq < 4; ++mq) {
+          __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
+          if (4 * ks + mq < NV) __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+  // Two register stages: step s + 2 is loaded while step s is multiplied and
+  // step s + 1 stored.  Whole pairs of steps run as one straight block (the
+  // last pair's second store writes a buffer that is not read again), then
+  // an odd last step.
+  Stage S0, S1;
+  if (nsteps > 0) {
+    load(S0, mb);
+    store(S0, 0);
+    load(S1, mb + min((int64_t)1, nsteps - 1) * WM);
+  }
+  __syncthreads();
+  int64_t s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    step(0, S0, s + 2);
+    store(S1, 1);
+    __syncthreads();
+    step(1, S1, s + 3);
+    store(S0, 0);
     __syncthreads();
   }
+  if (s < nsteps) step(0, S0, s + 2);
 
   // A dual output (dW | dW2) always goes through the partial buffer; the
   // reduction pass splits the rows.
@@ -706,7 +740,7 @@ hipError_t wgrad_t(const WgradArgs& a, hipStream_t st) {
   const int nt = tiles_k * tiles_n;
   int64_t chunk = (a.M + a.splits - 1) / a.splits;
   chunk = (chunk + WM - 1) / WM * WM;
-  dim3 grid(nt, a.splits);
+  dim3 grid((unsigned)(nt * a.splits));
   const bool gz = a.Gz != nullptr;
   switch (a.pro) {
     case WPRO_PLAIN: gz ? wgrad_launch<T, WPRO_PLAIN, 1>(a, grid, tiles_k, nt, chunk, st)
