@@ -519,10 +519,20 @@ hipError_t gemm_pro(const GemmArgs& a, hipStream_t st) {
 
 // ------------------------------------------------------------------ wgrad
 
-constexpr int WN = 128, WK = 128, WM = 64, LDW = WM + 8;
+constexpr int WM = 64, LDW = WM + 8;
 
-template <typename T, int PRO, int GPRO>
-__global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, int ntiles, int64_t chunk) {
+// Output tile TW x TW (TW = 128: 4 waves of 64 x 64; TW = 256, bf16: 8 waves
+// of 128 x 64, which reads every row of G and X half as often).
+template <int TW> struct WgTile {
+  static constexpr int NW = TW / 32;                       // waves
+  static constexpr int WTN = TW == 256 ? 128 : 64, WTK = 64;   // per-wave tile
+  static constexpr int NWK = TW / WTK;                      // waves along K
+};
+
+template <typename T, int PRO, int GPRO, int TW>
+__global__ __launch_bounds__(TW / 32 * 64) void wgrad_kernel(WgradArgs a, int tiles_k, int ntiles, int64_t chunk) {
+  using Tl = WgTile<TW>;
+  constexpr int WN = TW, WK = TW, NI = Tl::WTN / 32, NJ = Tl::WTK / 32;
   __shared__ __attribute__((aligned(32))) T Gt[2][WN * LDW];   // [n][m]
   __shared__ __attribute__((aligned(32))) T Xt[2][WK * LDW];   // [k][m]
   // One logical id per (slice, tile); consecutive ids share an XCD, so the
@@ -532,7 +542,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
   const int tk = tl % tiles_k, tnn = tl / tiles_k;
   const int n0 = tnn * WN, k0 = tk * WK;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / Tl::NWK, wn = w % Tl::NWK;   // this wave's n and k sub-tile
   const int N = a.N, K = a.K;
   const int64_t mb = (int64_t)split * chunk;
   const int64_t me = min(a.M, mb + chunk);
@@ -630,11 +640,11 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[NI][NJ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) acc[i][jj] = zero16();
+    for (int jj = 0; jj < NJ; ++jj) acc[i][jj] = zero16();
 
   const int64_t nsteps = me > mb ? (me - mb + WM - 1) / WM : 0;
   // MFMAs of one step on LDS buffer buf, with the loads of step `next` into
@@ -644,25 +654,28 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
     load(L, mb + min(next, nsteps - 1) * WM);
 #pragma unroll
     for (int ks = 0; ks < WM / 16; ++ks) {
-      x8_t<T> af[2], bf[2];
+      x8_t<T> af[NI], bf[NJ];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) af[i] = ld8<T>(&Gt[buf][(wm * 64 + 32 * i + l32) * LDW + 16 * ks + 8 * hh]);
+      for (int i = 0; i < NI; ++i)
+        af[i] = ld8<T>(&Gt[buf][(wm * Tl::WTN + 32 * i + l32) * LDW + 16 * ks + 8 * hh]);
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) bf[jj] = ld8<T>(&Xt[buf][(wn * 64 + 32 * jj + l32) * LDW + 16 * ks + 8 * hh]);
+      for (int jj = 0; jj < NJ; ++jj)
+        bf[jj] = ld8<T>(&Xt[buf][(wn * Tl::WTK + 32 * jj + l32) * LDW + 16 * ks + 8 * hh]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) mma32(acc[i][jj], af[i], bf[jj]);
+        for (int jj = 0; jj < NJ; ++jj) mma32(acc[i][jj], af[i], bf[jj]);
     }
     if constexpr (sizeof(T) == 2) {
       constexpr int NV = 4 * (2 + (GPRO == 1) + (PRO == WPRO_GATE_SEP));
+      constexpr int NMQ = NI * NJ;
 #pragma unroll
       for (int ks = 0; ks < WM / 16; ++ks) {
-        __builtin_amdgcn_sched_group_barrier(0x0100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x0100, NI + NJ, 0);
 #pragma unroll
-        for (int mq = 0; mq < 4; ++mq) {
+        for (int mq = 0; mq < NMQ; ++mq) {
           __builtin_amdgcn_sched_group_barrier(0x0008, 1, 0);
-          if (4 * ks + mq < NV) __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
+          if (NMQ * ks + mq < NV) __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
         }
       }
     }
@@ -694,13 +707,13 @@ __global__ __launch_bounds__(256) void wgrad_kernel(WgradArgs a, int tiles_k, in
   // reduction pass splits the rows.
   float* out = (a.splits > 1 || a.dW2 != nullptr) ? a.partial + (int64_t)split * N * K : a.dW;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < NI; ++i)
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+    for (int jj = 0; jj < NJ; ++jj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int n = n0 + wm * 64 + 32 * i + acc_row(r, hh);
-        const int k = k0 + wn * 64 + 32 * jj + l32;
+        const int n = n0 + wm * Tl::WTN + 32 * i + acc_row(r, hh);
+        const int k = k0 + wn * Tl::WTK + 32 * jj + l32;
         if (n < N && k < K) out[(int64_t)n * K + k] = acc[i][jj][r];
       }
 }
@@ -729,27 +742,43 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   else out[i] = s;
 }
 
+// The 256-wide tile needs N, K >= 256 (and bf16, for its LDS).
+bool wgrad_big_tile(int N, int K) { return N >= 256 && K >= 256; }
+
+// Prologues with extra operands (activation input, norm statistics, separate
+// gate) keep the 128-wide tile: the 256-wide one would spill.
 template <typename T, int PRO, int GPRO>
-void wgrad_launch(const WgradArgs& a, dim3 grid, int tiles_k, int nt, int64_t chunk, hipStream_t st) {
-  hipLaunchKernelGGL((wgrad_kernel<T, PRO, GPRO>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk);
+constexpr bool wgrad_big_ok() { return sizeof(T) == 2 && GPRO == 0 && PRO != WPRO_NORM && PRO != WPRO_GATE_SEP; }
+
+template <typename T, int PRO, int GPRO>
+void wgrad_launch(const WgradArgs& a, dim3 grid, int tiles_k, int nt, int64_t chunk, bool big, hipStream_t st) {
+  if constexpr (wgrad_big_ok<T, PRO, GPRO>()) {
+    if (big) {
+      hipLaunchKernelGGL((wgrad_kernel<T, PRO, GPRO, 256>), grid, dim3(512), 0, st, a, tiles_k, nt, chunk);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((wgrad_kernel<T, PRO, GPRO, 128>), grid, dim3(256), 0, st, a, tiles_k, nt, chunk);
 }
 
 template <typename T>
 hipError_t wgrad_t(const WgradArgs& a, hipStream_t st) {
-  const int tiles_k = (a.K + WK - 1) / WK, tiles_n = (a.N + WN - 1) / WN;
+  const bool gz = a.Gz != nullptr;
+  const bool big = sizeof(T) == 2 && wgrad_big_tile(a.N, a.K) && !gz && a.pro != WPRO_NORM && a.pro != WPRO_GATE_SEP;
+  const int TWv = big ? 256 : 128;
+  const int tiles_k = (a.K + TWv - 1) / TWv, tiles_n = (a.N + TWv - 1) / TWv;
   const int nt = tiles_k * tiles_n;
   int64_t chunk = (a.M + a.splits - 1) / a.splits;
   chunk = (chunk + WM - 1) / WM * WM;
   dim3 grid((unsigned)(nt * a.splits));
-  const bool gz = a.Gz != nullptr;
   switch (a.pro) {
-    case WPRO_PLAIN: gz ? wgrad_launch<T, WPRO_PLAIN, 1>(a, grid, tiles_k, nt, chunk, st)
-                        : wgrad_launch<T, WPRO_PLAIN, 0>(a, grid, tiles_k, nt, chunk, st); break;
-    case WPRO_NORM: wgrad_launch<T, WPRO_NORM, 0>(a, grid, tiles_k, nt, chunk, st); break;
-    case WPRO_CONCAT: gz ? wgrad_launch<T, WPRO_CONCAT, 1>(a, grid, tiles_k, nt, chunk, st)
-                         : wgrad_launch<T, WPRO_CONCAT, 0>(a, grid, tiles_k, nt, chunk, st); break;
-    case WPRO_GATE_TIED: wgrad_launch<T, WPRO_GATE_TIED, 0>(a, grid, tiles_k, nt, chunk, st); break;
-    case WPRO_GATE_SEP: wgrad_launch<T, WPRO_GATE_SEP, 0>(a, grid, tiles_k, nt, chunk, st); break;
+    case WPRO_PLAIN: gz ? wgrad_launch<T, WPRO_PLAIN, 1>(a, grid, tiles_k, nt, chunk, big, st)
+                        : wgrad_launch<T, WPRO_PLAIN, 0>(a, grid, tiles_k, nt, chunk, big, st); break;
+    case WPRO_NORM: wgrad_launch<T, WPRO_NORM, 0>(a, grid, tiles_k, nt, chunk, big, st); break;
+    case WPRO_CONCAT: gz ? wgrad_launch<T, WPRO_CONCAT, 1>(a, grid, tiles_k, nt, chunk, big, st)
+                         : wgrad_launch<T, WPRO_CONCAT, 0>(a, grid, tiles_k, nt, chunk, big, st); break;
+    case WPRO_GATE_TIED: wgrad_launch<T, WPRO_GATE_TIED, 0>(a, grid, tiles_k, nt, chunk, big, st); break;
+    case WPRO_GATE_SEP: wgrad_launch<T, WPRO_GATE_SEP, 0>(a, grid, tiles_k, nt, chunk, big, st); break;
     default: return hipErrorInvalidValue;
   }
   hipError_t e = hipGetLastError();
@@ -799,8 +828,13 @@ hipError_t launch_gemm_nt(const GemmArgs& a, bool bf16_data, hipStream_t st) {
 }
 
 int wgrad_splits(int64_t M, int N, int K) {
-  const int tiles = ((N + WN - 1) / WN) * ((K + WK - 1) / WK);
-  int64_t s = (1024 + tiles - 1) / tiles;
+  // About 256 workgroups of the 256-wide tile (one per CU), else 1024 of the
+  // 128-wide one.  (fp32 runs the 128-wide tile with the same count.)
+  const bool big = wgrad_big_tile(N, K);
+  const int TWv = big ? 256 : 128;
+  const int tiles = ((N + TWv - 1) / TWv) * ((K + TWv - 1) / TWv);
+  const int target = big ? 256 : 1024;
+  int64_t s = (target + tiles - 1) / tiles;
   const int64_t maxs = (M + 511) / 512;
   if (s > maxs) s = maxs;
   if (s < 1) s = 1;
