@@ -20,6 +20,8 @@
 // of the next product, with the A operand read column-wise from the same
 // row-major LDS tile (transposing LDS reads) in the matching row order.
 // Deterministic: no atomics.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -83,14 +85,15 @@ WHALE_DEV void p_ds_pack(const f32x16& s, const f32x16& dp, x8_t<T> (&pf)[2], x8
 // score MFMA; -D likewise starts the dP MFMA, so P = exp2(acc) and
 // dS = P * acc' need no other VALU work.  fp32 keeps Q exact and forms t with
 // one fused multiply-add.
-template <typename T, int DH>
-__global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
+template <typename T, int DH, int NWQ>
+__global__ __launch_bounds__(NWQ * 64, 2) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const T* __restrict__ dA, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, T* __restrict__ dQ, int d, int h, int QR, int nqb, float c, float scale,
     int nblocks) {
-  constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = kNW * 32;
-  constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (kNW * 64);
+  constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = NWQ * 32;
+  constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (NWQ * 64);
+  static_assert(NCH >= 1 && BN * CPR % (NWQ * 64) == 0, "tile/threads mismatch");
   constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Ks[2][BN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][BN * KLD];
@@ -136,7 +139,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
     const int last = L - 1 - t * BN;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + i * kNW * 64;
+      const int ch = tid + i * NWQ * 64;
       const int row = min(ch / CPR, last), e0 = 8 * (ch % CPR);
       const int64_t off = (int64_t)(t * BN + row) * d + e0;
       kr[i] = ld8<T>(Kh + off);
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + i * kNW * 64;
+      const int ch = tid + i * NWQ * 64;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       st8<T>(&Ks[buf][row * KLD + e0], kr[i]);
       st8<T>(&Vs[buf][row * KLD + e0], vr[i]);
@@ -238,14 +241,16 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dq_kernel(
 // starting values.  bf16 folds c into the K fragments.  Query rows past the
 // split are loaded as copies of its last row with -lse2 = -inf, so P = 0 and
 // dS = 0 for them.
-template <typename T, int DH>
-__global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
+template <typename T, int DH, int NWK>
+__global__ __launch_bounds__(NWK * 64, 2) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const T* __restrict__ dA, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ part,
     int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks) {
   constexpr int QT = 64, KS = DH / 16, NE = DH / 32;
-  constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (kNW * 64);
+  constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (NWK * 64);
+  constexpr int KB = NWK * 32;   // history rows per workgroup
+  static_assert(NCH >= 1 && QT * CPR % (NWK * 64) == 0, "tile/threads mismatch");
   constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Qs[2][QT * KLD];
   __shared__ __attribute__((aligned(32))) T Gs[2][QT * KLD];
@@ -259,12 +264,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
   const int j = bj % h, b = bj / h;
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
-  if (kt * 128 >= L) return;                       // workgroup-uniform
+  if (kt * KB >= L) return;                        // workgroup-uniform
   const int q_begin = split * qchunk;
   const int q_end = min(QR, q_begin + qchunk);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
   const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar
-  const int key = kt * 128 + w * 32 + l32;
+  const int key = kt * KB + w * 32 + l32;
   const bool kok = key < L;
   const int64_t qrow0 = (int64_t)b * QR;
 
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
     const int qt0 = q_begin + t * QT;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + i * kNW * 64;
+      const int ch = tid + i * NWK * 64;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       const int qq = min(qt0 + row, q_end - 1);
       const int64_t off = (qrow0 + qq) * d + j * DH + e0;
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void bwd_dkdv_kernel(
   auto store_tile = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = tid + i * kNW * 64;
+      const int ch = tid + i * NWK * 64;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       st8<T>(&Qs[buf][row * KLD + e0], qr[i]);
       st8<T>(&Gs[buf][row * KLD + e0], gr[i]);
@@ -444,24 +449,44 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   {
-    const int nqb = (a.QR + kNW * 32 - 1) / (kNW * 32);
-    const int64_t nblk = (int64_t)a.B * a.h * nqb;
-    hipLaunchKernelGGL((bwd_dq_kernel<T, DH>), dim3((unsigned)nblk), dim3(kNW * 64), 0, st, (const T*)a.Q,
-                       (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf, (T*)a.dQ, a.d, a.h,
-                       a.QR, nqb, c, a.scale, (int)nblk);
+    // Eight waves (256 queries) per workgroup where the request has enough
+    // queries: one K/V tile load then serves twice the queries of a CU.
+    auto go = [&](auto nwq) {
+      constexpr int NWQ = decltype(nwq)::value;
+      const int nqb = (a.QR + NWQ * 32 - 1) / (NWQ * 32);
+      const int64_t nblk = (int64_t)a.B * a.h * nqb;
+      hipLaunchKernelGGL((bwd_dq_kernel<T, DH, NWQ>), dim3((unsigned)nblk), dim3(NWQ * 64), 0, st, (const T*)a.Q,
+                         (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf, (T*)a.dQ, a.d, a.h,
+                         a.QR, nqb, c, a.scale, (int)nblk);
+    };
+    bool done = false;
+    if constexpr (DH == 64) {
+      if (a.QR >= 512) { go(std::integral_constant<int, 8>()); done = true; }
+    }
+    if (!done) go(std::integral_constant<int, kNW>());
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.T == 0 || a.max_L == 0) return hipSuccess;
   {
-    const int nkt = (a.max_L + 127) / 128;
-    const int64_t nblk = (int64_t)a.B * a.h * nkt;
     int qchunk = (a.QR + a.splits - 1) / a.splits;
     qchunk = (qchunk + 63) / 64 * 64;
     float* part = a.splits > 1 ? a.partial : nullptr;
-    hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH>), dim3((unsigned)nblk, a.splits), dim3(kNW * 64), 0, st,
-                       (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf,
-                       (T*)a.dK, (T*)a.dV, part, a.d, a.h, a.QR, nkt, qchunk, c, a.scale, a.T, (int)nblk);
+    // Eight waves (256 history rows) per workgroup when there is no query
+    // split: one Q / dA tile load then serves twice the rows of a CU.
+    auto go = [&](auto nwk) {
+      constexpr int NWK = decltype(nwk)::value;
+      const int nkt = (a.max_L + NWK * 32 - 1) / (NWK * 32);
+      const int64_t nblk = (int64_t)a.B * a.h * nkt;
+      hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, NWK>), dim3((unsigned)nblk, a.splits), dim3(NWK * 64), 0, st,
+                         (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf,
+                         (T*)a.dK, (T*)a.dV, part, a.d, a.h, a.QR, nkt, qchunk, c, a.scale, a.T, (int)nblk);
+    };
+    bool done = false;
+    if constexpr (DH == 64) {
+      if (a.splits == 1) { go(std::integral_constant<int, 8>()); done = true; }
+    }
+    if (!done) go(std::integral_constant<int, kNW>());
     e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     const int64_t n = a.T * a.d;
