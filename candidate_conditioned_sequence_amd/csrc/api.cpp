@@ -159,6 +159,25 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
   const bool bf = dtype == WHALE_BF16;
   const int nk = (int)norm;
   const bool nrm = norm != WHALE_NORM_NONE;
+  if (bf && rs_fwd_ok(s.d, s.d) && rs_fwd_ok(s.d, 2 * s.d)) {
+    // Row-streaming kernels: the norm (statistics, X_q / X_s) and the
+    // projection in one pass over the rows; K and V together.
+    RsFwdArgs q;
+    q.H = (const __bf16*)H_w; q.ldh = s.d; q.W = (const __bf16*)W_Q; q.W2 = (const __bf16*)W_Q; q.nsplit = s.d;
+    q.Y = (__bf16*)Q; q.Y2 = (__bf16*)Q; q.ldy = s.d;
+    q.Xn = nrm ? (__bf16*)X_q : nullptr; q.stats = nrm ? stats_q : nullptr;
+    q.gamma = g_q; q.beta = b_q; q.M = s.M; q.kind = nk; q.eps = eps;
+    WHALE_TRY(launch_rs_fwd(q, s.d, s.d, stream));
+    if (s.T > 0) {
+      RsFwdArgs kv = q;
+      kv.H = (const __bf16*)H_s; kv.W = (const __bf16*)W_K; kv.W2 = (const __bf16*)W_V;
+      kv.Y = (__bf16*)K; kv.Y2 = (__bf16*)V;
+      kv.Xn = nrm ? (__bf16*)X_s : nullptr; kv.stats = nrm ? stats_kv : nullptr;
+      kv.gamma = g_kv; kv.beta = b_kv; kv.M = s.T;
+      WHALE_TRY(launch_rs_fwd(kv, s.d, 2 * s.d, stream));
+    }
+    return WHALE_OK;
+  }
   // Each input is normalised either once into X_q / X_s (statistics computed
   // in the same pass) or, without them, per tile in the GEMM prologue.
   const bool mq = nrm && X_q != nullptr, ms = nrm && X_s != nullptr && s.T > 0;
@@ -500,19 +519,37 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
     WHALE_TRY(launch_fill_zero(dW_V, (int64_t)d * d, stream));
   }
   // dH_w = Norm_q backward(dQ W_Q) + dH_w_in ; dH_s = Norm_kv backward([dK, dV] [W_K; W_V])
+  // bf16 at d = 256: the row-streaming kernels (weight slice resident, rows
+  // streamed once); their dgamma / dbeta partials are one row per workgroup.
+  const bool rs = bf && rs_bwd_ok(d, d) && rs_bwd_ok(2 * d, d);
+  auto rs_args = [&](const void* X, const void* X2, const void* Wt, const void* nx, const float* st,
+                     const float* g, const void* R, void* out, float* part, int64_t M) {
+    RsBwdArgs r;
+    r.X = (const __bf16*)X; r.X2 = (const __bf16*)X2; r.ldx = d; r.ldx2 = d; r.ksplit = d;
+    r.W = (const __bf16*)Wt; r.nx = (const __bf16*)nx; r.stats = st; r.gamma = g; r.R = (const __bf16*)R;
+    r.Y = (__bf16*)out; r.part = part; r.M = M; r.kind = nk;
+    return r;
+  };
   WHALE_TRY(launch_transpose(W_Q, d, d, WQt, d, 0, bf, stream));
-  WHALE_TRY(norm_bwd_gemm(dQ, d, nullptr, 0, WQt, d, d, H_w, stats_q, g_q, nk, dH_w_in, dH_w, npq, s.M, d, bf,
-                          stream));
+  if (rs)
+    WHALE_TRY(launch_rs_bwd(rs_args(dQ, nullptr, WQt, H_w, stats_q, g_q, dH_w_in, dH_w, npq, s.M), d, d, stream));
+  else
+    WHALE_TRY(norm_bwd_gemm(dQ, d, nullptr, 0, WQt, d, d, H_w, stats_q, g_q, nk, dH_w_in, dH_w, npq, s.M, d, bf,
+                            stream));
   if (norm != WHALE_NORM_NONE)
-    WHALE_TRY(launch_colsum_reduce(npq, gemm_norm_bwd_tiles(s.M), d, dg_q,
+    WHALE_TRY(launch_colsum_reduce(npq, rs ? rs_bwd_grid(s.M) : gemm_norm_bwd_tiles(s.M), d, dg_q,
                                    norm == WHALE_NORM_LAYER ? db_q : nullptr, cscr, stream));
   if (s.T > 0) {
     WHALE_TRY(launch_transpose(W_K, d, d, WKVt, 2 * d, 0, bf, stream));
     WHALE_TRY(launch_transpose(W_V, d, d, WKVt, 2 * d, d, bf, stream));
-    WHALE_TRY(norm_bwd_gemm(dK, d, dV, d, WKVt, 2 * d, 2 * d, H_s, stats_kv, g_kv, nk, nullptr, dH_s, npk, s.T, d,
-                            bf, stream));
+    if (rs)
+      WHALE_TRY(launch_rs_bwd(rs_args(dK, dV, WKVt, H_s, stats_kv, g_kv, nullptr, dH_s, npk, s.T), 2 * d, d,
+                              stream));
+    else
+      WHALE_TRY(norm_bwd_gemm(dK, d, dV, d, WKVt, 2 * d, 2 * d, H_s, stats_kv, g_kv, nk, nullptr, dH_s, npk, s.T,
+                              d, bf, stream));
     if (norm != WHALE_NORM_NONE)
-      WHALE_TRY(launch_colsum_reduce(npk, gemm_norm_bwd_tiles(s.T), d, dg_kv,
+      WHALE_TRY(launch_colsum_reduce(npk, rs ? rs_bwd_grid(s.T) : gemm_norm_bwd_tiles(s.T), d, dg_kv,
                                      norm == WHALE_NORM_LAYER ? db_kv : nullptr, cscr, stream));
   } else if (norm != WHALE_NORM_NONE) {
     WHALE_TRY(launch_fill_zero(dg_kv, d, stream));

@@ -82,6 +82,40 @@ struct GemmArgs {
 hipError_t launch_gemm_nt(const GemmArgs& a, bool bf16_data, hipStream_t st);
 inline int64_t gemm_norm_bwd_tiles(int64_t M) { return (M + 63) / 64; }
 
+// ------------------------------------------------ row-streaming projections
+// bf16 only.  Forward: Y = Norm(H) W^T for H [M, K] (row stride ldh); weight
+// rows [0, nsplit) come from W and write Y, rows [nsplit, N) come from W2
+// and write Y2 (both [*, K]; outputs with row stride ldy).  With kind 0/1
+// the rows are normalised (gamma, beta over K; beta unused for kind 1) and
+// the normalised rows go to Xn [M, K] and (mean, rstd) to stats [M, 2] when
+// those are given; kind 2 multiplies H as it is.  Shapes: rs_fwd_ok(K, N).
+struct RsFwdArgs {
+  const __bf16* H; int64_t ldh;
+  const __bf16* W; const __bf16* W2; int nsplit;
+  __bf16* Y; __bf16* Y2; int64_t ldy;
+  __bf16* Xn; float* stats;
+  const float* gamma; const float* beta;
+  int64_t M; int kind; float eps;
+};
+// Backward: dX [M, N] = Norm backward(dY W^T) + R with dY = [X | X2] split at
+// ksplit = 256 along K (X2 only for K = 512), W [N, K] (the transposed forward weight),
+// nx [M, N] the norm's input, stats its (mean, rstd), gamma [N]; R [M, N] may
+// be null.  Column partials of dgamma / dbeta go to part [rs_bwd_grid(M), 2, N]
+// (kind 0/1).  Shapes: rs_bwd_ok(K, N).
+struct RsBwdArgs {
+  const __bf16* X; const __bf16* X2; int64_t ldx, ldx2; int ksplit;
+  const __bf16* W;
+  const __bf16* nx; const float* stats; const float* gamma;
+  const __bf16* R;
+  __bf16* Y; float* part;
+  int64_t M; int kind;
+};
+bool rs_fwd_ok(int K, int N);
+bool rs_bwd_ok(int K, int N);
+int64_t rs_bwd_grid(int64_t M);
+hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st);
+hipError_t launch_rs_bwd(const RsBwdArgs& a, int K, int N, hipStream_t st);
+
 // dW[N,K] = sum_m G[m,n] * Xop[m,k], fp32, with optional prologue on Xop
 // (norm of X, concat [X | X2], or tied/separate gate recomputed from U) and
 // on G (G * SiLU'(Gz) when Gz is set).  With G2, columns >= nsplit of G come

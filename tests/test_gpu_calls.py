@@ -69,15 +69,29 @@ def test_xattn_fwd(gpu, case):
     assert_close("lse", got[fin], lse_ref[fin], dtype, factor=0.1)
 
 
-@pytest.mark.parametrize("dtype,norm,keep", [("f32", O.NORM_LAYER, False), ("bf16", O.NORM_LAYER, False),
-                                             ("bf16", O.NORM_RMS, False), ("f32", O.NORM_NONE, False),
-                                             ("f32", O.NORM_LAYER, True), ("bf16", O.NORM_LAYER, True),
-                                             ("bf16", O.NORM_RMS, True)])
-def test_proj_qkv(gpu, dtype, norm, keep):
+# bf16 at d = 256 runs the row-streaming kernels (32-row blocks, one
+# workgroup per CU); the long histories give workgroups several blocks each,
+# so the transfers run two blocks ahead, and leave a ragged last block.
+PROJ_L = [0, 200, 77]
+PROJ_LONG = [9000, 17000, 5, 31]
+PROJ_CASES = [
+    ("f32", O.NORM_LAYER, False, 128, PROJ_L), ("bf16", O.NORM_LAYER, False, 128, PROJ_L),
+    ("bf16", O.NORM_RMS, False, 128, PROJ_L), ("f32", O.NORM_NONE, False, 128, PROJ_L),
+    ("f32", O.NORM_LAYER, True, 128, PROJ_L), ("bf16", O.NORM_LAYER, True, 128, PROJ_L),
+    ("bf16", O.NORM_RMS, True, 128, PROJ_L),
+    ("bf16", O.NORM_LAYER, True, 256, PROJ_L), ("bf16", O.NORM_LAYER, False, 256, PROJ_L),
+    ("bf16", O.NORM_RMS, True, 256, PROJ_L), ("bf16", O.NORM_NONE, False, 256, PROJ_L),
+    ("bf16", O.NORM_LAYER, True, 256, PROJ_LONG), ("bf16", O.NORM_RMS, False, 256, [1, 33, 64]),
+]
+
+
+@pytest.mark.parametrize("dtype,norm,keep,d,L", PROJ_CASES,
+                         ids=lambda v: str(len(v)) if isinstance(v, list) else str(v))
+def test_proj_qkv(gpu, dtype, norm, keep, d, L):
     """keep: the normalised inputs are written out once (X_q, X_s) and the
     projections read them; otherwise the projections normalise per tile."""
-    print(f"\n[proj_qkv] {dtype} norm={norm} keep={keep}", flush=True)
-    B, C, n_q, d, h, L = 3, 5, 7, 128, 2, [0, 200, 77]
+    print(f"\n[proj_qkv] {dtype} norm={norm} keep={keep} d={d} L={L}", flush=True)
+    B, C, n_q, h = len(L), 5, 7, d // 64
     M, off = B * C * n_q, offsets(L)
     T = int(off[-1])
     Hw, Hs = draw(4, (M, d), dtype, 2.0) + 0.5, draw(5, (T, d), dtype)
@@ -98,6 +112,15 @@ def test_proj_qkv(gpu, dtype, norm, keep):
     if keep:
         assert_close("X_q", Xq, O.norm_fwd(Hw, norm, g[0], bt[0], 1e-5)[0], dtype)
         assert_close("X_s", Xs, O.norm_fwd(Hs, norm, g[1], bt[1], 1e-5)[0], dtype)
+    if norm != O.NORM_NONE:
+        # (statistics of the rows as the device holds them: H_w + 0.5 is
+        # rounded to bf16 again on upload)
+        for name, got, x in (("stats_q", sq, Hw), ("stats_kv", skv, Hs)):
+            x = (synth.round_bf16(x) if dtype == "bf16" else x).astype(np.float64)
+            mean = x.mean(1) if norm == O.NORM_LAYER else np.zeros(len(x))
+            var = ((x - mean[:, None]) ** 2).mean(1)
+            want = np.stack([mean, 1 / np.sqrt(var + 1e-5)], 1)
+            assert_close(name, got, want, "f32")
 
 
 @pytest.mark.parametrize("dtype,act", [("f32", O.ACT_SILU), ("bf16", O.ACT_SILU), ("bf16", O.ACT_NONE)])
@@ -236,14 +259,17 @@ def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d):
         assert_close("db_f", db, ref["db_f"], dtype)
 
 
-@pytest.mark.parametrize("dtype,norm,d,keep", [("f32", O.NORM_LAYER, 128, False), ("bf16", O.NORM_LAYER, 128, False),
-                                               ("bf16", O.NORM_RMS, 256, False), ("f32", O.NORM_LAYER, 64, False),
-                                               ("bf16", O.NORM_LAYER, 512, False), ("f32", O.NORM_NONE, 128, False),
-                                               ("bf16", O.NORM_LAYER, 256, True), ("f32", O.NORM_RMS, 128, True)])
-def test_proj_qkv_bwd(gpu, dtype, norm, d, keep):
+@pytest.mark.parametrize("dtype,norm,d,keep,L", [
+    ("f32", O.NORM_LAYER, 128, False, PROJ_L), ("bf16", O.NORM_LAYER, 128, False, PROJ_L),
+    ("bf16", O.NORM_RMS, 256, False, PROJ_L), ("f32", O.NORM_LAYER, 64, False, PROJ_L),
+    ("bf16", O.NORM_LAYER, 512, False, PROJ_L), ("f32", O.NORM_NONE, 128, False, PROJ_L),
+    ("bf16", O.NORM_LAYER, 256, True, PROJ_L), ("f32", O.NORM_RMS, 128, True, PROJ_L),
+    ("bf16", O.NORM_NONE, 256, False, PROJ_L), ("bf16", O.NORM_LAYER, 256, True, PROJ_LONG),
+    ("bf16", O.NORM_RMS, 256, True, [1, 33, 64])], ids=lambda v: str(len(v)) if isinstance(v, list) else str(v))
+def test_proj_qkv_bwd(gpu, dtype, norm, d, keep, L):
     """keep: the forward's normalised inputs are handed to the backward."""
-    print(f"\n[proj_qkv_bwd] {dtype} norm={norm} d={d} keep={keep}", flush=True)
-    B, C, n_q, L = 3, 5, 7, [0, 200, 77]
+    print(f"\n[proj_qkv_bwd] {dtype} norm={norm} d={d} keep={keep} L={L}", flush=True)
+    B, C, n_q = len(L), 5, 7
     h = d // 64
     M, off = B * C * n_q, offsets(L)
     T = int(off[-1])
