@@ -100,7 +100,7 @@ struct RsFwdArgs {
 // Backward: dX [M, N] = Norm backward(dY W^T) + R with dY = [X | X2] split at
 // ksplit = 256 along K (X2 only for K = 512), W [N, K] (the transposed forward weight),
 // nx [M, N] the norm's input, stats its (mean, rstd), gamma [N]; R [M, N] may
-// be null.  Column partials of dgamma / dbeta go to part [rs_bwd_grid(M), 2, N]
+// be null (and must be at K = 512).  Column partials of dgamma / dbeta go to part [rs_bwd_grid(M), 2, N]
 // (kind 0/1).  Shapes: rs_bwd_ok(K, N).
 struct RsBwdArgs {
   const __bf16* X; const __bf16* X2; int64_t ldx, ldx2; int ksplit;

@@ -100,6 +100,39 @@ WHALE_DEV void block_mfma(f32x16& acc, const bf16x8 (&wf)[K / 16], uint32_t xbuf
   __builtin_amdgcn_sched_group_barrier(0x0008, AHEAD, 0);
 }
 
+// Output staging.  A block of 32 rows x N columns (bf16) sits in LDS with
+// the 16-byte chunk c of row r at position c ^ (r & 7).  Each wave writes
+// its 4-column pieces (row l32, columns n0 + 8 g + 4 hh) from registers;
+// after a barrier, whole rows leave as 16 bytes per lane (N/8 lanes a row),
+// so every store instruction writes complete 128-byte lines.
+template <int N>
+WHALE_DEV void stage_piece(uint32_t ob, int l32, int hh, int n0, int g, const bf16x4& v) {
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int c = (n0 >> 3) + g;
+  *(lds_bf16x4*)(uintptr_t)(ob + l32 * (N * 2) + 16 * (c ^ (l32 & 7)) + 8 * hh) = v;
+}
+// Rows of the staged block: instruction j covers rows j * (64 / (N/8)) ...;
+// wave w takes j = w + NW t.  dst(m, n) gives the address of row m, column n.
+template <int N, int NW, typename Dst>
+WHALE_DEV void store_rows(uint32_t ob, int w, int lane, int64_t m0, int64_t M, Dst dst) {
+  constexpr int RC = N / 8, RPI = 64 / RC, NIW = kRB / RPI / NW;
+  static_assert(NIW >= 1 && (kRB / RPI) % NW == 0, "rows per wave");
+#pragma unroll
+  for (int t = 0; t < NIW; ++t) {
+    const int j = w + NW * t;
+    const int r = j * RPI + lane / RC, c = lane % RC;
+    const bf16x8 v = lds_ld8(ob + r * (N * 2) + 16 * (c ^ (r & 7)));
+    const int64_t m = m0 + r;
+    if (m < M) st8<bf16>(dst(m, 8 * c), v);
+  }
+}
+// vmcnt(IPW * k) for k = 0, 1, 2 newer blocks of transfers in flight.
+template <int IPW> WHALE_DEV void wait_newer(int k) {
+  if (k >= 2) wait_vm<2 * IPW>();
+  else if (k == 1) wait_vm<IPW>();
+  else wait_vm<0>();
+}
+
 WHALE_DEV bf16x4 lds_ld4(uint32_t a) {
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   return *(const lds_bf16x4*)(uintptr_t)a;
@@ -117,9 +150,10 @@ WHALE_DEV f32x4 lds_ldf4(uint32_t a) {
 // Y = Norm(H) W^T.  Waves with n0 < nsplit use W and write Y, the others W2
 // and Y2 (the K and V projections in one pass over the history rows).  Each
 // wave moves and normalises the rows of its own transfers (2 rows per
-// instruction at K = 256), so only the barrier that publishes the
-// normalised block is needed; three buffers let block i+2 arrive while
-// block i is multiplied and block i+1 normalised.
+// instruction at K = 256), so one barrier per block publishes both the
+// normalised next block and this block's staged output.  Four input
+// buffers keep three blocks of transfers in flight (HBM latency at one
+// workgroup per CU needs that much); two output tiles alternate.
 template <int K, int N>
 __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int NW = N / 32, NT = NW * 64;
@@ -127,9 +161,10 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int BLK = kRB * K * 2;                 // bytes per block
   constexpr int NI = BLK / 1024;                   // transfer instructions per block
   constexpr int IPW = NI / NW;                     // ... per wave
-  constexpr int NBUF = 3;
+  constexpr int NBUF = 4;
   static_assert(NI % NW == 0 && IPW >= 1 && K == 256, "one panel, whole instructions per wave");
   __shared__ __attribute__((aligned(1024))) char xs[NBUF][BLK];
+  __shared__ __attribute__((aligned(1024))) char ob[2][kRB * N * 2];
   __shared__ __attribute__((aligned(16))) float gb[2][K];
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
@@ -153,8 +188,9 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   // The weight slice is resident from here on: a wait the compiler sees, so
   // that it places no wait for these loads inside the loop.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  bf16* Yb = second ? a.Y2 : a.Y;
-  const int ycol = (second ? n0 - a.nsplit : n0) + 4 * hh;
+  auto ydst = [&](int64_t m, int n) {
+    return n < a.nsplit ? a.Y + m * a.ldy + n : a.Y2 + m * a.ldy + (n - a.nsplit);
+  };
 
   // Transfers of block b into buffer p: instruction j of the block covers
   // chunk positions [64 j, 64 j + 64); this wave issues j = w + NW t.
@@ -210,9 +246,8 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
     }
   };
 
-  if (nmine > 0) issue(b0, 0);
-  if (nmine > 1) issue(b0 + G, 1);
-  if (nmine > 1) wait_vm<IPW>(); else wait_vm<0>();
+  for (int k = 0; k < NBUF - 1 && k < nmine; ++k) issue(b0 + k * G, k);
+  wait_newer<IPW>(min(NBUF - 2, nmine - 1));        // block 0 landed
   __syncthreads();                                   // gamma / beta
   if (nmine > 0) normalise(b0, 0);
   __syncthreads();
@@ -220,27 +255,28 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   for (int i = 0; i < nmine; ++i) {
     const int p = i % NBUF;
     const int64_t m0 = (int64_t)(b0 + i * G) * kRB;
-    // Buffer (i+2) % 3 was last read by block i-1, before the last barrier.
-    if (i + 2 < nmine) issue(b0 + (i + 2) * G, (i + 2) % NBUF);
+    // Buffer (i+3) % 4 was last read by block i-1, before the last barrier.
+    if (i + NBUF - 1 < nmine) issue(b0 + (i + NBUF - 1) * G, (i + NBUF - 1) % NBUF);
     f32x16 acc = zero16();
     block_mfma<K>(acc, wf, lds_addr(&xs[p][0]), l32, hh);
-    // This wave's transfers of block i+1 have landed once at most the
-    // block i+2 ones are outstanding (loads complete in order).  The wait
-    // comes before this block's stores, so that it never counts them.
-    if (i + 2 < nmine) wait_vm<IPW>(); else wait_vm<0>();
-    const int64_t m = m0 + l32;
-    if (m < M) {
-      bf16* yrow = Yb + m * a.ldy + ycol;
+    // Output tile i & 1 was last read by the stores of block i-2, before
+    // the last barrier.
+    const uint32_t obp = lds_addr(&ob[i & 1][0]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 o;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 o;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) o[u] = from_f<bf16>(acc[4 * g + u]);
-        st4<bf16>(yrow + 8 * g, o);
-      }
+      for (int u = 0; u < 4; ++u) o[u] = from_f<bf16>(acc[4 * g + u]);
+      stage_piece<N>(obp, l32, hh, n0, g, o);
     }
-    if (i + 1 < nmine) normalise(b0 + (i + 1) * G, (i + 1) % NBUF);
+    // This wave's transfers of block i+1 have landed once at most the newer
+    // blocks' ones are outstanding (loads complete in order).
+    if (i + 1 < nmine) {
+      wait_newer<IPW>(min(NBUF - 2, nmine - i - 2));
+      normalise(b0 + (i + 1) * G, (i + 1) % NBUF);
+    }
     __syncthreads();
+    store_rows<N, NW>(obp, w, lane, m0, M, ydst);
   }
 }
 
@@ -248,11 +284,14 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
 // dX = Norm backward(dY W^T) + R with dY = [X | X2] split at ksplit along K.
 // Per block: MFMAs, then this wave's partial row sums of the norm backward
 // (over its 32 columns) go to LDS; one barrier publishes them and the next
-// block's transfers; then every wave forms the full row sums in a fixed
-// order and writes its columns.  dgamma / dbeta column partials accumulate
-// in registers over all rows a lane handles and are reduced across lanes
-// once, at the end: part [gridDim.x, 2, N].
-template <int K, int N>
+// block's transfers; then the transfers of block i+2 start, the previous
+// block's staged output rows are stored, and every wave forms the full row
+// sums in a fixed order and stages its columns.  Two input buffers are all
+// that fit next to the output tiles (x, R and the K-deep dY rows per block).
+// dgamma / dbeta column partials accumulate in registers over all rows a
+// lane handles and are reduced across lanes once, at the end:
+// part [gridDim.x, 2, N].  HASR: R is read (K = 256 only, for LDS space).
+template <int K, int N, bool HASR>
 __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
   constexpr int NW = N / 32, NT = NW * 64;
   constexpr int XB = kRB * K * 2, NB = kRB * N * 2;
@@ -261,7 +300,8 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
   static_assert((K == 256 || K == 512) && N == 256, "panels of 256 columns");
   __shared__ __attribute__((aligned(1024))) char xs[2][XB];
   __shared__ __attribute__((aligned(1024))) char ns[2][NB];
-  __shared__ __attribute__((aligned(1024))) char rsb[2][NB];
+  __shared__ __attribute__((aligned(1024))) char rsb[HASR ? 2 : 1][HASR ? NB : 16];
+  __shared__ __attribute__((aligned(1024))) char ob[2][NB];
   __shared__ __attribute__((aligned(256))) float ss[2][64];
   __shared__ __attribute__((aligned(16))) float red[2][NW][kRB][2];
   __shared__ __attribute__((aligned(16))) float gm[N];
@@ -273,7 +313,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
   const int G = gridDim.x, b0 = blockIdx.x;
   const int nmine = b0 < nblk ? (int)((nblk - 1 - b0) / G + 1) : 0;
   const int kind = a.kind;
-  const bool nrm = kind != 2, hasR = a.R != nullptr;
+  const bool nrm = kind != 2, hasR = HASR && a.R != nullptr;
 
   const int n0 = 32 * w;
   bf16x8 wf[K / 16];
@@ -309,11 +349,12 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
 #pragma unroll
       for (int t = 0; t < NI; ++t) {
         const int j = w + NW * t;
-        dma_rows(a.R, N, m0, 2 * j, M, lane, lds_addr(&rsb[p][1024 * j]));
+        dma_rows(a.R, N, m0, 2 * j, M, lane, lds_addr(&rsb[HASR ? p : 0][1024 * j]));
       }
     }
   };
 
+  auto ydst = [&](int64_t m, int n) { return a.Y + m * N + n; };
   float pg[16], pb[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) { pg[u] = 0.f; pb[u] = 0.f; }
@@ -345,7 +386,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
       const int c = swz((n0 >> 3) + g, l32);
       const uint32_t off = l32 * (N * 2) + 16 * c + 8 * hh;
       if (nrm) xv[g] = lds_ld4(lds_addr(&ns[p][0]) + off);
-      if (hasR) r4[g] = lds_ld4(lds_addr(&rsb[p][0]) + off);
+      if (hasR) r4[g] = lds_ld4(lds_addr(&rsb[HASR ? p : 0][0]) + off);
       const f32x4 gg = lds_ldf4(lds_addr(&gm[n0 + 8 * g + 4 * hh]));
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -363,6 +404,10 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
     // This wave's transfers of block i+1 (and its older stores) are done.
     wait_vm<0>();
     __syncthreads();
+    // Buffer p is free since the barrier; block i+2 goes there.
+    if (i + 2 < nmine) issue(b0 + (i + 2) * G, p);
+    // The previous block's output (staged before the barrier).
+    if (i > 0) store_rows<N, NW>(lds_addr(&ob[(i - 1) & 1][0]), w, lane, m0 - (int64_t)G * kRB, M, ydst);
 
     float c1 = 0.f, c2 = 0.f;
     if (nrm) {
@@ -376,9 +421,11 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
       c1 = kind == 0 ? t1 * invn : 0.f;
       c2 = t2 * invn;
     }
-    const int64_t m = m0 + l32;
-    if (m < M) {
-      bf16* orow = a.Y + m * N + n0 + 4 * hh;
+    // Output tile i & 1 was last read by the stores of block i-2, before
+    // this block's barrier.
+    const uint32_t obp = lds_addr(&ob[i & 1][0]);
+    const bool valid = m0 + l32 < M;
+    {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 gg = lds_ldf4(lds_addr(&gm[n0 + 8 * g + 4 * hh]));
@@ -390,14 +437,18 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
           const float xh = nrm ? (to_f(xv[g][u]) - mean) * rstd : 0.f;
           const float rv = hasR ? to_f(r4[g][u]) : 0.f;
           o[u] = from_f<bf16>(rv + (nrm ? rstd * (dxn * gg[u] - c1 - xh * c2) : dxn));
-          pg[e] += dxn * xh;
-          pb[e] += dxn;
+          if (valid) {
+            pg[e] += dxn * xh;
+            pb[e] += dxn;
+          }
         }
-        st4<bf16>(orow + 8 * g, o);
+        stage_piece<N>(obp, l32, hh, n0, g, o);
       }
     }
-    // Buffer p is free since the barrier; block i+2 goes there.
-    if (i + 2 < nmine) issue(b0 + (i + 2) * G, p);
+  }
+  if (nmine > 0) {
+    __syncthreads();
+    store_rows<N, NW>(lds_addr(&ob[(nmine - 1) & 1][0]), w, lane, (int64_t)(b0 + (nmine - 1) * G) * kRB, M, ydst);
   }
 
   if (nrm) {
@@ -445,12 +496,14 @@ hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
 
 hipError_t launch_rs_bwd(const RsBwdArgs& a, int K, int N, hipStream_t st) {
   // Columns [0, 256) of dY come from X, [256, 512) from X2.
-  if (!rs_bwd_ok(K, N) || a.M < 0 || a.ksplit != 256 || (K == 512 && a.X2 == nullptr)) return hipErrorInvalidValue;
+  // (At K = 512 the LDS holds no R tiles: R must be null there.)
+  if (!rs_bwd_ok(K, N) || a.M < 0 || a.ksplit != 256 || (K == 512 && (a.X2 == nullptr || a.R != nullptr)))
+    return hipErrorInvalidValue;
   if (a.M == 0) return hipSuccess;
   const int g = (int)rs_bwd_grid(a.M);
   if (K == 256)
-    hipLaunchKernelGGL((rs_bwd_kernel<256, 256>), dim3(g), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((rs_bwd_kernel<256, 256, true>), dim3(g), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((rs_bwd_kernel<512, 256>), dim3(g), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((rs_bwd_kernel<512, 256, false>), dim3(g), dim3(512), 0, st, a);
   return hipGetLastError();
 }
