@@ -167,6 +167,7 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
     q.Y = (__bf16*)Q; q.Y2 = (__bf16*)Q; q.ldy = s.d;
     q.Xn = nrm ? (__bf16*)X_q : nullptr; q.stats = nrm ? stats_q : nullptr;
     q.gamma = g_q; q.beta = b_q; q.M = s.M; q.kind = nk; q.eps = eps;
+    q.gate = 0; q.ngroups = 1; q.Z = nullptr; q.ldz = 0;
     WHALE_TRY(launch_rs_fwd(q, s.d, s.d, stream));
     if (s.T > 0) {
       RsFwdArgs kv = q;
@@ -266,6 +267,22 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   Carve c(workspace);
   void* G = c.take((size_t)s.M * H * esz(dtype));
   void* Xf = c.take((size_t)s.M * s.d * esz(dtype));
+  GemmArgs b = gemm_defaults();
+  b.X = G; b.ldx = H; b.W = W_D; b.ldw = H; b.Y = Y; b.ldy = s.d; b.R = F; b.ldr = s.d;
+  b.M = s.M; b.N = s.d; b.K = H; b.pro = PRO_PLAIN; b.epi = EPI_RESID;
+  constexpr int kGroup = 512;   // up-projection columns per row-streaming workgroup
+  if (bf && gate == WHALE_GATE_SHARED && rs_fwd_ok(s.d, kGroup) && H % kGroup == 0 && 256 % (8 * (H / kGroup)) == 0) {
+    // Up projection by the row-streaming kernel: Norm_f (statistics saved
+    // for the backward), F W_U^T and the tied gate in one pass over F.
+    RsFwdArgs u;
+    u.H = (const __bf16*)F; u.ldh = s.d; u.W = (const __bf16*)W_U; u.W2 = (const __bf16*)W_U; u.nsplit = kGroup;
+    u.Y = (__bf16*)G; u.Y2 = (__bf16*)G; u.ldy = H; u.Xn = nullptr;
+    u.stats = norm != WHALE_NORM_NONE ? stats_f : nullptr; u.gamma = g_f; u.beta = b_f;
+    u.M = s.M; u.kind = (int)norm; u.eps = eps;
+    u.gate = 1; u.ngroups = H / kGroup; u.Z = (__bf16*)U_saved; u.ldz = H;
+    WHALE_TRY(launch_rs_fwd(u, s.d, kGroup, stream));
+    return ret(launch_gemm_nt(b, bf, stream));
+  }
   // X_f = Norm_f(F) once (statistics saved for the backward), so that the
   // up projection does not renormalise F for every block of its H columns.
   const void* Xin = F;
@@ -281,9 +298,6 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   if (gate == WHALE_GATE_SHARED) { a.N = H; a.epi = EPI_GATE_TIED; a.ldz = H; }
   else { a.N = 2 * H; a.epi = EPI_GATE_SEP; a.ldz = 2 * H; }
   WHALE_TRY(launch_gemm_nt(a, bf, stream));
-  GemmArgs b = gemm_defaults();
-  b.X = G; b.ldx = H; b.W = W_D; b.ldw = H; b.Y = Y; b.ldy = s.d; b.R = F; b.ldr = s.d;
-  b.M = s.M; b.N = s.d; b.K = H; b.pro = PRO_PLAIN; b.epi = EPI_RESID;
   return ret(launch_gemm_nt(b, bf, stream));
 }
 

@@ -88,7 +88,8 @@ inline int64_t gemm_norm_bwd_tiles(int64_t M) { return (M + 63) / 64; }
 // and write Y2 (both [*, K]; outputs with row stride ldy).  With kind 0/1
 // the rows are normalised (gamma, beta over K; beta unused for kind 1) and
 // the normalised rows go to Xn [M, K] and (mean, rstd) to stats [M, 2] when
-// those are given; kind 2 multiplies H as it is.  Shapes: rs_fwd_ok(K, N).
+// those are given (by column group 0); kind 2 multiplies H as it is.
+// Shapes: rs_fwd_ok(K, N).
 struct RsFwdArgs {
   const __bf16* H; int64_t ldh;
   const __bf16* W; const __bf16* W2; int nsplit;
@@ -96,6 +97,10 @@ struct RsFwdArgs {
   __bf16* Xn; float* stats;
   const float* gamma; const float* beta;
   int64_t M; int kind; float eps;
+  // gate = 1: the tied SwiGLU gate.  W has ngroups * N rows (N per column
+  // group), Z [M, ngroups N] (row stride ldz, may be null) receives the
+  // product and Y the gated U = SiLU(Z) Z; W2 / Y2 / nsplit unused (nsplit = N).
+  int gate; int ngroups; __bf16* Z; int64_t ldz;
 };
 // Backward: dX [M, N] = Norm backward(dY W^T) + R with dY = [X | X2] split at
 // ksplit = 256 along K (X2 only for K = 512), W [N, K] (the transposed forward weight),

@@ -112,9 +112,10 @@ WHALE_DEV void stage_piece(uint32_t ob, int l32, int hh, int n0, int g, const bf
   *(lds_bf16x4*)(uintptr_t)(ob + l32 * (N * 2) + 16 * (c ^ (l32 & 7)) + 8 * hh) = v;
 }
 // Rows of the staged block: instruction j covers rows j * (64 / (N/8)) ...;
-// wave w takes j = w + NW t.  dst(m, n) gives the address of row m, column n.
-template <int N, int NW, typename Dst>
-WHALE_DEV void store_rows(uint32_t ob, int w, int lane, int64_t m0, int64_t M, Dst dst) {
+// wave w takes j = w + NW t.  emit(m, n, v) writes the 8 values v of row m
+// from column n on.
+template <int N, int NW, typename Emit>
+WHALE_DEV void store_rows(uint32_t ob, int w, int lane, int64_t m0, int64_t M, Emit emit) {
   constexpr int RC = N / 8, RPI = 64 / RC, NIW = kRB / RPI / NW;
   static_assert(NIW >= 1 && (kRB / RPI) % NW == 0, "rows per wave");
 #pragma unroll
@@ -123,7 +124,7 @@ WHALE_DEV void store_rows(uint32_t ob, int w, int lane, int64_t m0, int64_t M, D
     const int r = j * RPI + lane / RC, c = lane % RC;
     const bf16x8 v = lds_ld8(ob + r * (N * 2) + 16 * (c ^ (r & 7)));
     const int64_t m = m0 + r;
-    if (m < M) st8<bf16>(dst(m, 8 * c), v);
+    if (m < M) emit(m, 8 * c, v);
   }
 }
 // vmcnt(IPW * k) for k = 0, 1, 2 newer blocks of transfers in flight.
@@ -148,7 +149,10 @@ WHALE_DEV f32x4 lds_ldf4(uint32_t a) {
 
 // ------------------------------------------------------------------ forward
 // Y = Norm(H) W^T.  Waves with n0 < nsplit use W and write Y, the others W2
-// and Y2 (the K and V projections in one pass over the history rows).  Each
+// and Y2 (the K and V projections in one pass over the history rows).  With
+// the tied gate (gate = 1) the ngroups * N weight rows are split into
+// column groups of N, one per workgroup; the staged block holds Z = the
+// product (bf16) and the stores write Z (when kept) and U = SiLU(Z) Z.  Each
 // wave moves and normalises the rows of its own transfers (2 rows per
 // instruction at K = 256), so one barrier per block publishes both the
 // normalised next block and this block's staged output.  Four input
@@ -171,13 +175,18 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
             hh = lane >> 5;
   const int64_t M = a.M;
   const int64_t nblk = (M + kRB - 1) / kRB;
-  const int G = gridDim.x, b0 = blockIdx.x;
+  // Workgroup id 8 q + x (x = XCD): column group q % ngroups, row-block
+  // walker 8 (q / ngroups) + x, so the groups of one row block share an XCD.
+  const int ng = a.ngroups;
+  const int grp = (blockIdx.x >> 3) % ng;
+  const int G = gridDim.x / ng, b0 = ((blockIdx.x >> 3) / ng) * 8 + (blockIdx.x & 7);
   const int nmine = b0 < nblk ? (int)((nblk - 1 - b0) / G + 1) : 0;
   const bool nrm = a.kind != 2;
 
   const int n0 = 32 * w;
   const bool second = n0 >= a.nsplit;
-  const bf16* Wr = second ? a.W2 + (int64_t)(n0 - a.nsplit + l32) * K : a.W + (int64_t)(n0 + l32) * K;
+  const bf16* Wr = second ? a.W2 + (int64_t)(n0 - a.nsplit + l32) * K
+                          : a.W + (int64_t)(grp * N + n0 + l32) * K;
   bf16x8 wf[K / 16];
 #pragma unroll
   for (int ks = 0; ks < K / 16; ++ks) wf[ks] = ld8<bf16>(Wr + 16 * ks + 8 * hh);
@@ -188,8 +197,17 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   // The weight slice is resident from here on: a wait the compiler sees, so
   // that it places no wait for these loads inside the loop.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
-  auto ydst = [&](int64_t m, int n) {
-    return n < a.nsplit ? a.Y + m * a.ldy + n : a.Y2 + m * a.ldy + (n - a.nsplit);
+  auto emit = [&](int64_t m, int n, const bf16x8& v) {
+    if (a.gate) {
+      const int col = grp * N + n;
+      if (a.Z) st8<bf16>(a.Z + m * a.ldz + col, v);
+      bf16x8 u;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { const float z = to_f(v[e]); u[e] = from_f<bf16>(siluf_(z) * z); }
+      st8<bf16>(a.Y + m * a.ldy + col, u);
+    } else {
+      st8<bf16>(n < a.nsplit ? a.Y + m * a.ldy + n : a.Y2 + m * a.ldy + (n - a.nsplit), v);
+    }
   };
 
   // Transfers of block b into buffer p: instruction j of the block covers
@@ -240,8 +258,8 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)la = y;
       const int64_t m = m0 + r;
       if (m < M) {
-        if (a.Xn) st8<bf16>(a.Xn + m * K + 8 * c, y);
-        if (a.stats && pos == 0) *reinterpret_cast<f32x2*>(a.stats + 2 * m) = f32x2{mean, rstd};
+        if (a.Xn && grp == 0) st8<bf16>(a.Xn + m * K + 8 * c, y);
+        if (a.stats && pos == 0 && grp == 0) *reinterpret_cast<f32x2*>(a.stats + 2 * m) = f32x2{mean, rstd};
       }
     }
   };
@@ -276,7 +294,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       normalise(b0 + (i + 1) * G, (i + 1) % NBUF);
     }
     __syncthreads();
-    store_rows<N, NW>(obp, w, lane, m0, M, ydst);
+    store_rows<N, NW>(obp, w, lane, m0, M, emit);
   }
 }
 
@@ -354,7 +372,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_bwd_kernel(RsBwdArgs a) {
     }
   };
 
-  auto ydst = [&](int64_t m, int n) { return a.Y + m * N + n; };
+  auto ydst = [&](int64_t m, int n, const bf16x8& v) { st8<bf16>(a.Y + m * N + n, v); };
   float pg[16], pb[16];
 #pragma unroll
   for (int u = 0; u < 16; ++u) { pg[u] = 0.f; pb[u] = 0.f; }
@@ -484,9 +502,14 @@ int64_t rs_bwd_grid(int64_t M) {
 
 hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
   if (!rs_fwd_ok(K, N) || a.M < 0 || a.nsplit % 32 != 0 || a.nsplit <= 0) return hipErrorInvalidValue;
+  if (a.ngroups < 1 || kCUsRS % (8 * a.ngroups) != 0 || (a.ngroups > 1 && (!a.gate || a.nsplit != N)))
+    return hipErrorInvalidValue;
   if (a.M == 0) return hipSuccess;
+  // Row-block walkers per column group: a multiple of 8 (one set per XCD).
   const int64_t nblk = (a.M + kRB - 1) / kRB;
-  const int g = (int)(nblk < kCUsRS ? nblk : kCUsRS);
+  const int64_t per = kCUsRS / a.ngroups;
+  const int64_t gg = ((nblk < per ? nblk : per) + 7) / 8 * 8;
+  const int g = (int)(gg * a.ngroups);
   if (N == 256)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 256>), dim3(g), dim3(512), 0, st, a);
   else

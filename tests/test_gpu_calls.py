@@ -140,13 +140,18 @@ def test_fusion_mlp(gpu, dtype, act):
         assert_close("Z", Z, Z_ref, dtype)
 
 
-@pytest.mark.parametrize("dtype,gate,norm,d", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128),
-                                               ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256),
-                                               ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128),
-                                               ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64)])
-def test_swiglu_ffn(gpu, dtype, gate, norm, d):
-    print(f"\n[swiglu_ffn] {dtype} gate={gate} norm={norm} d={d}", flush=True)
-    M, H = 200, 4 * d
+# bf16, shared gate, d = 256 and H a multiple of 512: the up projection runs
+# in the row-streaming kernel (column groups of 512; M = 9001 gives its
+# workgroups several 32-row blocks and a ragged last one).
+@pytest.mark.parametrize("dtype,gate,norm,d,M,H", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128, 200, 512),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 200, 1024),
+                                                   ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128, 200, 512),
+                                                   ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64, 200, 256),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_RMS, 256, 9001, 1024),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_NONE, 256, 333, 512),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 77, 2048)])
+def test_swiglu_ffn(gpu, dtype, gate, norm, d, M, H):
+    print(f"\n[swiglu_ffn] {dtype} gate={gate} norm={norm} d={d} M={M} H={H}", flush=True)
     Fm = draw(14, (M, d), dtype)
     Wu = weights(15, (2 if gate == O.GATE_SEPARATE else 1) * H, d, dtype)
     Wd = weights(16, d, H, dtype)
@@ -164,6 +169,11 @@ def test_swiglu_ffn(gpu, dtype, gate, norm, d):
     torch.cuda.synchronize()
     assert_close("Y", Y, Y_ref, dtype)
     assert_close("U", U, U_ref, dtype)
+    if norm != O.NORM_NONE:
+        x = Fm.astype(np.float64)
+        mean = x.mean(1) if norm == O.NORM_LAYER else np.zeros(M)
+        want = np.stack([mean, 1 / np.sqrt(((x - mean[:, None]) ** 2).mean(1) + 1e-5)], 1)
+        assert_close("stats_f", sf, want, "f32")
 
 
 BWD_CASES = [
