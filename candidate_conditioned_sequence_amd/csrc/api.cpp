@@ -432,10 +432,20 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   WHALE_TRY(w1.gate(H).run(bf, stream));
   // dU = (dY W_D) * gate'(U)
   WHALE_TRY(launch_transpose(W_D, d, H, WDt, d, 0, bf, stream));       // [H, d]
-  GemmArgs g = gemm_defaults();
-  g.X = dY; g.ldx = d; g.W = WDt; g.ldw = d; g.Y = dU; g.ldy = Hu; g.Z = (void*)U_saved; g.ldz = Hu;
-  g.M = s.M; g.N = H; g.K = d; g.pro = PRO_PLAIN; g.epi = sep ? EPI_DGATE_SEP : EPI_DGATE_TIED;
-  WHALE_TRY(launch_gemm_nt(g, bf, stream));
+  constexpr int kGroup = 512;   // columns per row-streaming workgroup
+  if (bf && !sep && rs_fwd_ok(d, kGroup) && H % kGroup == 0 && 256 % (8 * (H / kGroup)) == 0) {
+    RsFwdArgs r;
+    r.H = (const __bf16*)dY; r.ldh = d; r.W = (const __bf16*)WDt; r.W2 = (const __bf16*)WDt; r.nsplit = kGroup;
+    r.Y = (__bf16*)dU; r.Y2 = (__bf16*)dU; r.ldy = Hu; r.Xn = nullptr; r.stats = nullptr;
+    r.gamma = nullptr; r.beta = nullptr; r.M = s.M; r.kind = 2; r.eps = 0.f;
+    r.gate = 2; r.ngroups = H / kGroup; r.Z = (__bf16*)U_saved; r.ldz = Hu;
+    WHALE_TRY(launch_rs_fwd(r, d, kGroup, stream));
+  } else {
+    GemmArgs g = gemm_defaults();
+    g.X = dY; g.ldx = d; g.W = WDt; g.ldw = d; g.Y = dU; g.ldy = Hu; g.Z = (void*)U_saved; g.ldz = Hu;
+    g.M = s.M; g.N = H; g.K = d; g.pro = PRO_PLAIN; g.epi = sep ? EPI_DGATE_SEP : EPI_DGATE_TIED;
+    WHALE_TRY(launch_gemm_nt(g, bf, stream));
+  }
   // dW_U = dU^T X_f, X_f = Norm_f(F) formed once from the saved statistics
   const void* Xin = F;
   if (norm != WHALE_NORM_NONE) {

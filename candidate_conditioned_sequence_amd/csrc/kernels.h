@@ -100,6 +100,9 @@ struct RsFwdArgs {
   // gate = 1: the tied SwiGLU gate.  W has ngroups * N rows (N per column
   // group), Z [M, ngroups N] (row stride ldz, may be null) receives the
   // product and Y the gated U = SiLU(Z) Z; W2 / Y2 / nsplit unused (nsplit = N).
+  // gate = 2: its backward (kind 2): Y = (H W^T) * (SiLU'(Z) Z + SiLU(Z))
+  // with Z the saved product (input, required); the product is rounded to
+  // bf16 once before the scaling.
   int gate; int ngroups; __bf16* Z; int64_t ldz;
 };
 // Backward: dX [M, N] = Norm backward(dY W^T) + R with dY = [X | X2] split at

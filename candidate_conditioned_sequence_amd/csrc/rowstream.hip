@@ -158,7 +158,10 @@ WHALE_DEV f32x4 lds_ldf4(uint32_t a) {
 // normalised next block and this block's staged output.  Four input
 // buffers keep three blocks of transfers in flight (HBM latency at one
 // workgroup per CU needs that much); two output tiles alternate.
-template <int K, int N>
+// EPI: 0 plain stores (Y / Y2 split at nsplit), 1 the tied gate, 2 the tied
+// gate's backward (no norm): the staged product P = dY W_D^T is scaled by
+// SiLU'(u) u + SiLU(u) with u = Z, read two lines ahead of the stores.
+template <int K, int N, int EPI>
 __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int NW = N / 32, NT = NW * 64;
   constexpr int CPR = K / 8;                       // 16-byte chunks per row
@@ -181,7 +184,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   const int grp = (blockIdx.x >> 3) % ng;
   const int G = gridDim.x / ng, b0 = ((blockIdx.x >> 3) / ng) * 8 + (blockIdx.x & 7);
   const int nmine = b0 < nblk ? (int)((nblk - 1 - b0) / G + 1) : 0;
-  const bool nrm = a.kind != 2;
+  const bool nrm = EPI != 2 && a.kind != 2;
 
   const int n0 = 32 * w;
   const bool second = n0 >= a.nsplit;
@@ -192,13 +195,13 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   for (int ks = 0; ks < K / 16; ++ks) wf[ks] = ld8<bf16>(Wr + 16 * ks + 8 * hh);
   for (int k = tid; k < K; k += NT) {
     gb[0][k] = nrm ? a.gamma[k] : 1.f;
-    gb[1][k] = a.kind == 0 ? a.beta[k] : 0.f;
+    gb[1][k] = nrm && a.kind == 0 ? a.beta[k] : 0.f;
   }
   // The weight slice is resident from here on: a wait the compiler sees, so
   // that it places no wait for these loads inside the loop.
   __builtin_amdgcn_s_waitcnt(kVmcnt0);
   auto emit = [&](int64_t m, int n, const bf16x8& v) {
-    if (a.gate) {
+    if (EPI == 1) {
       const int col = grp * N + n;
       if (a.Z) st8<bf16>(a.Z + m * a.ldz + col, v);
       bf16x8 u;
@@ -275,6 +278,18 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
     const int64_t m0 = (int64_t)(b0 + i * G) * kRB;
     // Buffer (i+3) % 4 was last read by block i-1, before the last barrier.
     if (i + NBUF - 1 < nmine) issue(b0 + (i + NBUF - 1) * G, (i + NBUF - 1) % NBUF);
+    // The gate input of the rows this wave stores for block i (see
+    // store_rows), in flight during the MFMAs.
+    constexpr int RC = N / 8, RPI = 64 / RC, NIW = kRB / RPI / NW;
+    bf16x8 zin[EPI == 2 ? NIW : 1];
+    if constexpr (EPI == 2) {
+#pragma unroll
+      for (int t = 0; t < NIW; ++t) {
+        const int r = (w + NW * t) * RPI + lane / RC;
+        const int64_t m = min(m0 + r, M - 1);
+        zin[t] = ld8<bf16>(a.Z + m * a.ldz + grp * N + 8 * (lane % RC));
+      }
+    }
     f32x16 acc = zero16();
     block_mfma<K>(acc, wf, lds_addr(&xs[p][0]), l32, hh);
     // Output tile i & 1 was last read by the stores of block i-2, before
@@ -294,7 +309,25 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       normalise(b0 + (i + 1) * G, (i + 1) % NBUF);
     }
     __syncthreads();
-    store_rows<N, NW>(obp, w, lane, m0, M, emit);
+    if constexpr (EPI == 2) {
+#pragma unroll
+      for (int t = 0; t < NIW; ++t) {
+        const int r = (w + NW * t) * RPI + lane / RC, c = lane % RC;
+        const bf16x8 v = lds_ld8(obp + r * (N * 2) + 16 * (c ^ (r & 7)));
+        const int64_t m = m0 + r;
+        if (m < M) {
+          bf16x8 o;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float u = to_f(zin[t][e]);
+            o[e] = from_f<bf16>(to_f(v[e]) * (dsiluf_(u) * u + siluf_(u)));
+          }
+          st8<bf16>(a.Y + m * a.ldy + grp * N + 8 * c, o);
+        }
+      }
+    } else {
+      store_rows<N, NW>(obp, w, lane, m0, M, emit);
+    }
   }
 }
 
@@ -510,10 +543,16 @@ hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
   const int64_t per = kCUsRS / a.ngroups;
   const int64_t gg = ((nblk < per ? nblk : per) + 7) / 8 * 8;
   const int g = (int)(gg * a.ngroups);
-  if (N == 256)
-    hipLaunchKernelGGL((rs_fwd_kernel<256, 256>), dim3(g), dim3(512), 0, st, a);
+  if (N == 256 && a.gate == 0)
+    hipLaunchKernelGGL((rs_fwd_kernel<256, 256, 0>), dim3(g), dim3(512), 0, st, a);
+  else if (a.gate == 0)
+    hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 0>), dim3(g), dim3(1024), 0, st, a);
+  else if (a.gate == 1 && N == 512)
+    hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 1>), dim3(g), dim3(1024), 0, st, a);
+  else if (a.gate == 2 && N == 512 && a.Z != nullptr)
+    hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 2>), dim3(g), dim3(1024), 0, st, a);
   else
-    hipLaunchKernelGGL((rs_fwd_kernel<256, 512>), dim3(g), dim3(1024), 0, st, a);
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

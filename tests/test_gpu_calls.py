@@ -231,15 +231,17 @@ def test_fusion_mlp_bwd(gpu, dtype, act):
     assert_close("dW_F", dWf, dWf_ref, dtype)
 
 
-@pytest.mark.parametrize("dtype,gate,norm,d", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128),
-                                               ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256),
-                                               ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128),
-                                               ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64),
-                                               ("bf16", O.GATE_SHARED, O.NORM_LAYER, 512)])
-def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d):
-    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm} d={d}", flush=True)
-    M = 300
-    H = 4 * d
+# bf16, shared gate, d = 256: the gate backward runs in the row-streaming
+# kernel (M = 9001: several 32-row blocks per workgroup and a ragged one).
+@pytest.mark.parametrize("dtype,gate,norm,d,M,H", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128, 300, 512),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 300, 1024),
+                                                   ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128, 300, 512),
+                                                   ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64, 300, 256),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 512, 300, 2048),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_RMS, 256, 9001, 1024),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_NONE, 256, 77, 512)])
+def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d, M, H):
+    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm} d={d} M={M} H={H}", flush=True)
     Fm, dY = draw(41, (M, d), dtype), draw(42, (M, d), dtype)
     Wu = weights(43, (2 if gate == O.GATE_SEPARATE else 1) * H, d, dtype)
     Wd = weights(44, d, H, dtype)
