@@ -487,13 +487,13 @@ template <typename T, int PRO>
 hipError_t gemm_epi(const GemmArgs& a, hipStream_t st) {
   switch (a.epi) {
     case EPI_STORE: return gemm_go<T, PRO, EPI_STORE, 128, sizeof(T) == 2 ? 256 : 128, 64>(a, st);
-    case EPI_RESID: return gemm_go<T, PRO, EPI_RESID, 128, 128, 64>(a, st);
-    case EPI_SILU_RESID: return gemm_go<T, PRO, EPI_SILU_RESID, 128, 128, 64>(a, st);
+    case EPI_RESID: return gemm_go<T, PRO, EPI_RESID, 128, sizeof(T) == 2 ? 256 : 128, 64>(a, st);
+    case EPI_SILU_RESID: return gemm_go<T, PRO, EPI_SILU_RESID, 128, sizeof(T) == 2 ? 256 : 128, 64>(a, st);
     case EPI_GATE_TIED: return gemm_go<T, PRO, EPI_GATE_TIED, 128, 128, 64>(a, st);
     case EPI_GATE_SEP: return gemm_go<T, PRO, EPI_GATE_SEP, 128, 128, 64>(a, st);
     case EPI_DGATE_TIED: return gemm_go<T, PRO, EPI_DGATE_TIED, 128, 128, 32>(a, st);
     case EPI_DGATE_SEP: return gemm_go<T, PRO, EPI_DGATE_SEP, 128, 128, 32>(a, st);
-    case EPI_DUAL_RESID2: return gemm_go<T, PRO, EPI_DUAL_RESID2, 128, 128, 32>(a, st);
+    case EPI_DUAL_RESID2: return gemm_go<T, PRO, EPI_DUAL_RESID2, 128, sizeof(T) == 2 ? 256 : 128, 32>(a, st);
     case EPI_NORM_BWD:
       // Row-complete tiles (BN == N); the K step shrinks with the tile so
       // that the double-buffered tiles fit in LDS.
