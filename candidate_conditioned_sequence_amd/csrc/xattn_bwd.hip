@@ -4,9 +4,10 @@
 // Q-parallel and KV-parallel schedules chosen by shape (paper-daily.com deep
 // reading §2; gist.science Technical Summary §2.2, "Asymmetric Backward
 // Variants"; pith.science verdict record, referee_report.summary).  Here:
-//  * D[m, j] = <dA[m, j], A[m, j]> (one pass over dA and A),
 //  * a Q-parallel kernel: each workgroup owns a block of queries of one
-//    (request, head) and walks the request's history, recomputing
+//    (request, head); it first forms D[m, j] = <dA[m, j], A[m, j]> for its
+//    queries (from the dA rows it holds anyway) and writes it for the
+//    KV-parallel kernel, then walks the request's history, recomputing
 //    P = exp2(s*c - lse2), dP = dA V^T, dS = P (dP - D), and accumulates
 //    dQ^T += K^T dS^T in registers: no reduction at all;
 //  * a KV-parallel kernel: each workgroup owns 128 history rows of one
@@ -28,26 +29,6 @@
 namespace {
 
 constexpr int kNW = 4;
-
-// ----------------------------------------------------------------- D
-template <typename T, int DH>
-__global__ __launch_bounds__(256) void bwd_dot_kernel(const T* __restrict__ A, const T* __restrict__ dA,
-                                                      float* __restrict__ D, int64_t Mh, int d, int h) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= Mh) return;
-  const int64_t m = i / h;
-  const int j = (int)(i % h);
-  const T* a = A + m * d + j * DH;
-  const T* g = dA + m * d + j * DH;
-  float s = 0.f;
-#pragma unroll
-  for (int e = 0; e < DH; e += 8) {
-    const x8_t<T> av = ld8<T>(a + e), gv = ld8<T>(g + e);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) s = fmaf(to_f(av[u]), to_f(gv[u]), s);
-  }
-  D[i] = s;
-}
 
 // Probabilities and dS of one 32x32 score block, packed pairwise into two
 // B operands (bf16: v_cvt_pk; the pair order is the accumulator row order).
@@ -88,9 +69,9 @@ WHALE_DEV void p_ds_pack(const f32x16& s, const f32x16& dp, x8_t<T> (&pf)[2], x8
 template <typename T, int DH, int NWQ>
 __global__ __launch_bounds__(NWQ * 64, 2) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int64_t* __restrict__ offsets, const T* __restrict__ dA, const float* __restrict__ lse,
-    const float* __restrict__ Dbuf, T* __restrict__ dQ, int d, int h, int QR, int nqb, float c, float scale,
-    int nblocks) {
+    const int64_t* __restrict__ offsets, const T* __restrict__ dA, const T* __restrict__ A,
+    const float* __restrict__ lse, float* __restrict__ Dbuf, T* __restrict__ dQ, int d, int h, int QR, int nqb,
+    float c, float scale, int nblocks) {
   constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = NWQ * 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (NWQ * 64);
   static_assert(NCH >= 1 && BN * CPR % (NWQ * 64) == 0, "tile/threads mismatch");
@@ -110,12 +91,22 @@ __global__ __launch_bounds__(NWQ * 64, 2) void bwd_dq_kernel(
   const bool qok = q < QR;
 
   x8_t<T> qf[KS], gf[KS];
+  // D = <dA, A> of this lane's query: each lane holds half of the row (the
+  // chunks of hh), the two halves meet across l and l ^ 32.
+  float dpart = 0.f;
   {
     const int64_t off = (qrow0 + q) * d + j * DH + 8 * hh;
+    x8_t<T> af[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = qok ? ld8<T>(Q + off + 16 * ks) : zero8<T>();
       gf[ks] = qok ? ld8<T>(dA + off + 16 * ks) : zero8<T>();
+      af[ks] = qok ? ld8<T>(A + off + 16 * ks) : zero8<T>();
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dpart = fmaf(to_f(af[ks][u]), to_f(gf[ks][u]), dpart);
       if (kFold) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) qf[ks][u] = from_f<T>(to_f(qf[ks][u]) * c);
@@ -123,7 +114,8 @@ __global__ __launch_bounds__(NWQ * 64, 2) void bwd_dq_kernel(
     }
   }
   const float lse2 = qok ? lse[(qrow0 + q) * h + j] * kLog2e : INFINITY;
-  const float Dq = qok ? Dbuf[(qrow0 + q) * h + j] : 0.f;
+  const float Dq = half_sum(dpart);
+  if (qok && hh == 0) Dbuf[(qrow0 + q) * h + j] = Dq;
 
   f32x16 acc[NE];
 #pragma unroll
@@ -441,14 +433,11 @@ __global__ __launch_bounds__(256) void kv_split_reduce_kernel(const float* __res
 
 template <typename T, int DH>
 hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
-  const int64_t M = (int64_t)a.B * a.QR;
-  const int64_t Mh = M * a.h;
   const float c = a.scale * kLog2e;
-  hipLaunchKernelGGL((bwd_dot_kernel<T, DH>), dim3((unsigned)((Mh + 255) / 256)), dim3(256), 0, st, (const T*)a.A,
-                     (const T*)a.dA, a.Dbuf, Mh, a.d, a.h);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  hipError_t e;
   {
+    // The dQ kernel also forms D = <dA, A> and writes it to Dbuf, which the
+    // dK/dV kernel reads after it (same stream).
     // Eight waves (256 queries) per workgroup where the request has enough
     // queries: one K/V tile load then serves twice the queries of a CU.
     auto go = [&](auto nwq) {
@@ -456,8 +445,8 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
       const int nqb = (a.QR + NWQ * 32 - 1) / (NWQ * 32);
       const int64_t nblk = (int64_t)a.B * a.h * nqb;
       hipLaunchKernelGGL((bwd_dq_kernel<T, DH, NWQ>), dim3((unsigned)nblk), dim3(NWQ * 64), 0, st, (const T*)a.Q,
-                         (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf, (T*)a.dQ, a.d, a.h,
-                         a.QR, nqb, c, a.scale, (int)nblk);
+                         (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, (const T*)a.A, a.lse, a.Dbuf,
+                         (T*)a.dQ, a.d, a.h, a.QR, nqb, c, a.scale, (int)nblk);
     };
     bool done = false;
     if constexpr (DH == 64) {
