@@ -52,14 +52,14 @@ _SIGS = {
     "whale_jagged_xattn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_fusion_mlp": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P]),
     "whale_swiglu_ffn_workspace_size": (_S, [_D, _I, _I, ctypes.c_int32]),
-    "whale_swiglu_ffn": (_I, [_D, _I, _P, _I, _F, _P, _P, _P, _I, ctypes.c_int32, _P, _P, _P, _P, _P, _S, _P]),
+    "whale_swiglu_ffn": (_I, [_D, _I, _P, _I, _F, _P, _P, _P, _I, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _S, _P]),
     "whale_jagged_xattn_bwd_workspace_size": (_S, [_D, _I]),
     "whale_jagged_xattn_bwd": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
     "whale_fusion_mlp_bwd_workspace_size": (_S, [_D, _I]),
     "whale_fusion_mlp_bwd": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P, _P, _P, _P, _S, _P]),
     "whale_swiglu_ffn_bwd_workspace_size": (_S, [_D, _I, _I, ctypes.c_int32]),
     "whale_swiglu_ffn_bwd": (_I, [_D, _I, _P, _I, _F, _P, _P, _P, _P, _I, ctypes.c_int32, _P, _P, _P, _P, _P, _P,
-                                  _P, _P, _P, _S, _P]),
+                                  _P, _P, _P, _P, _S, _P]),
     "whale_proj_qkv_bwd_workspace_size": (_S, [_D, _I]),
     "whale_proj_qkv_bwd": (_I, [_D, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                 _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _S, _P]),
@@ -152,10 +152,11 @@ def whale_swiglu_ffn_workspace_size(d_, dtype_code, gate, H):
     return load().whale_swiglu_ffn_workspace_size(ctypes.byref(d_), dtype_code, gate, H)
 
 
-def whale_swiglu_ffn(d_, F, norm, eps, g_f, b_f, W_U, gate, H, W_D, Y, U_saved, stats_f, workspace, stream=None):
+def whale_swiglu_ffn(d_, F, norm, eps, g_f, b_f, W_U, gate, H, W_D, Y, U_saved, stats_f, workspace, stream=None,
+                     X_f=None):
     ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load().whale_swiglu_ffn(ctypes.byref(d_), _dtype_code(F), _ptr(F), norm, eps, _ptr(g_f), _ptr(b_f),
-                                 _ptr(W_U), gate, H, _ptr(W_D), _ptr(Y), _ptr(U_saved), _ptr(stats_f),
+                                 _ptr(W_U), gate, H, _ptr(W_D), _ptr(Y), _ptr(U_saved), _ptr(stats_f), _ptr(X_f),
                                  _ptr(workspace), ws, _stream(stream))
     _check("whale_swiglu_ffn", rc)
 
@@ -189,10 +190,11 @@ def whale_swiglu_ffn_bwd_workspace_size(d_, dtype_code, gate, H):
 
 
 def whale_swiglu_ffn_bwd(d_, F, norm, eps, g_f, b_f, stats_f, W_U, gate, H, W_D, U_saved, dY, dF, dW_U, dW_D, dg_f,
-                         db_f, workspace, stream=None):
+                         db_f, workspace, stream=None, X_f=None):
     ws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = load().whale_swiglu_ffn_bwd(ctypes.byref(d_), _dtype_code(F), _ptr(F), norm, eps, _ptr(g_f), _ptr(b_f),
-                                     _ptr(stats_f), _ptr(W_U), gate, H, _ptr(W_D), _ptr(U_saved), _ptr(dY), _ptr(dF),
+                                     _ptr(stats_f), _ptr(W_U), gate, H, _ptr(W_D), _ptr(U_saved), _ptr(X_f), _ptr(dY),
+                                     _ptr(dF),
                                      _ptr(dW_U), _ptr(dW_D), _ptr(dg_f), _ptr(db_f), _ptr(workspace), ws,
                                      _stream(stream))
     _check("whale_swiglu_ffn_bwd", rc)

@@ -249,8 +249,8 @@ size_t whale_swiglu_ffn_workspace_size(const whale_dims_t* dims, whale_dtype_t d
 
 whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, const void* F, whale_norm_t norm,
                                 float eps, const float* g_f, const float* b_f, const void* W_U, whale_gate_t gate,
-                                int32_t H, const void* W_D, void* Y, void* U_saved, float* stats_f, void* workspace,
-                                size_t ws_bytes, hipStream_t stream) {
+                                int32_t H, const void* W_D, void* Y, void* U_saved, float* stats_f, void* X_f,
+                                void* workspace, size_t ws_bytes, hipStream_t stream) {
   Shape s;
   whale_status_t rc = check_dims(dims, dtype, &s);
   if (rc != WHALE_OK) return rc;
@@ -276,7 +276,7 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
     // for the backward), F W_U^T and the tied gate in one pass over F.
     RsFwdArgs u;
     u.H = (const __bf16*)F; u.ldh = s.d; u.W = (const __bf16*)W_U; u.W2 = (const __bf16*)W_U; u.nsplit = kGroup;
-    u.Y = (__bf16*)G; u.Y2 = (__bf16*)G; u.ldy = H; u.Xn = nullptr;
+    u.Y = (__bf16*)G; u.Y2 = (__bf16*)G; u.ldy = H; u.Xn = norm != WHALE_NORM_NONE ? (__bf16*)X_f : nullptr;
     u.stats = norm != WHALE_NORM_NONE ? stats_f : nullptr; u.gamma = g_f; u.beta = b_f;
     u.M = s.M; u.kind = (int)norm; u.eps = eps;
     u.gate = 1; u.ngroups = H / kGroup; u.Z = (__bf16*)U_saved; u.ldz = H;
@@ -287,8 +287,9 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   // up projection does not renormalise F for every block of its H columns.
   const void* Xin = F;
   if (norm != WHALE_NORM_NONE) {
-    WHALE_TRY(launch_norm_apply(F, nullptr, stats_f, g_f, b_f, Xf, s.M, s.d, (int)norm, eps, bf, stream));
-    Xin = Xf;
+    void* dst = X_f ? X_f : Xf;
+    WHALE_TRY(launch_norm_apply(F, nullptr, stats_f, g_f, b_f, dst, s.M, s.d, (int)norm, eps, bf, stream));
+    Xin = dst;
   }
   GemmArgs a = gemm_defaults();
   a.X = Xin; a.ldx = s.d;
@@ -402,7 +403,8 @@ size_t whale_swiglu_ffn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype
 whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* F, whale_norm_t norm,
                                     float eps, const float* g_f, const float* b_f, const float* stats_f,
                                     const void* W_U, whale_gate_t gate, int32_t H, const void* W_D,
-                                    const void* U_saved, const void* dY, void* dF, float* dW_U, float* dW_D,
+                                    const void* U_saved, const void* X_f, const void* dY, void* dF, float* dW_U,
+                                    float* dW_D,
                                     float* dg_f, float* db_f, void* workspace, size_t ws_bytes, hipStream_t stream) {
   Shape s;
   whale_status_t rc = check_dims(dims, dtype, &s);
@@ -449,8 +451,12 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   // dW_U = dU^T X_f, X_f = Norm_f(F) formed once from the saved statistics
   const void* Xin = F;
   if (norm != WHALE_NORM_NONE) {
-    WHALE_TRY(launch_norm_apply(F, stats_f, nullptr, g_f, b_f, Xf, s.M, d, nk, eps, bf, stream));
-    Xin = Xf;
+    if (X_f) {
+      Xin = X_f;
+    } else {
+      WHALE_TRY(launch_norm_apply(F, stats_f, nullptr, g_f, b_f, Xf, s.M, d, nk, eps, bf, stream));
+      Xin = Xf;
+    }
   }
   Wg w2(dU, Hu, Xin, d, WPRO_PLAIN, s.M, Hu, d, dW_U, part);
   WHALE_TRY(w2.run(bf, stream));

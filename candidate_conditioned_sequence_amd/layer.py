@@ -63,10 +63,11 @@ class FusionLayer:
             Y = _empty((M, d), dt, dev)
             U = _empty((M, Hu), dt, dev) if save else None
             sf = _empty((M, 2), torch.float32, dev) if nn else None
+            Xf = _empty((M, d), dt, dev) if (save and nn) else None
             ws = _ws(wb.whale_swiglu_ffn_workspace_size(dm, wb._dtype_code(F), self.gate, H), dev)
             wb.whale_swiglu_ffn(dm, F, self.norm, self.eps, p["g_f"], p["b_f"], p["W_U"], self.gate, H, p["W_D"], Y, U,
-                                sf, ws, stream)
-            out.update(Y=Y, U=U, stats_f=sf)
+                                sf, ws, stream, X_f=Xf)
+            out.update(Y=Y, U=U, stats_f=sf, X_f=Xf)
         else:
             out["Y"] = F
         if save:
@@ -90,7 +91,7 @@ class FusionLayer:
             ws = _ws(wb.whale_swiglu_ffn_bwd_workspace_size(dm, code, self.gate, self.H), dev)
             wb.whale_swiglu_ffn_bwd(dm, c["F"], self.norm, self.eps, p["g_f"], p["b_f"], c["stats_f"], p["W_U"],
                                     self.gate, self.H, p["W_D"], c["U"], dY, dF, g["dW_U"], g["dW_D"], g["dg_f"],
-                                    g["db_f"], ws, stream)
+                                    g["db_f"], ws, stream, X_f=c.get("X_f"))
         else:
             dF = dY
         dA, dHw_mlp = _empty((M, d), dt, dev), _empty((M, d), dt, dev)

@@ -162,6 +162,9 @@ whale_status_t whale_fusion_mlp(const whale_dims_t* dims, whale_dtype_t dtype,
  * stacked [W_G; W_U], 2H rows).  U_saved ([M, H] or [M, 2H], columns
  * [U_g | U_u] for the separate gate) is written when non-NULL; stats_f
  * ([M, 2]) is required unless norm is none.  The backward needs both.
+ * X_f ([M, d], data type, may be NULL; unused for norm none) receives
+ * Norm_f(F); passing it on to whale_swiglu_ffn_bwd saves the backward from
+ * forming it again.
  * workspace: at least whale_swiglu_ffn_workspace_size(...) bytes of device
  * memory (holds G).  Requires H % 64 == 0.
  */
@@ -171,7 +174,7 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype,
                                 const void* F, whale_norm_t norm, float eps,
                                 const float* g_f, const float* b_f,
                                 const void* W_U, whale_gate_t gate, int32_t H, const void* W_D,
-                                void* Y, void* U_saved, float* stats_f,
+                                void* Y, void* U_saved, float* stats_f, void* X_f,
                                 void* workspace, size_t ws_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------- backward */
@@ -215,8 +218,9 @@ whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
  * dF = dY + Norm_f backward(dX_f); dg_f/db_f are the norm parameter
  * gradients (db_f is zero for RMSNorm; neither is written, and both may be
  * NULL, for norm none).  U_saved and stats_f come from the forward (stats_f
- * may be NULL only for norm none).  Weight and norm parameter gradients are
- * fp32.
+ * may be NULL only for norm none).  X_f: the forward's Norm_f(F) if it wrote
+ * it, else NULL (it is then formed again in the workspace).  Weight and norm
+ * parameter gradients are fp32.
  */
 size_t whale_swiglu_ffn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype,
                                            whale_gate_t gate, int32_t H);
@@ -224,7 +228,7 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
                                     const void* F, whale_norm_t norm, float eps,
                                     const float* g_f, const float* b_f, const float* stats_f,
                                     const void* W_U, whale_gate_t gate, int32_t H, const void* W_D,
-                                    const void* U_saved, const void* dY,
+                                    const void* U_saved, const void* X_f, const void* dY,
                                     void* dF, float* dW_U, float* dW_D, float* dg_f, float* db_f,
                                     void* workspace, size_t ws_bytes, hipStream_t stream);
 

@@ -233,15 +233,15 @@ def test_fusion_mlp_bwd(gpu, dtype, act):
 
 # bf16, shared gate, d = 256: the gate backward runs in the row-streaming
 # kernel (M = 9001: several 32-row blocks per workgroup and a ragged one).
-@pytest.mark.parametrize("dtype,gate,norm,d,M,H", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128, 300, 512),
-                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 300, 1024),
-                                                   ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128, 300, 512),
-                                                   ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64, 300, 256),
-                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 512, 300, 2048),
-                                                   ("bf16", O.GATE_SHARED, O.NORM_RMS, 256, 9001, 1024),
-                                                   ("bf16", O.GATE_SHARED, O.NORM_NONE, 256, 77, 512)])
-def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d, M, H):
-    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm} d={d} M={M} H={H}", flush=True)
+# keep: the forward writes X_f = Norm_f(F) and the backward reads it.
+@pytest.mark.parametrize("dtype,gate,norm,d,M,H,keep", [
+    ("f32", O.GATE_SHARED, O.NORM_LAYER, 128, 300, 512, False), ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 300, 1024, False),
+    ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128, 300, 512, True), ("f32", O.GATE_SEPARATE, O.NORM_NONE, 64, 300, 256, False),
+    ("bf16", O.GATE_SHARED, O.NORM_LAYER, 512, 300, 2048, False), ("bf16", O.GATE_SHARED, O.NORM_RMS, 256, 9001, 1024, True),
+    ("bf16", O.GATE_SHARED, O.NORM_NONE, 256, 77, 512, True), ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 300, 1024, True),
+    ("f32", O.GATE_SHARED, O.NORM_LAYER, 128, 300, 512, True)])
+def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d, M, H, keep):
+    print(f"\n[swiglu_ffn_bwd] {dtype} gate={gate} norm={norm} d={d} M={M} H={H} keep={keep}", flush=True)
     Fm, dY = draw(41, (M, d), dtype), draw(42, (M, d), dtype)
     Wu = weights(43, (2 if gate == O.GATE_SEPARATE else 1) * H, d, dtype)
     Wd = weights(44, d, H, dtype)
@@ -254,13 +254,16 @@ def test_swiglu_ffn_bwd(gpu, dtype, gate, norm, d, M, H):
     sf = torch.empty((M, 2), device=gpu)
     code = wb._dtype_code(tF)
     ws = torch.empty(wb.whale_swiglu_ffn_workspace_size(dm, code, gate, H), dtype=torch.uint8, device=gpu)
-    wb.whale_swiglu_ffn(dm, tF, norm, 1e-5, tg, tb, tWu, gate, H, tWd, Y, U, sf, ws)
+    Xf = torch.empty_like(tF) if keep else None
+    wb.whale_swiglu_ffn(dm, tF, norm, 1e-5, tg, tb, tWu, gate, H, tWd, Y, U, sf, ws, X_f=Xf)
+    if keep and norm != O.NORM_NONE:
+        assert_close("X_f", Xf, O.norm_fwd(Fm, norm, g, bt, 1e-5)[0], dtype)
     dF = torch.empty_like(tF)
     dWu, dWd = torch.empty(tuple(Wu.shape), device=gpu), torch.empty(tuple(Wd.shape), device=gpu)
     dg, db = torch.empty(d, device=gpu), torch.empty(d, device=gpu)
     ws = torch.empty(wb.whale_swiglu_ffn_bwd_workspace_size(dm, code, gate, H), dtype=torch.uint8, device=gpu)
     wb.whale_swiglu_ffn_bwd(dm, tF, norm, 1e-5, tg, tb, sf, tWu, gate, H, tWd, U, to_dev(dY, dtype, gpu), dF, dWu,
-                            dWd, dg, db, ws)
+                            dWd, dg, db, ws, X_f=Xf)
     torch.cuda.synchronize()
     assert_close("dF", dF, ref["dF"], dtype)
     assert_close("dW_U", dWu, ref["dW_U"], dtype)

@@ -58,9 +58,9 @@ def test_host_validation_rejects_before_launch():
         assert lib.whale_jagged_xattn_fwd(ctypes.byref(bad), 1, fake, fake, fake, fake, 0.0, fake, None, None) == 4
     # FFN hidden width not a multiple of 64, workspace too small
     assert lib.whale_swiglu_ffn(ctypes.byref(d), 1, fake, 0, 1e-5, fake, fake, fake, 0, 100, fake, fake, None, fake,
-                                fake, 1 << 30, None) == 4
+                                None, fake, 1 << 30, None) == 4
     assert lib.whale_swiglu_ffn(ctypes.byref(d), 1, fake, 0, 1e-5, fake, fake, fake, 0, 512, fake, fake, None, fake,
-                                fake, 16, None) == 5
+                                None, fake, 16, None) == 5
     # LayerNorm without its statistics buffer
     assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 0, 1e-5, fake, fake, fake, fake, fake, fake, fake, fake,
                               fake, fake, None, fake, None, None, None) == 1
