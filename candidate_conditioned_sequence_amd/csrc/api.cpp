@@ -364,6 +364,21 @@ whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   void* WFt = c.take((size_t)2 * d * d * esz(dtype));
   float* part = (float*)c.take(wgrad_partial_bytes(s.M, d, 2 * d));
   void* dZw = c.take((size_t)s.M * d * esz(dtype));
+  if (bf && silu && rs_fwd_ok(d, 2 * d)) {
+    // Row-streaming kernel: dZ = dF * SiLU'(Z) (written for the weight
+    // gradient) and [dA | dH_w - dF] = dZ W_F with the residual, in one pass.
+    WHALE_TRY(launch_transpose(W_F, d, 2 * d, WFt, d, 0, bf, stream));
+    RsFwdArgs r;
+    r.H = (const __bf16*)dF; r.ldh = d; r.W = (const __bf16*)WFt; r.W2 = (const __bf16*)WFt + (size_t)d * d;
+    r.nsplit = d; r.Y = (__bf16*)dA; r.Y2 = (__bf16*)dH_w; r.ldy = d;
+    r.Xn = (__bf16*)dZw; r.stats = nullptr; r.gamma = nullptr; r.beta = nullptr;
+    r.M = s.M; r.kind = 2; r.eps = 0.f;
+    r.gate = 3; r.ngroups = 1; r.Z = (__bf16*)Z_saved; r.ldz = d;
+    WHALE_TRY(launch_rs_fwd(r, d, 2 * d, stream));
+    Wg w(dZw, d, A, d, WPRO_CONCAT, s.M, d, 2 * d, dW_F, part);
+    w.concat(H_w, d, d);
+    return ret(w.run(bf, stream));
+  }
   // dZ = dF * act'(Z) once; both products below read it.
   const void* dZ = dF;
   if (silu) {

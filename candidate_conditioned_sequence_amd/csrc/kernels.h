@@ -103,6 +103,9 @@ struct RsFwdArgs {
   // gate = 2: its backward (kind 2): Y = (H W^T) * (SiLU'(Z) Z + SiLU(Z))
   // with Z the saved product (input, required); the product is rounded to
   // bf16 once before the scaling.
+  // gate = 3: the fusion MLP's backward (kind 2, ngroups 1): H = dF, Z the
+  // saved pre-activation (input, row stride ldz); Xn receives dZ = dF SiLU'(Z)
+  // (required), Y = dZ W^T for rows < nsplit of W, Y2 = dF + dZ W2^T.
   int gate; int ngroups; __bf16* Z; int64_t ldz;
 };
 // Backward: dX [M, N] = Norm backward(dY W^T) + R with dY = [X | X2] split at

@@ -160,7 +160,11 @@ WHALE_DEV f32x4 lds_ldf4(uint32_t a) {
 // workgroup per CU needs that much); two output tiles alternate.
 // EPI: 0 plain stores (Y / Y2 split at nsplit), 1 the tied gate, 2 the tied
 // gate's backward (no norm): the staged product P = dY W_D^T is scaled by
-// SiLU'(u) u + SiLU(u) with u = Z, read two lines ahead of the stores.
+// SiLU'(u) u + SiLU(u) with u = Z, read two lines ahead of the stores;
+// 3 the fusion MLP's backward (no norm): the rows H = dF and Z arrive
+// together, each wave forms dZ = dF SiLU'(Z) for its rows (in LDS and to
+// Xn), the MFMAs read dZ, and columns >= nsplit add the residual dF.  The
+// second input stream leaves room for two buffers only.
 template <int K, int N, int EPI>
 __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int NW = N / 32, NT = NW * 64;
@@ -168,9 +172,10 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int BLK = kRB * K * 2;                 // bytes per block
   constexpr int NI = BLK / 1024;                   // transfer instructions per block
   constexpr int IPW = NI / NW;                     // ... per wave
-  constexpr int NBUF = 4;
+  constexpr int NBUF = EPI == 3 ? 2 : 4;
   static_assert(NI % NW == 0 && IPW >= 1 && K == 256, "one panel, whole instructions per wave");
   __shared__ __attribute__((aligned(1024))) char xs[NBUF][BLK];
+  __shared__ __attribute__((aligned(1024))) char zb[EPI == 3 ? NBUF : 1][EPI == 3 ? BLK : 16];
   __shared__ __attribute__((aligned(1024))) char ob[2][kRB * N * 2];
   __shared__ __attribute__((aligned(16))) float gb[2][K];
 
@@ -221,6 +226,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
     for (int t = 0; t < IPW; ++t) {
       const int j = w + NW * t;
       dma_rows(a.H, a.ldh, m0, 2 * j, M, lane, lds_addr(&xs[p][1024 * j]));
+      if constexpr (EPI == 3) dma_rows(a.Z, a.ldz, m0, 2 * j, M, lane, lds_addr(&zb[p][1024 * j]));
     }
   };
   // Normalise this wave's rows of block b in buffer p (after its transfers
@@ -228,6 +234,25 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   // kernels), the normalised row written back in place, to Xn and the
   // statistics to stats.
   auto normalise = [&](int b, int p) {
+    if constexpr (EPI == 3) {
+      // dZ = dF SiLU'(Z) over this wave's rows, into the Z buffer and to Xn.
+      const int64_t m0 = (int64_t)b * kRB;
+#pragma unroll
+      for (int t = 0; t < IPW; ++t) {
+        const int j = w + NW * t;
+        const int q = 64 * j + lane, r = q / CPR, c = swz(q % CPR, r);
+        const bf16x8 df = lds_ld8(lds_addr(&xs[p][16 * q]));
+        const uint32_t za = lds_addr(&zb[p][16 * q]);
+        const bf16x8 z = lds_ld8(za);
+        bf16x8 dz;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dz[u] = from_f<bf16>(to_f(df[u]) * dsiluf_(to_f(z[u])));
+        *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)za = dz;
+        const int64_t m = m0 + r;
+        if (m < M) st8<bf16>(a.Xn + m * K + 8 * c, dz);
+      }
+      return;
+    }
     if (!nrm) return;
     const int64_t m0 = (int64_t)b * kRB;
 #pragma unroll
@@ -291,15 +316,23 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       }
     }
     f32x16 acc = zero16();
-    block_mfma<K>(acc, wf, lds_addr(&xs[p][0]), l32, hh);
+    block_mfma<K>(acc, wf, lds_addr(EPI == 3 ? &zb[p][0] : &xs[p][0]), l32, hh);
     // Output tile i & 1 was last read by the stores of block i-2, before
     // the last barrier.
     const uint32_t obp = lds_addr(&ob[i & 1][0]);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 o;
+      if (EPI == 3 && second) {
+        // residual dF of row l32, columns n0 - nsplit + 8 g + 4 hh + u
+        const int c = ((n0 - a.nsplit) >> 3) + g;
+        const bf16x4 rv = lds_ld4(lds_addr(&xs[p][0]) + 512 * l32 + 16 * (c ^ (l32 & 7)) + 8 * hh);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) o[u] = from_f<bf16>(acc[4 * g + u]);
+        for (int u = 0; u < 4; ++u) o[u] = from_f<bf16>(acc[4 * g + u] + to_f(rv[u]));
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) o[u] = from_f<bf16>(acc[4 * g + u]);
+      }
       stage_piece<N>(obp, l32, hh, n0, g, o);
     }
     // This wave's transfers of block i+1 have landed once at most the newer
@@ -551,6 +584,8 @@ hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 1>), dim3(g), dim3(1024), 0, st, a);
   else if (a.gate == 2 && N == 512 && a.Z != nullptr)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 2>), dim3(g), dim3(1024), 0, st, a);
+  else if (a.gate == 3 && N == 512 && a.Z != nullptr && a.Xn != nullptr && a.ngroups == 1)
+    hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 3>), dim3(g), dim3(1024), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

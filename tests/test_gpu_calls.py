@@ -208,15 +208,18 @@ def test_xattn_bwd(gpu, case):
     assert_close("dV", dV, dV_ref, dtype)
 
 
-@pytest.mark.parametrize("dtype,act", [("f32", O.ACT_SILU), ("bf16", O.ACT_SILU), ("bf16", O.ACT_NONE)])
-def test_fusion_mlp_bwd(gpu, dtype, act):
-    print(f"\n[fusion_mlp_bwd] {dtype} act={act}", flush=True)
-    M, d = 300, 128
+# bf16 with SiLU at d = 256: the row-streaming kernel (dZ, dA and dH_w in one
+# pass; M = 9001 gives several 32-row blocks per workgroup and a ragged one).
+@pytest.mark.parametrize("dtype,act,M,d", [("f32", O.ACT_SILU, 300, 128), ("bf16", O.ACT_SILU, 300, 128),
+                                           ("bf16", O.ACT_NONE, 300, 128), ("bf16", O.ACT_SILU, 9001, 256),
+                                           ("bf16", O.ACT_SILU, 77, 256), ("bf16", O.ACT_NONE, 300, 256)])
+def test_fusion_mlp_bwd(gpu, dtype, act, M, d):
+    print(f"\n[fusion_mlp_bwd] {dtype} act={act} M={M} d={d}", flush=True)
     A, Hw, dF = draw(31, (M, d), dtype), draw(32, (M, d), dtype), draw(33, (M, d), dtype)
     Wf = weights(34, d, 2 * d, dtype)
     dA_ref, dHw_ref, dWf_ref = O.fusion_mlp_bwd(A, Hw, Wf, act, dF)
     _, Z = O.fusion_mlp(A, Hw, Wf, act)
-    dm = wb.dims(1, M, 1, d, 2, 0, 0)
+    dm = wb.dims(1, M, 1, d, d // 64, 0, 0)
     tA, tHw, tWf = to_dev(A, dtype, gpu), to_dev(Hw, dtype, gpu), to_dev(Wf, dtype, gpu)
     F, tZ = torch.empty_like(tA), torch.empty_like(tA)
     wb.whale_fusion_mlp(dm, tA, tHw, tWf, act, F, tZ if act == O.ACT_SILU else None)
