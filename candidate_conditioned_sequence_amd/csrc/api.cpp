@@ -162,7 +162,7 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
   if (bf && rs_fwd_ok(s.d, s.d) && rs_fwd_ok(s.d, 2 * s.d)) {
     // Row-streaming kernels: the norm (statistics, X_q / X_s) and the
     // projection in one pass over the rows; K and V together.
-    RsFwdArgs q;
+    RsFwdArgs q{};
     q.H = (const __bf16*)H_w; q.ldh = s.d; q.W = (const __bf16*)W_Q; q.W2 = (const __bf16*)W_Q; q.nsplit = s.d;
     q.Y = (__bf16*)Q; q.Y2 = (__bf16*)Q; q.ldy = s.d;
     q.Xn = nrm ? (__bf16*)X_q : nullptr; q.stats = nrm ? stats_q : nullptr;
@@ -227,6 +227,16 @@ whale_status_t whale_fusion_mlp(const whale_dims_t* dims, whale_dtype_t dtype, c
   if (rc != WHALE_OK) return rc;
   if (act != WHALE_ACT_SILU && act != WHALE_ACT_NONE) return WHALE_ERR_SHAPE;
   if (!A || !H_w || !W_F || !F) return WHALE_ERR_NULL;
+  if (dtype == WHALE_BF16 && act == WHALE_ACT_SILU && rs_fwd_ok(2 * s.d, s.d)) {
+    // Row-streaming kernel: [A | H_w] W_F^T, SiLU and the residual H_w (read
+    // from the staged rows) in one pass.
+    RsFwdArgs r{};
+    r.H = (const __bf16*)A; r.ldh = s.d; r.H2 = (const __bf16*)H_w; r.ldh2 = s.d;
+    r.W = (const __bf16*)W_F; r.W2 = (const __bf16*)W_F; r.nsplit = s.d;
+    r.Y = (__bf16*)F; r.Y2 = (__bf16*)F; r.ldy = s.d; r.M = s.M; r.kind = 2;
+    r.gate = 4; r.ngroups = 1; r.Z = (__bf16*)Z_saved; r.ldz = s.d;
+    return ret(launch_rs_fwd(r, 2 * s.d, s.d, stream));
+  }
   GemmArgs a = gemm_defaults();
   a.X = A; a.ldx = s.d; a.X2 = H_w; a.ldx2 = s.d; a.ksplit = s.d;
   a.W = W_F; a.ldw = 2 * s.d; a.Y = F; a.ldy = s.d; a.R = H_w; a.ldr = s.d; a.Z = Z_saved; a.ldz = s.d;
@@ -274,7 +284,7 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   if (bf && gate == WHALE_GATE_SHARED && rs_fwd_ok(s.d, kGroup) && H % kGroup == 0 && 256 % (8 * (H / kGroup)) == 0) {
     // Up projection by the row-streaming kernel: Norm_f (statistics saved
     // for the backward), F W_U^T and the tied gate in one pass over F.
-    RsFwdArgs u;
+    RsFwdArgs u{};
     u.H = (const __bf16*)F; u.ldh = s.d; u.W = (const __bf16*)W_U; u.W2 = (const __bf16*)W_U; u.nsplit = kGroup;
     u.Y = (__bf16*)G; u.Y2 = (__bf16*)G; u.ldy = H; u.Xn = norm != WHALE_NORM_NONE ? (__bf16*)X_f : nullptr;
     u.stats = norm != WHALE_NORM_NONE ? stats_f : nullptr; u.gamma = g_f; u.beta = b_f;
@@ -368,7 +378,7 @@ whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
     // Row-streaming kernel: dZ = dF * SiLU'(Z) (written for the weight
     // gradient) and [dA | dH_w - dF] = dZ W_F with the residual, in one pass.
     WHALE_TRY(launch_transpose(W_F, d, 2 * d, WFt, d, 0, bf, stream));
-    RsFwdArgs r;
+    RsFwdArgs r{};
     r.H = (const __bf16*)dF; r.ldh = d; r.W = (const __bf16*)WFt; r.W2 = (const __bf16*)WFt + (size_t)d * d;
     r.nsplit = d; r.Y = (__bf16*)dA; r.Y2 = (__bf16*)dH_w; r.ldy = d;
     r.Xn = (__bf16*)dZw; r.stats = nullptr; r.gamma = nullptr; r.beta = nullptr;
@@ -451,7 +461,7 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
   WHALE_TRY(launch_transpose(W_D, d, H, WDt, d, 0, bf, stream));       // [H, d]
   constexpr int kGroup = 512;   // columns per row-streaming workgroup
   if (bf && !sep && rs_fwd_ok(d, kGroup) && H % kGroup == 0 && 256 % (8 * (H / kGroup)) == 0) {
-    RsFwdArgs r;
+    RsFwdArgs r{};
     r.H = (const __bf16*)dY; r.ldh = d; r.W = (const __bf16*)WDt; r.W2 = (const __bf16*)WDt; r.nsplit = kGroup;
     r.Y = (__bf16*)dU; r.Y2 = (__bf16*)dU; r.ldy = Hu; r.Xn = nullptr; r.stats = nullptr;
     r.gamma = nullptr; r.beta = nullptr; r.M = s.M; r.kind = 2; r.eps = 0.f;

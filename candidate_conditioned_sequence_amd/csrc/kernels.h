@@ -92,6 +92,7 @@ inline int64_t gemm_norm_bwd_tiles(int64_t M) { return (M + 63) / 64; }
 // Shapes: rs_fwd_ok(K, N).
 struct RsFwdArgs {
   const __bf16* H; int64_t ldh;
+  const __bf16* H2; int64_t ldh2;   // gate = 4: columns [256, 512) of the rows
   const __bf16* W; const __bf16* W2; int nsplit;
   __bf16* Y; __bf16* Y2; int64_t ldy;
   __bf16* Xn; float* stats;
@@ -106,6 +107,9 @@ struct RsFwdArgs {
   // gate = 3: the fusion MLP's backward (kind 2, ngroups 1): H = dF, Z the
   // saved pre-activation (input, row stride ldz); Xn receives dZ = dF SiLU'(Z)
   // (required), Y = dZ W^T for rows < nsplit of W, Y2 = dF + dZ W2^T.
+  // gate = 4: the fusion MLP (K = 512, N = 256, kind 2): P = [H | H2] W^T,
+  // Y = H2 + SiLU(P), Z = P when non-null.  Shapes for gate 0 to 3:
+  // K = 256; gate 4: K = 512, N = 256.
   int gate; int ngroups; __bf16* Z; int64_t ldz;
 };
 // Backward: dX [M, N] = Norm backward(dY W^T) + R with dY = [X | X2] split at

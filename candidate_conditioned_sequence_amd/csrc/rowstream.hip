@@ -164,7 +164,10 @@ WHALE_DEV f32x4 lds_ldf4(uint32_t a) {
 // 3 the fusion MLP's backward (no norm): the rows H = dF and Z arrive
 // together, each wave forms dZ = dF SiLU'(Z) for its rows (in LDS and to
 // Xn), the MFMAs read dZ, and columns >= nsplit add the residual dF.  The
-// second input stream leaves room for two buffers only.
+// second input stream leaves room for two buffers only;
+// 4 the fusion MLP (K = 512, no norm): the rows are [H | H2] (two panels),
+// Y = H2 + SiLU(P) with the residual read from the second panel in LDS, and
+// Z = P (when kept) from a second staged tile.
 template <int K, int N, int EPI>
 __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int NW = N / 32, NT = NW * 64;
@@ -172,11 +175,12 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int BLK = kRB * K * 2;                 // bytes per block
   constexpr int NI = BLK / 1024;                   // transfer instructions per block
   constexpr int IPW = NI / NW;                     // ... per wave
-  constexpr int NBUF = EPI == 3 ? 2 : 4;
-  static_assert(NI % NW == 0 && IPW >= 1 && K == 256, "one panel, whole instructions per wave");
+  constexpr int NBUF = (EPI == 3 || EPI == 4) ? 2 : 4;
+  static_assert(NI % NW == 0 && IPW >= 1 && (K == 256 || (K == 512 && EPI == 4)), "panels, whole instructions");
   __shared__ __attribute__((aligned(1024))) char xs[NBUF][BLK];
   __shared__ __attribute__((aligned(1024))) char zb[EPI == 3 ? NBUF : 1][EPI == 3 ? BLK : 16];
   __shared__ __attribute__((aligned(1024))) char ob[2][kRB * N * 2];
+  __shared__ __attribute__((aligned(1024))) char ob2[EPI == 4 ? 2 : 1][EPI == 4 ? kRB * N * 2 : 16];
   __shared__ __attribute__((aligned(16))) float gb[2][K];
 
   const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, l32 = lane & 31,
@@ -224,8 +228,9 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
     const int64_t m0 = (int64_t)b * kRB;
 #pragma unroll
     for (int t = 0; t < IPW; ++t) {
-      const int j = w + NW * t;
-      dma_rows(a.H, a.ldh, m0, 2 * j, M, lane, lds_addr(&xs[p][1024 * j]));
+      const int j = w + NW * t, panel = j >> 4;
+      dma_rows(panel ? a.H2 : a.H, panel ? a.ldh2 : a.ldh, m0, 2 * (j & 15), M, lane,
+               lds_addr(&xs[p][panel * kPanel + 1024 * (j & 15)]));
       if constexpr (EPI == 3) dma_rows(a.Z, a.ldz, m0, 2 * j, M, lane, lds_addr(&zb[p][1024 * j]));
     }
   };
@@ -323,7 +328,19 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       bf16x4 o;
-      if (EPI == 3 && second) {
+      if constexpr (EPI == 4) {
+        // residual H2 of row l32, columns n0 + 8 g + 4 hh + u (second panel)
+        const int c = (n0 >> 3) + g;
+        const bf16x4 rv = lds_ld4(lds_addr(&xs[p][kPanel]) + 512 * l32 + 16 * (c ^ (l32 & 7)) + 8 * hh);
+        bf16x4 zo;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float z = acc[4 * g + u];
+          o[u] = from_f<bf16>(to_f(rv[u]) + siluf_(z));
+          zo[u] = from_f<bf16>(z);
+        }
+        stage_piece<N>(lds_addr(&ob2[i & 1][0]), l32, hh, n0, g, zo);
+      } else if (EPI == 3 && second) {
         // residual dF of row l32, columns n0 - nsplit + 8 g + 4 hh + u
         const int c = ((n0 - a.nsplit) >> 3) + g;
         const bf16x4 rv = lds_ld4(lds_addr(&xs[p][0]) + 512 * l32 + 16 * (c ^ (l32 & 7)) + 8 * hh);
@@ -360,6 +377,11 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       }
     } else {
       store_rows<N, NW>(obp, w, lane, m0, M, emit);
+      if constexpr (EPI == 4) {
+        if (a.Z)
+          store_rows<N, NW>(lds_addr(&ob2[i & 1][0]), w, lane, m0, M,
+                            [&](int64_t m, int n, const bf16x8& v) { st8<bf16>(a.Z + m * a.ldz + n, v); });
+      }
     }
   }
 }
@@ -559,7 +581,7 @@ constexpr int kCUsRS = 256;
 
 }  // namespace
 
-bool rs_fwd_ok(int K, int N) { return K == 256 && (N == 256 || N == 512); }
+bool rs_fwd_ok(int K, int N) { return (K == 256 && (N == 256 || N == 512)) || (K == 512 && N == 256); }
 bool rs_bwd_ok(int K, int N) { return (K == 256 || K == 512) && N == 256; }
 int64_t rs_bwd_grid(int64_t M) {
   const int64_t g = (M + 63) / 64;
@@ -576,16 +598,18 @@ hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
   const int64_t per = kCUsRS / a.ngroups;
   const int64_t gg = ((nblk < per ? nblk : per) + 7) / 8 * 8;
   const int g = (int)(gg * a.ngroups);
-  if (N == 256 && a.gate == 0)
+  if (K == 256 && N == 256 && a.gate == 0)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 256, 0>), dim3(g), dim3(512), 0, st, a);
-  else if (a.gate == 0)
+  else if (K == 256 && N == 512 && a.gate == 0)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 0>), dim3(g), dim3(1024), 0, st, a);
-  else if (a.gate == 1 && N == 512)
+  else if (K == 256 && N == 512 && a.gate == 1)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 1>), dim3(g), dim3(1024), 0, st, a);
-  else if (a.gate == 2 && N == 512 && a.Z != nullptr)
+  else if (K == 256 && N == 512 && a.gate == 2 && a.Z != nullptr)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 2>), dim3(g), dim3(1024), 0, st, a);
-  else if (a.gate == 3 && N == 512 && a.Z != nullptr && a.Xn != nullptr && a.ngroups == 1)
+  else if (K == 256 && N == 512 && a.gate == 3 && a.Z != nullptr && a.Xn != nullptr && a.ngroups == 1)
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 3>), dim3(g), dim3(1024), 0, st, a);
+  else if (a.gate == 4 && K == 512 && N == 256 && a.H2 != nullptr && a.ngroups == 1)
+    hipLaunchKernelGGL((rs_fwd_kernel<512, 256, 4>), dim3(g), dim3(512), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
