@@ -284,13 +284,17 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   if (bf && gate == WHALE_GATE_SHARED && rs_fwd_ok(s.d, kGroup) && H % kGroup == 0 && 256 % (8 * (H / kGroup)) == 0) {
     // Up projection by the row-streaming kernel: Norm_f (statistics saved
     // for the backward), F W_U^T and the tied gate in one pass over F.
+    // Only the product U is written (to U_saved, else to the workspace); the
+    // down projection forms the gate SiLU(U) U from it in its prologue.
+    void* Ubuf = U_saved ? U_saved : G;
     RsFwdArgs u{};
     u.H = (const __bf16*)F; u.ldh = s.d; u.W = (const __bf16*)W_U; u.W2 = (const __bf16*)W_U; u.nsplit = kGroup;
-    u.Y = (__bf16*)G; u.Y2 = (__bf16*)G; u.ldy = H; u.Xn = norm != WHALE_NORM_NONE ? (__bf16*)X_f : nullptr;
+    u.Y = nullptr; u.Y2 = nullptr; u.ldy = H; u.Xn = norm != WHALE_NORM_NONE ? (__bf16*)X_f : nullptr;
     u.stats = norm != WHALE_NORM_NONE ? stats_f : nullptr; u.gamma = g_f; u.beta = b_f;
     u.M = s.M; u.kind = (int)norm; u.eps = eps;
-    u.gate = 1; u.ngroups = H / kGroup; u.Z = (__bf16*)U_saved; u.ldz = H;
+    u.gate = 1; u.ngroups = H / kGroup; u.Z = (__bf16*)Ubuf; u.ldz = H;
     WHALE_TRY(launch_rs_fwd(u, s.d, kGroup, stream));
+    b.X = Ubuf; b.pro = PRO_GATE;
     return ret(launch_gemm_nt(b, bf, stream));
   }
   // X_f = Norm_f(F) once (statistics saved for the backward), so that the

@@ -169,7 +169,10 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
       const int ch = tid + NT * i;
       if (ch >= BM * CPR) continue;
       x8_t<T> v = ar[slot][i];
-      if (PRO == PRO_DACT) {
+      if (PRO == PRO_GATE) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { const float z = to_f(v[u]); v[u] = from_f<T>(siluf_(z) * z); }
+      } else if (PRO == PRO_DACT) {
         v = dact8<T>(v, ld8<T>(aptr2[i] + k0));
       } else if (PRO == PRO_NORM && a.norm_kind != 2) {
         const int k = k0 + 8 * (ch % CPR);
@@ -513,6 +516,9 @@ hipError_t gemm_pro(const GemmArgs& a, hipStream_t st) {
     case PRO_NORM: return gemm_epi<T, PRO_NORM>(a, st);
     case PRO_CONCAT: return gemm_epi<T, PRO_CONCAT>(a, st);
     case PRO_DACT: return gemm_epi<T, PRO_DACT>(a, st);
+    case PRO_GATE:
+      if (a.epi != EPI_RESID) return hipErrorInvalidValue;
+      return gemm_go<T, PRO_GATE, EPI_RESID, 128, sizeof(T) == 2 ? 256 : 128, 64>(a, st);
   }
   return hipErrorInvalidValue;
 }

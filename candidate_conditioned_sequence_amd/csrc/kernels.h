@@ -50,7 +50,8 @@ enum GemmPro {
   PRO_PLAIN = 0,
   PRO_NORM = 1,          // X rows normalised with stats + gamma/beta (norm_kind 0/1; 2 = none)
   PRO_CONCAT = 2,        // columns >= ksplit come from X2 (multiple of 64)
-  PRO_DACT = 3           // X = X * SiLU'(X2) elementwise (dZ from dF and Z)
+  PRO_DACT = 3,          // X = X * SiLU'(X2) elementwise (dZ from dF and Z)
+  PRO_GATE = 4           // X = SiLU(X) * X elementwise (the tied gate from its saved product; EPI_RESID only)
 };
 enum GemmEpi {
   EPI_STORE = 0,         // Y = acc; with Y2: columns >= nsplit go to Y2 (column - nsplit)
@@ -99,8 +100,9 @@ struct RsFwdArgs {
   const float* gamma; const float* beta;
   int64_t M; int kind; float eps;
   // gate = 1: the tied SwiGLU gate.  W has ngroups * N rows (N per column
-  // group), Z [M, ngroups N] (row stride ldz, may be null) receives the
-  // product and Y the gated U = SiLU(Z) Z; W2 / Y2 / nsplit unused (nsplit = N).
+  // group), Z [M, ngroups N] (row stride ldz) receives the product and Y the
+  // gated U = SiLU(Z) Z; either may be null; W2 / Y2 / nsplit unused
+  // (nsplit = N).
   // gate = 2: its backward (kind 2): Y = (H W^T) * (SiLU'(Z) Z + SiLU(Z))
   // with Z the saved product (input, required); the product is rounded to
   // bf16 once before the scaling.

@@ -213,10 +213,12 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
     if (EPI == 1) {
       const int col = grp * N + n;
       if (a.Z) st8<bf16>(a.Z + m * a.ldz + col, v);
-      bf16x8 u;
+      if (a.Y) {
+        bf16x8 u;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) { const float z = to_f(v[e]); u[e] = from_f<bf16>(siluf_(z) * z); }
-      st8<bf16>(a.Y + m * a.ldy + col, u);
+        for (int e = 0; e < 8; ++e) { const float z = to_f(v[e]); u[e] = from_f<bf16>(siluf_(z) * z); }
+        st8<bf16>(a.Y + m * a.ldy + col, u);
+      }
     } else {
       st8<bf16>(n < a.nsplit ? a.Y + m * a.ldy + n : a.Y2 + m * a.ldy + (n - a.nsplit), v);
     }
