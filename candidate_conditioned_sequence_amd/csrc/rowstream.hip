@@ -113,7 +113,9 @@ WHALE_DEV void stage_piece(uint32_t ob, int l32, int hh, int n0, int g, const bf
 }
 // Rows of the staged block: instruction j covers rows j * (64 / (N/8)) ...;
 // wave w takes j = w + NW t.  emit(m, n, v) writes the 8 values v of row m
-// from column n on.
+// from column n on.  Rows past M store again row M-1's values (their inputs
+// are copies of row M-1, so the values are the same bits), so the stores
+// need no branch.
 template <int N, int NW, typename Emit>
 WHALE_DEV void store_rows(uint32_t ob, int w, int lane, int64_t m0, int64_t M, Emit emit) {
   constexpr int RC = N / 8, RPI = 64 / RC, NIW = kRB / RPI / NW;
@@ -123,8 +125,7 @@ WHALE_DEV void store_rows(uint32_t ob, int w, int lane, int64_t m0, int64_t M, E
     const int j = w + NW * t;
     const int r = j * RPI + lane / RC, c = lane % RC;
     const bf16x8 v = lds_ld8(ob + r * (N * 2) + 16 * (c ^ (r & 7)));
-    const int64_t m = m0 + r;
-    if (m < M) emit(m, 8 * c, v);
+    emit(min(m0 + r, M - 1), 8 * c, v);
   }
 }
 // vmcnt(IPW * k) for k = 0, 1, 2 newer blocks of transfers in flight.
@@ -255,8 +256,7 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) dz[u] = from_f<bf16>(to_f(df[u]) * dsiluf_(to_f(z[u])));
         *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)za = dz;
-        const int64_t m = m0 + r;
-        if (m < M) st8<bf16>(a.Xn + m * K + 8 * c, dz);
+        st8<bf16>(a.Xn + min(m0 + r, M - 1) * K + 8 * c, dz);   // (rows past M: row M-1 again)
       }
       return;
     }
@@ -291,11 +291,9 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
         y[u + 4] = from_f<bf16>((v[u + 4] - mean) * rstd * g1[u] + e1[u]);
       }
       *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)la = y;
-      const int64_t m = m0 + r;
-      if (m < M) {
-        if (a.Xn && grp == 0) st8<bf16>(a.Xn + m * K + 8 * c, y);
-        if (a.stats && pos == 0 && grp == 0) *reinterpret_cast<f32x2*>(a.stats + 2 * m) = f32x2{mean, rstd};
-      }
+      const int64_t m = min(m0 + r, M - 1);   // (rows past M: row M-1 again, same values)
+      if (a.Xn && grp == 0) st8<bf16>(a.Xn + m * K + 8 * c, y);
+      if (a.stats && pos == 0 && grp == 0) *reinterpret_cast<f32x2*>(a.stats + 2 * m) = f32x2{mean, rstd};
     }
   };
 
@@ -355,7 +353,9 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       stage_piece<N>(obp, l32, hh, n0, g, o);
     }
     // This wave's transfers of block i+1 have landed once at most the newer
-    // blocks' ones are outstanding (loads complete in order).
+    // blocks' ones are outstanding (loads complete in order; the stores
+    // issued between are waited for too, which measured no slower than
+    // counting them).
     if (i + 1 < nmine) {
       wait_newer<IPW>(min(NBUF - 2, nmine - i - 2));
       normalise(b0 + (i + 1) * G, (i + 1) % NBUF);
@@ -366,16 +366,14 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
       for (int t = 0; t < NIW; ++t) {
         const int r = (w + NW * t) * RPI + lane / RC, c = lane % RC;
         const bf16x8 v = lds_ld8(obp + r * (N * 2) + 16 * (c ^ (r & 7)));
-        const int64_t m = m0 + r;
-        if (m < M) {
-          bf16x8 o;
+        const int64_t m = min(m0 + r, M - 1);   // (rows past M: row M-1 again, same values)
+        bf16x8 o;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float u = to_f(zin[t][e]);
-            o[e] = from_f<bf16>(to_f(v[e]) * (dsiluf_(u) * u + siluf_(u)));
-          }
-          st8<bf16>(a.Y + m * a.ldy + grp * N + 8 * c, o);
+        for (int e = 0; e < 8; ++e) {
+          const float u = to_f(zin[t][e]);
+          o[e] = from_f<bf16>(to_f(v[e]) * (dsiluf_(u) * u + siluf_(u)));
         }
+        st8<bf16>(a.Y + m * a.ldy + grp * N + 8 * c, o);
       }
     } else {
       store_rows<N, NW>(obp, w, lane, m0, M, emit);
