@@ -74,8 +74,8 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
   constexpr int CPR = BK / 8;                 // 8-element chunks per tile row
   constexpr int ACH = (BM * CPR + NT - 1) / NT, BCH = (BN * CPR + NT - 1) / NT;   // chunks per thread
   static_assert((BM * CPR) % 64 == 0 && (BN * CPR) % NT == 0, "tile/threads");
-  // Row-complete tiles (norm backward) stage the whole tile; others 64 rows per pass.
-  constexpr int SROWS = (EPI == EPI_NORM_BWD) ? BM : 64;
+  // The epilogue stages 64 rows per pass (row-complete for the norm backward).
+  constexpr int SROWS = 64;
   constexpr int TILE_BYTES = 2 * (BM + BN) * LDT * (int)sizeof(T);
   constexpr int STG_BYTES = SROWS * SLD * 4;
   __shared__ __attribute__((aligned(32))) char smem[TILE_BYTES > STG_BYTES ? TILE_BYTES : STG_BYTES];
@@ -376,12 +376,15 @@ __global__ __launch_bounds__((BM / 64) * (BN / 64) * 64, 2) void gemm_nt_kernel(
 #pragma unroll
         for (int u = 0; u < 8; ++u) { red[(slot * 2 + 0) * N + c0 + u] = pg[u]; red[(slot * 2 + 1) * N + c0 + u] = pb[u]; }
         __syncthreads();
+        // One partial row per 64-row pass (a pass wholly past M writes none).
         const int nslots = (NT / 64) * rpp;
-        for (int c = tid; c < 2 * N; c += NT) {
-          const int which = c / N, col = c % N;
-          float sacc = 0.f;
-          for (int q = 0; q < nslots; ++q) sacc += red[(q * 2 + which) * N + col];
-          a.part[(int64_t)tm * 2 * N + c] = sacc;
+        if (r0 < M) {
+          for (int c = tid; c < 2 * N; c += NT) {
+            const int which = c / N, col = c % N;
+            float sacc = 0.f;
+            for (int q = 0; q < nslots; ++q) sacc += red[(q * 2 + which) * N + col];
+            a.part[((int64_t)tm * NP + pass) * 2 * N + c] = sacc;
+          }
         }
       } else {
         // Generic epilogue: 8-column chunks, coalesced 16-byte accesses.
@@ -468,7 +471,7 @@ hipError_t gemm_go(const GemmArgs& a, hipStream_t st) {
   if (nt > (int64_t)1 << 30) return hipErrorInvalidValue;
   constexpr int NT = (BM / 64) * (BN / 64) * 64;
   constexpr int LDT = BK + 8, SLD = BN + 4;
-  constexpr int SROWS = (EPI == EPI_NORM_BWD) ? BM : 64;
+  constexpr int SROWS = 64;
   constexpr int lds = (2 * (BM + BN) * LDT * (int)sizeof(T) > SROWS * SLD * 4) ? 2 * (BM + BN) * LDT * (int)sizeof(T)
                                                                                : SROWS * SLD * 4;
   constexpr int per_cu_lds = 160 * 1024 / lds;
@@ -503,7 +506,12 @@ hipError_t gemm_epi(const GemmArgs& a, hipStream_t st) {
       if (a.N != 64 && a.N != 128 && a.N != 256 && a.N != 512) return hipErrorInvalidValue;
       if (a.N <= 64) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 64, 32>(a, st);
       if (a.N <= 128) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 128, 32>(a, st);
-      if (a.N <= 256) return gemm_go<T, PRO, EPI_NORM_BWD, 64, 256, 32>(a, st);
+      // bf16 with a plain prologue: 128-row tiles (eight waves), the epilogue
+      // staged 64 rows per pass, so each weight tile serves twice the rows.
+      if (a.N <= 256) {
+        if constexpr (sizeof(T) == 2 && PRO == PRO_PLAIN) return gemm_go<T, PRO, EPI_NORM_BWD, 128, 256, 32>(a, st);
+        return gemm_go<T, PRO, EPI_NORM_BWD, 64, 256, 32>(a, st);
+      }
       return gemm_go<T, PRO, EPI_NORM_BWD, 64, 512, sizeof(T) == 2 ? 32 : 16>(a, st);
   }
   return hipErrorInvalidValue;
