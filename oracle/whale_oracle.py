@@ -14,7 +14,8 @@ Recommendation with Wukong-HSTU Architecture"):
   [GS 2.1]  gist.science explainer, Technical Summary §2.1 (Core Architecture,
             "Attention-Based Fusion Module")
   [GS 2.2]  gist.science explainer, Technical Summary §2.2 (Efficiency
-            Optimizations: shared-gate SwiGLU, mixed precision)
+            Optimizations: shared key-value, shared-gate SwiGLU, mixed
+            precision)
   [PD 2]    paper-daily.com deep reading of WHALE, §2 (method details)
   [PV km]   pith.science verdict record, pith_extraction.key_machinery
   [PV ref]  pith.science verdict record, referee_report: minor comments on
@@ -52,6 +53,10 @@ reason in the design notes of the repository):
   R8  tied gate: G = SiLU(U) * U with U = X_f W_U^T.  Separate gate (merged
       GEMM with [W_G; W_U]): G = SiLU(U_g) * U_u.
   R9  an empty history (L_b = 0) gives A = 0, lse = -inf, zero gradients.
+  R10 shared key-value (K = V, [GS 2.2]) means one projection, through W_K,
+      whose output serves as both keys and values; the layer then has no
+      W_V, and the gradient of that one tensor is the sum of its gradients
+      in the two roles.  A layer whose parameters hold no W_V is tied.
 
 Layouts (row-vector convention y = x W^T, weights stored [out, in]):
   H_w, Q, A, F, Y : [M, d] with M = B*C*n_q, row m = (b*C + c)*n_q + i
@@ -139,21 +144,29 @@ def proj_qkv(H_w, H_s, norm, eps, g_q, b_q, g_kv, b_kv, W_Q, W_K, W_V):
 
     Queries from the normalised Wukong output, shared keys and values from the
     normalised HSTU output [PV km], [PD 2].  K and V are computed once per
-    history row: no candidate index appears (Footnote 1, [PV ref])."""
+    history row: no candidate index appears (Footnote 1, [PV ref]).
+    W_V = None is the shared key-value form (R10): V is K itself."""
     X_q, _, _ = norm_fwd(H_w, norm, g_q, b_q, eps)
     X_s, _, _ = norm_fwd(H_s, norm, g_kv, b_kv, eps)
-    return X_q @ _f64(W_Q).T, X_s @ _f64(W_K).T, X_s @ _f64(W_V).T
+    K = X_s @ _f64(W_K).T
+    return X_q @ _f64(W_Q).T, K, (K if W_V is None else X_s @ _f64(W_V).T)
 
 
 def proj_qkv_bwd(H_w, H_s, norm, eps, g_q, b_q, g_kv, b_kv, W_Q, W_K, W_V, dQ, dK, dV):
     """Chain rule through proj_qkv.  Returns a dict with dH_w (the Q-path part
-    only), dH_s, dW_Q, dW_K, dW_V, dg_q, db_q, dg_kv, db_kv."""
-    dQ, dK, dV = _f64(dQ), _f64(dK), _f64(dV)
+    only), dH_s, dW_Q, dW_K, dW_V, dg_q, db_q, dg_kv, db_kv.  In the shared
+    key-value form (W_V and dV None, R10) dK is the gradient of the one
+    tensor and there is no dW_V."""
+    dQ, dK = _f64(dQ), _f64(dK)
     X_q, _, _ = norm_fwd(H_w, norm, g_q, b_q, eps)
     X_s, _, _ = norm_fwd(H_s, norm, g_kv, b_kv, eps)
-    out = {"dW_Q": dQ.T @ X_q, "dW_K": dK.T @ X_s, "dW_V": dV.T @ X_s}
+    out = {"dW_Q": dQ.T @ X_q, "dW_K": dK.T @ X_s}
     dX_q = dQ @ _f64(W_Q)
-    dX_s = dK @ _f64(W_K) + dV @ _f64(W_V)
+    dX_s = dK @ _f64(W_K)
+    if W_V is not None:
+        dV = _f64(dV)
+        out["dW_V"] = dV.T @ X_s
+        dX_s = dX_s + dV @ _f64(W_V)
     out["dH_w"], out["dg_q"], out["db_q"] = norm_bwd(H_w, norm, g_q, eps, dX_q)
     out["dH_s"], out["dg_kv"], out["db_kv"] = norm_bwd(H_s, norm, g_kv, eps, dX_s)
     return out
@@ -299,11 +312,12 @@ def swiglu_ffn_bwd(F, norm, eps, g_f, b_f, W_U, gate, W_D, dY):
 def layer_fwd(H_w, H_s, offsets, C, n_q, h, p, norm=NORM_LAYER, eps=1e-5,
               act=ACT_SILU, gate=GATE_SHARED, ffn=True, scale=None):
     """One fusion layer: a1..a5 in order [GS 2.1].  `p` holds W_Q, W_K, W_V,
-    W_F, W_U, W_D and the norm parameters g_q, b_q, g_kv, b_kv, g_f, b_f.
+    W_F, W_U, W_D and the norm parameters g_q, b_q, g_kv, b_kv, g_f, b_f;
+    without W_V the layer shares one tensor as keys and values (R10).
     Returns a dict with every intermediate; 'Y' is the layer output (F when
     ffn is False)."""
     Q, K, V = proj_qkv(H_w, H_s, norm, eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"],
-                       p["W_Q"], p["W_K"], p["W_V"])
+                       p["W_Q"], p["W_K"], p.get("W_V"))
     A, lse = xattn_fwd(Q, K, V, offsets, C, n_q, h, scale)
     F, Z = fusion_mlp(A, H_w, p["W_F"], act)
     out = {"Q": Q, "K": K, "V": V, "A": A, "lse": lse, "F": F, "Z": Z}
@@ -328,9 +342,15 @@ def layer_bwd(H_w, H_s, offsets, C, n_q, h, p, dY, norm=NORM_LAYER, eps=1e-5,
         dF = _f64(dY)
     dA, dH_w_mlp, g["dW_F"] = fusion_mlp_bwd(fw["A"], H_w, p["W_F"], act, dF)
     dQ, dK, dV = xattn_bwd(fw["Q"], fw["K"], fw["V"], offsets, C, n_q, h, scale, dA)
+    W_V = p.get("W_V")
+    if W_V is None:
+        # One tensor in both roles: its gradient is the sum of the two (R10).
+        dK, dV = dK + dV, None
     pb = proj_qkv_bwd(H_w, H_s, norm, eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"],
-                      p["W_Q"], p["W_K"], p["W_V"], dQ, dK, dV)
-    g["dW_Q"], g["dW_K"], g["dW_V"] = pb["dW_Q"], pb["dW_K"], pb["dW_V"]
+                      p["W_Q"], p["W_K"], W_V, dQ, dK, dV)
+    for k in ("dW_Q", "dW_K", "dW_V"):
+        if k in pb:
+            g[k] = pb[k]
     g["dH_w"] = dH_w_mlp + pb["dH_w"]
     g["dH_s"] = pb["dH_s"]
     g.update(dg_q=pb["dg_q"], db_q=pb["db_q"], dg_kv=pb["dg_kv"], db_kv=pb["db_kv"])

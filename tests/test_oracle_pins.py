@@ -330,6 +330,59 @@ def test_gradients_match_torch_autograd():
         np.testing.assert_allclose(g[gname], T[name].grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
 
 
+def test_shared_kv_layer_matches_finite_differences_and_autograd():
+    """Shared key-value form (one tensor as keys and values, no W_V): every
+    gradient against central differences, and against torch autograd through
+    a model that feeds the same tensor to both roles of the attention."""
+    x, p, dY, kw = _layer_case(37, lengths=(4, 1, 3))
+    del p["W_V"]
+
+    def loss():
+        return float((O.layer_fwd(x["H_w"], x["H_s"], p=p, **kw)["Y"] * dY).sum())
+
+    g = O.layer_bwd(x["H_w"], x["H_s"], p=p, dY=dY, **kw)
+    assert "dW_V" not in g and g["dV"] is None
+    eps = 1e-6
+    for name, gname in GRAD_OF.items():
+        if name == "W_V":
+            continue
+        arr = x[name] if name in x else p[name]
+        num = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            old = arr[idx]
+            arr[idx] = old + eps
+            lp = loss()
+            arr[idx] = old - eps
+            lm = loss()
+            arr[idx] = old
+            num[idx] = (lp - lm) / (2 * eps)
+        np.testing.assert_allclose(g[gname], num, rtol=1e-6, atol=1e-7, err_msg=name)
+
+    T = {k: t64(v).requires_grad_() for k, v in {**x, **p}.items()}
+    C, n_q, h, off = kw["C"], kw["n_q"], kw["h"], kw["offsets"]
+    d = T["H_w"].shape[1]
+    Xq = TF.layer_norm(T["H_w"], (d,), T["g_q"], T["b_q"], 1e-5)
+    Xs = TF.layer_norm(T["H_s"], (d,), T["g_kv"], T["b_kv"], 1e-5)
+    Q, K = Xq @ T["W_Q"].T, Xs @ T["W_K"].T
+    dh = d // h
+    A_rows = []
+    for b in range(len(off) - 1):
+        q = Q[b * C * n_q:(b + 1) * C * n_q].reshape(-1, h, dh).transpose(0, 1)
+        k = K[off[b]:off[b + 1]].reshape(-1, h, dh).transpose(0, 1)
+        if k.shape[1] == 0:
+            A_rows.append(torch.zeros(C * n_q, d, dtype=torch.float64))
+            continue
+        A_rows.append(TF.scaled_dot_product_attention(q, k, k).transpose(0, 1).reshape(-1, d))
+    A = torch.cat(A_rows)
+    F = T["H_w"] + TF.silu(torch.cat([A, T["H_w"]], 1) @ T["W_F"].T)
+    U = TF.layer_norm(F, (d,), T["g_f"], T["b_f"], 1e-5) @ T["W_U"].T
+    Y = F + (TF.silu(U) * U) @ T["W_D"].T
+    (Y * t64(dY)).sum().backward()
+    for name, gname in GRAD_OF.items():
+        if name != "W_V":
+            np.testing.assert_allclose(g[gname], T[name].grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
+
+
 def test_single_key_backward_closed_form():
     c = small_case(seed=29, lengths=(1, 1, 1))
     dA = rnd(31, *c["Q"].shape)
