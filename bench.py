@@ -37,17 +37,19 @@ XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_pp_kernel<64>",
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 
-def flops(cfg, T, H, gate_sep=False):
-    """Algorithmic FLOPs of one layer (forward, backward) for T history rows."""
+def flops(cfg, T, H, gate_sep=False, shared_kv=False):
+    """Algorithmic FLOPs of one layer (forward, backward) for T history rows.
+    With shared keys and values the history side has one projection, not two."""
     M, d, QR = cfg.M, cfg.d, cfg.C * cfg.n_q
     Hu = 2 * H if gate_sep else H
     attn_f = 4.0 * QR * d * T
-    gemm_f = 2.0 * M * d * d + 4.0 * T * d * d + 2.0 * M * 2 * d * d + 2.0 * M * d * Hu + 2.0 * M * H * d
+    kv_f = (2.0 if shared_kv else 4.0) * T * d * d
+    gemm_f = 2.0 * M * d * d + kv_f + 2.0 * M * 2 * d * d + 2.0 * M * d * Hu + 2.0 * M * H * d
     return {"attn_fwd": attn_f, "gemm_fwd": gemm_f, "fwd": attn_f + gemm_f,
             "attn_bwd": 2.5 * attn_f, "gemm_bwd": 2.0 * gemm_f, "bwd": 2.5 * attn_f + 2.0 * gemm_f}
 
 
-def cpu_baseline(cfg, p, L, n_req):
+def cpu_baseline(cfg, p, L, n_req, shared_kv=False):
     """fp64 oracle, forward + backward of the first n_req requests."""
     from candidate_conditioned_sequence_amd import synth
     from oracle import whale_oracle as O
@@ -63,7 +65,7 @@ def cpu_baseline(cfg, p, L, n_req):
     O.layer_bwd(H_w, H_s, off, cfg.C, cfg.n_q, cfg.h, p, dY)
     dt = time.perf_counter() - t0
     sub = synth.scaled(cfg, B=n_req)
-    f = flops(sub, int(off[-1]), cfg.H)
+    f = flops(sub, int(off[-1]), cfg.H, shared_kv=shared_kv)
     total = f["fwd"] + f["bwd"]
     return {"value": total / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "requests_per_s": n_req / dt, "seconds": dt,
@@ -79,6 +81,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
+    ap.add_argument("--shared-kv", action="store_true",
+                    help="shared key-value layer: one history-side projection whose output serves as K and V")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy (negation) of 512 MiB fp32, 3 times: the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -99,6 +103,8 @@ def main():
     L = synth.lengths(cfg)
     T = int(L.sum())
     p = synth.layer_params(cfg)
+    if args.shared_kv:
+        del p["W_V"]
     print(f"[bench] generating inputs: B={cfg.B} C={cfg.C} n_q={cfg.n_q} d={cfg.d} h={cfg.h} T={T}", file=sys.stderr,
           flush=True)
     H_w, H_s, off = synth.inputs(cfg)
@@ -192,7 +198,7 @@ def main():
         per_call[n].append(e0.elapsed_time(e1))
     avg = {n: float(np.mean(v)) for n, v in per_call.items() if v}
 
-    f = flops(cfg, T, cfg.H)
+    f = flops(cfg, T, cfg.H, shared_kv=args.shared_kv)
     step_flops = f["fwd"] + (0.0 if args.fwd_only else f["bwd"])
     fwd_ms = sum(avg[c] for c in ("proj_qkv", "xattn_fwd", "fusion_mlp", "swiglu_ffn"))
     value = step_flops / (ms * 1e-3) / 1e12
@@ -203,10 +209,10 @@ def main():
     kname = "xattn_fwd_pp_kernel<64>"
     tr = XATTN_FWD_TRAFFIC
     traffic = None
-    if tr is not None and tr["kernel"] == kname:
+    if tr is not None and tr["kernel"] == kname and not args.shared_kv:
         traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]))
     M, d = cfg.M, cfg.d
-    algo_bytes = 2 * (M * d + 2 * T * d + M * d) + 4 * M * cfg.h
+    algo_bytes = 2 * (M * d + (1 if args.shared_kv else 2) * T * d + M * d) + 4 * M * cfg.h
     roof = {"bound": "mfma", "kernel": kname, "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic, "traffic_unit": "bytes per launch", "algorithmic_bytes": algo_bytes,
@@ -217,7 +223,7 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "fusion layer fwd+bwd" if not args.fwd_only else "fusion layer fwd",
                    "B": cfg.B, "C": cfg.C, "n_q": cfg.n_q, "d": cfg.d, "h": cfg.h, "H": cfg.H, "L_b": int(L[0]),
-                   "T": T, "gate": "shared", "norm": "layer"},
+                   "T": T, "gate": "shared", "norm": "layer", "kv": "shared" if args.shared_kv else "separate"},
         "requests_per_s": round(cfg.B / (ms * 1e-3), 1),
         "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
         "fwd": {"ms": round(fwd_ms, 3), "tflops": round(f["fwd"] / (fwd_ms * 1e-3) / 1e12, 1),
@@ -230,7 +236,7 @@ def main():
     }
     if not args.no_cpu:
         print(f"[bench] cpu baseline ({args.cpu_requests} requests, fp64 oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(cfg, p, L, args.cpu_requests)
+        res["cpu_baseline"] = cpu_baseline(cfg, p, L, args.cpu_requests, args.shared_kv)
     print(json.dumps(res))
 
 

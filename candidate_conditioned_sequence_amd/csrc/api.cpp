@@ -152,14 +152,17 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
   whale_status_t rc = check_dims(dims, dtype, &s);
   if (rc != WHALE_OK) return rc;
   if (!norm_ok(norm) || !(eps >= 0.f) || !std::isfinite(eps)) return WHALE_ERR_SHAPE;
-  if (!H_w || !W_Q || !W_K || !W_V || !Q) return WHALE_ERR_NULL;
-  if (s.T > 0 && (!H_s || !K || !V)) return WHALE_ERR_NULL;
+  // Shared key-value form: no W_V and no V; K serves as both.
+  const bool tied = !W_V && !V;
+  if (!H_w || !W_Q || !W_K || (!W_V && !tied) || !Q) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!H_s || !K || (!V && !tied))) return WHALE_ERR_NULL;
   if (!norm_params_ok(norm, g_q, b_q) || !norm_params_ok(norm, g_kv, b_kv)) return WHALE_ERR_NULL;
   if (norm != WHALE_NORM_NONE && (!stats_q || (s.T > 0 && !stats_kv))) return WHALE_ERR_NULL;
   const bool bf = dtype == WHALE_BF16;
   const int nk = (int)norm;
   const bool nrm = norm != WHALE_NORM_NONE;
-  if (bf && rs_fwd_ok(s.d, s.d) && rs_fwd_ok(s.d, 2 * s.d)) {
+  const int nkv = tied ? s.d : 2 * s.d;   // history-side output columns
+  if (bf && rs_fwd_ok(s.d, s.d) && rs_fwd_ok(s.d, nkv)) {
     // Row-streaming kernels: the norm (statistics, X_q / X_s) and the
     // projection in one pass over the rows; K and V together.
     RsFwdArgs q{};
@@ -171,11 +174,11 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
     WHALE_TRY(launch_rs_fwd(q, s.d, s.d, stream));
     if (s.T > 0) {
       RsFwdArgs kv = q;
-      kv.H = (const __bf16*)H_s; kv.W = (const __bf16*)W_K; kv.W2 = (const __bf16*)W_V;
-      kv.Y = (__bf16*)K; kv.Y2 = (__bf16*)V;
+      kv.H = (const __bf16*)H_s; kv.W = (const __bf16*)W_K; kv.W2 = (const __bf16*)(tied ? W_K : W_V);
+      kv.Y = (__bf16*)K; kv.Y2 = (__bf16*)(tied ? K : V);
       kv.Xn = nrm ? (__bf16*)X_s : nullptr; kv.stats = nrm ? stats_kv : nullptr;
       kv.gamma = g_kv; kv.beta = b_kv; kv.M = s.T;
-      WHALE_TRY(launch_rs_fwd(kv, s.d, 2 * s.d, stream));
+      WHALE_TRY(launch_rs_fwd(kv, s.d, nkv, stream));
     }
     return WHALE_OK;
   }
@@ -194,11 +197,13 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
   a.pro = (nrm && !mq) ? PRO_NORM : PRO_PLAIN; a.epi = EPI_STORE;
   WHALE_TRY(launch_gemm_nt(a, bf, stream));
   if (s.T > 0) {
-    // K and V in one pass over the history rows: weight rows [0, d) from W_K, [d, 2d) from W_V.
+    // K and V in one pass over the history rows: weight rows [0, d) from W_K, [d, 2d) from W_V
+    // (K alone in the shared key-value form).
     GemmArgs b = a;
     b.X = ms ? X_s : H_s; b.stats = stats_kv; b.gamma = g_kv; b.beta = b_kv;
     b.pro = (nrm && !ms) ? PRO_NORM : PRO_PLAIN;
-    b.W = W_K; b.W2 = W_V; b.nsplit = s.d; b.Y = K; b.Y2 = V; b.M = s.T; b.N = 2 * s.d;
+    b.W = W_K; b.Y = K; b.M = s.T; b.N = nkv;
+    if (!tied) { b.W2 = W_V; b.nsplit = s.d; b.Y2 = V; }
     WHALE_TRY(launch_gemm_nt(b, bf, stream));
   }
   return WHALE_OK;
@@ -336,7 +341,9 @@ whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dt
   whale_status_t rc = check_dims(dims, dtype, &s);
   if (rc != WHALE_OK) return rc;
   if (!Q || !offsets || !A || !lse || !dA || !dQ || !workspace) return WHALE_ERR_NULL;
-  if (s.T > 0 && (!K || !V || !dK || !dV)) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!K || !V || !dK)) return WHALE_ERR_NULL;
+  // dV = NULL: shared key-value form, V must be K; dK receives dK + dV.
+  if (s.T > 0 && !dV && V != K) return WHALE_ERR_SHAPE;
   if (!(scale >= 0.f) || !std::isfinite(scale)) return WHALE_ERR_SHAPE;
   if (ws_bytes < whale_jagged_xattn_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
   Carve c(workspace);
@@ -527,8 +534,11 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
   whale_status_t rc = check_dims(dims, dtype, &s);
   if (rc != WHALE_OK) return rc;
   if (!norm_ok(norm) || !(eps >= 0.f) || !std::isfinite(eps)) return WHALE_ERR_SHAPE;
-  if (!H_w || !W_Q || !W_K || !W_V || !dQ || !dH_w || !dW_Q || !dW_K || !dW_V || !workspace) return WHALE_ERR_NULL;
-  if (s.T > 0 && (!H_s || !dK || !dV || !dH_s)) return WHALE_ERR_NULL;
+  // Shared key-value form: no W_V, dV or dW_V; dK is the gradient of the one tensor.
+  const bool tied = !W_V && !dV && !dW_V;
+  if (!H_w || !W_Q || !W_K || (!W_V && !tied) || !dQ || !dH_w || !dW_Q || !dW_K || (!dW_V && !tied) || !workspace)
+    return WHALE_ERR_NULL;
+  if (s.T > 0 && (!H_s || !dK || (!dV && !tied) || !dH_s)) return WHALE_ERR_NULL;
   if (!norm_params_ok(norm, g_q, b_q) || !norm_params_ok(norm, g_kv, b_kv)) return WHALE_ERR_NULL;
   if (norm != WHALE_NORM_NONE) {
     if (!stats_q || (s.T > 0 && !stats_kv) || !dg_q || !dg_kv) return WHALE_ERR_NULL;
@@ -570,12 +580,15 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
   }
   Wg wq(dQ, d, Xqin, d, WPRO_PLAIN, s.M, d, d, dW_Q, part);
   WHALE_TRY(wq.run(bf, stream));
-  if (s.T > 0) {
+  if (s.T > 0 && tied) {
+    Wg wk(dK, d, Xsin, d, WPRO_PLAIN, s.T, d, d, dW_K, part);
+    WHALE_TRY(wk.run(bf, stream));
+  } else if (s.T > 0) {
     Wg wkv(dK, d, Xsin, d, WPRO_PLAIN, s.T, 2 * d, d, dW_K, part);
     WHALE_TRY(wkv.dual(dV, d, dW_V).run(bf, stream));
   } else {
     WHALE_TRY(launch_fill_zero(dW_K, (int64_t)d * d, stream));
-    WHALE_TRY(launch_fill_zero(dW_V, (int64_t)d * d, stream));
+    if (!tied) WHALE_TRY(launch_fill_zero(dW_V, (int64_t)d * d, stream));
   }
   // dH_w = Norm_q backward(dQ W_Q) + dH_w_in ; dH_s = Norm_kv backward([dK, dV] [W_K; W_V])
   // bf16 at d = 256: the row-streaming kernels (weight slice resident, rows
@@ -599,14 +612,16 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
     WHALE_TRY(launch_colsum_reduce(npq, rs ? rs_bwd_grid(s.M) : gemm_norm_bwd_tiles(s.M), d, dg_q,
                                    norm == WHALE_NORM_LAYER ? db_q : nullptr, cscr, stream));
   if (s.T > 0) {
-    WHALE_TRY(launch_transpose(W_K, d, d, WKVt, 2 * d, 0, bf, stream));
-    WHALE_TRY(launch_transpose(W_V, d, d, WKVt, 2 * d, d, bf, stream));
+    // dH_s = Norm_kv backward(dK W_K [+ dV W_V]): W^T is [d, 2d] ([d, d] when tied).
+    const int kk = tied ? d : 2 * d;
+    WHALE_TRY(launch_transpose(W_K, d, d, WKVt, kk, 0, bf, stream));
+    if (!tied) WHALE_TRY(launch_transpose(W_V, d, d, WKVt, kk, d, bf, stream));
     if (rs)
-      WHALE_TRY(launch_rs_bwd(rs_args(dK, dV, WKVt, H_s, stats_kv, g_kv, nullptr, dH_s, npk, s.T), 2 * d, d,
-                              stream));
+      WHALE_TRY(launch_rs_bwd(rs_args(dK, tied ? nullptr : dV, WKVt, H_s, stats_kv, g_kv, nullptr, dH_s, npk, s.T),
+                              kk, d, stream));
     else
-      WHALE_TRY(norm_bwd_gemm(dK, d, dV, d, WKVt, 2 * d, 2 * d, H_s, stats_kv, g_kv, nk, nullptr, dH_s, npk, s.T,
-                              d, bf, stream));
+      WHALE_TRY(norm_bwd_gemm(dK, d, tied ? nullptr : dV, tied ? 0 : d, WKVt, kk, kk, H_s, stats_kv, g_kv, nk,
+                              nullptr, dH_s, npk, s.T, d, bf, stream));
     if (norm != WHALE_NORM_NONE)
       WHALE_TRY(launch_colsum_reduce(npk, rs ? rs_bwd_grid(s.T) : gemm_norm_bwd_tiles(s.T), d, dg_kv,
                                      norm == WHALE_NORM_LAYER ? db_kv : nullptr, cscr, stream));

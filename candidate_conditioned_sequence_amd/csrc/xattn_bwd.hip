@@ -395,8 +395,17 @@ __global__ __launch_bounds__(NWK * 64, 2) void bwd_dkdv_kernel(
   }
 
   if (!kok) return;
+  // dV == nullptr: shared key-value form (V is K), one gradient dK + dV.
+  const bool tied = dV == nullptr;
   if (part == nullptr) {
     T* dkp = dK + (lo + key) * d + j * DH;
+    if (tied) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dkp[32 * e + acc_row(r, hh)] = from_f<T>(fmaf(dk[e][r], scale, dv[e][r]));
+      return;
+    }
     T* dvp = dV + (lo + key) * d + j * DH;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
@@ -408,6 +417,13 @@ __global__ __launch_bounds__(NWK * 64, 2) void bwd_dkdv_kernel(
       }
   } else {
     float* pk = part + ((int64_t)split * 2 * T_rows + lo + key) * d + j * DH;
+    if (tied) {
+#pragma unroll
+      for (int e = 0; e < NE; ++e)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pk[32 * e + acc_row(r, hh)] = fmaf(dk[e][r], scale, dv[e][r]);
+      return;
+    }
     float* pv = pk + T_rows * d;
 #pragma unroll
     for (int e = 0; e < NE; ++e)
@@ -420,11 +436,13 @@ __global__ __launch_bounds__(NWK * 64, 2) void bwd_dkdv_kernel(
   }
 }
 
+// Partials are [S][2][n] (dK then dV); with dV == nullptr (shared key-value
+// form) only the first half of each split holds data, already dK + dV.
 template <typename T>
 __global__ __launch_bounds__(256) void kv_split_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
                                                               T* __restrict__ dK, T* __restrict__ dV) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= 2 * n) return;
+  if (i >= (dV ? 2 * n : n)) return;
   float s = 0.f;
   for (int k = 0; k < splits; ++k) s += part[(int64_t)k * 2 * n + i];
   if (i < n) dK[i] = from_f<T>(s);
@@ -479,7 +497,8 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     const int64_t n = a.T * a.d;
-    hipLaunchKernelGGL(kv_split_reduce_kernel<T>, dim3((unsigned)((2 * n + 255) / 256)), dim3(256), 0, st, a.partial,
+    const int64_t nr = a.dV ? 2 * n : n;
+    hipLaunchKernelGGL(kv_split_reduce_kernel<T>, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, st, a.partial,
                        a.splits, n, (T*)a.dK, (T*)a.dV);
     return hipGetLastError();
   }

@@ -20,7 +20,9 @@ def _ws(nbytes, dev):
 
 class FusionLayer:
     """Weights are torch device tensors in the layer's dtype (W_Q, W_K, W_V,
-    W_F, W_U, W_D); norm parameters are fp32 (g_q, b_q, g_kv, b_kv, g_f, b_f)."""
+    W_F, W_U, W_D); norm parameters are fp32 (g_q, b_q, g_kv, b_kv, g_f, b_f).
+    Without W_V (absent or None) the layer shares one tensor as keys and
+    values (gist.science Technical Summary §2.2, shared key-value)."""
 
     def __init__(self, params, C, n_q, h, norm=wb.NORM_LAYER, eps=1e-5, act=wb.ACT_SILU, gate=wb.GATE_SHARED,
                  ffn=True, scale=0.0):
@@ -30,6 +32,7 @@ class FusionLayer:
         self.scale = scale
         self.d = params["W_Q"].shape[0]
         self.H = params["W_D"].shape[1]
+        self.tied_kv = params.get("W_V") is None
         self.ctx = None
 
     def dims(self, H_w, max_L, total_L):
@@ -41,7 +44,8 @@ class FusionLayer:
         M, T, d = H_w.shape[0], H_s.shape[0], self.d
         dm = self.dims(H_w, max_L, T)
         nn = self.norm != wb.NORM_NONE
-        Q, K, V = _empty((M, d), dt, dev), _empty((T, d), dt, dev), _empty((T, d), dt, dev)
+        Q, K = _empty((M, d), dt, dev), _empty((T, d), dt, dev)
+        V = None if self.tied_kv else _empty((T, d), dt, dev)
         sq = _empty((M, 2), torch.float32, dev) if nn else None
         skv = _empty((T, 2), torch.float32, dev) if nn else None
         # The normalised inputs are written once (the projections then read them
@@ -50,7 +54,9 @@ class FusionLayer:
         Xq = _empty((M, d), dt, dev) if nn else None
         Xs = _empty((T, d), dt, dev) if nn else None
         wb.whale_proj_qkv(dm, H_w, H_s, self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"], p["W_Q"],
-                          p["W_K"], p["W_V"], Q, K, V, sq, skv, Xq, Xs, stream)
+                          p["W_K"], p.get("W_V"), Q, K, V, sq, skv, Xq, Xs, stream)
+        if self.tied_kv:
+            V = K
         A, lse = _empty((M, d), dt, dev), _empty((M, self.h), torch.float32, dev)
         wb.whale_jagged_xattn_fwd(dm, Q, K, V, offsets, self.scale, A, lse, stream)
         F = _empty((M, d), dt, dev)
@@ -99,19 +105,20 @@ class FusionLayer:
         ws = _ws(wb.whale_fusion_mlp_bwd_workspace_size(dm, code), dev)
         wb.whale_fusion_mlp_bwd(dm, c["A"], c["H_w"], p["W_F"], self.act, c["Z"], dF, dA, dHw_mlp, g["dW_F"], ws,
                                 stream)
-        dQ, dK, dV = _empty((M, d), dt, dev), _empty((T, d), dt, dev), _empty((T, d), dt, dev)
+        dQ, dK = _empty((M, d), dt, dev), _empty((T, d), dt, dev)
+        dV = None if self.tied_kv else _empty((T, d), dt, dev)
         ws = _ws(wb.whale_jagged_xattn_bwd_workspace_size(dm, code), dev)
         wb.whale_jagged_xattn_bwd(dm, c["Q"], c["K"], c["V"], c["offsets"], self.scale, c["A"], c["lse"], dA, dQ, dK,
                                   dV, ws, stream)
         g["dH_w"], g["dH_s"] = _empty((M, d), dt, dev), _empty((T, d), dt, dev)
-        for k in ("dW_Q", "dW_K", "dW_V"):
+        for k in ("dW_Q", "dW_K") + (() if self.tied_kv else ("dW_V",)):
             g[k] = _empty((d, d), torch.float32, dev)
         for k in ("dg_q", "db_q", "dg_kv", "db_kv"):
             g[k] = _empty((d,), torch.float32, dev)
         ws = _ws(wb.whale_proj_qkv_bwd_workspace_size(dm, code), dev)
         wb.whale_proj_qkv_bwd(dm, c["H_w"], c["H_s"], self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"],
-                              c["stats_q"], c["stats_kv"], p["W_Q"], p["W_K"], p["W_V"], dQ, dK, dV, dHw_mlp,
-                              g["dH_w"], g["dH_s"], g["dW_Q"], g["dW_K"], g["dW_V"], g["dg_q"], g["db_q"], g["dg_kv"],
+                              c["stats_q"], c["stats_kv"], p["W_Q"], p["W_K"], p.get("W_V"), dQ, dK, dV, dHw_mlp,
+                              g["dH_w"], g["dH_s"], g["dW_Q"], g["dW_K"], g.get("dW_V"), g["dg_q"], g["db_q"], g["dg_kv"],
                               g["db_kv"], ws, c.get("X_q"), c.get("X_s"), stream)
         g.update(dA=dA, dQ=dQ, dK=dK, dV=dV, dF=dF)
         return g

@@ -7,8 +7,9 @@
  *   [GS 2.1]  gist.science explainer, Technical Summary §2.1 (Core
  *             Architecture, "Attention-Based Fusion Module")
  *   [GS 2.2]  gist.science explainer, Technical Summary §2.2 (Efficiency
- *             Optimizations: asymmetric backward variants, shared-gate
- *             SwiGLU, BF16 mixed precision, shape-hint tensors)
+ *             Optimizations: shared key-value, asymmetric backward
+ *             variants, shared-gate SwiGLU, BF16 mixed precision, shape-hint
+ *             tensors)
  *   [PD 2]    paper-daily.com deep reading of WHALE, §2 (method details;
  *             query-dimension split of the backward)
  *   [PV km]   pith.science verdict record, pith_extraction.key_machinery
@@ -115,6 +116,11 @@ const char* whale_version(void);
  * are written once and the projections read them; NULL, the projections
  * normalise their input tiles on the fly.  Passing them on to
  * whale_proj_qkv_bwd saves the backward from forming them again.
+ *
+ * Shared key-value form ([GS 2.2]: one tensor serves as keys and values,
+ * which halves the history-side memory traffic): W_V and V both NULL.  Only
+ * K = Norm_kv(H_s) W_K^T is computed, and the caller passes K as both K and
+ * V to the attention calls.  Exactly one of W_V, V NULL is WHALE_ERR_NULL.
  */
 whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype,
                               const void* H_w, const void* H_s,
@@ -136,7 +142,8 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype,
  * All C*n_q queries of a request read the same K/V rows: each K/V tile is
  * staged once per workgroup and reused by all of its queries.
  * scale == 0 selects 1/sqrt(d_h).  An empty history (L_b = 0) gives A = 0
- * and lse = -inf.  lse may be NULL.
+ * and lse = -inf.  lse may be NULL.  K and V may be the same buffer (the
+ * shared key-value form of whale_proj_qkv).
  */
 whale_status_t whale_jagged_xattn_fwd(const whale_dims_t* dims, whale_dtype_t dtype,
                                       const void* Q, const void* K, const void* V,
@@ -191,6 +198,9 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype,
  * query splits, whose fp32 partials are summed in a fixed order.
  * lse must be the forward's.  workspace: at least
  * whale_jagged_xattn_bwd_workspace_size(dims, dtype) bytes of device memory.
+ * Shared key-value form: V == K and dV NULL; dK then receives the gradient
+ * of the one tensor, scale dS^T Q + P^T dA, summed in fp32 and rounded
+ * once.  dV NULL with V != K is WHALE_ERR_SHAPE.
  */
 size_t whale_jagged_xattn_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype);
 whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
@@ -242,6 +252,10 @@ whale_status_t whale_swiglu_ffn_bwd(const whale_dims_t* dims, whale_dtype_t dtyp
  * the norm parameter gradients are then not written and may be NULL).
  * X_q / X_s: the forward's normalised inputs if it wrote them, else NULL
  * (they are then formed again in the workspace).
+ * Shared key-value form: W_V, dV and dW_V all NULL; dK is then the gradient
+ * of the one tensor (from whale_jagged_xattn_bwd with dV NULL), and
+ * dW_K = dK^T X_s, dX_s = dK W_K.  Some but not all three NULL is
+ * WHALE_ERR_NULL.
  */
 size_t whale_proj_qkv_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype);
 whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,

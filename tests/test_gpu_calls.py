@@ -217,6 +217,41 @@ def test_xattn_bwd(gpu, case):
     assert_close("dV", dV, dV_ref, dtype)
 
 
+# Shared key-value form: V is K, and the backward returns one gradient dK + dV.
+# The first three cases run split query ranges with fp32 partials (ragged and
+# empty histories among them); the last has enough history tiles for no split.
+SHARED_KV_CASES = [
+    ("f32", 128, 2, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 128, 4, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 256, 4, 20, 15, [130, 1, 700, 64]),
+    ("bf16", 256, 4, 16, 32, [2100, 2050, 1999, 2100, 7, 2100, 1500, 2048]),
+]
+
+
+@pytest.mark.parametrize("case", SHARED_KV_CASES, ids=lambda c: f"{c[0]}-d{c[1]}h{c[2]}-C{c[3]}nq{c[4]}-B{len(c[5])}")
+def test_xattn_shared_kv(gpu, case):
+    dtype, d, h, C, n_q, L = case
+    print(f"\n[xattn shared kv] {case}", flush=True)
+    B = len(L)
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Q, K, dA = draw(71, (M, d), dtype), draw(72, (T, d), dtype), draw(73, (M, d), dtype)
+    A_ref, _ = O.xattn_fwd(Q, K, K, off, C, n_q, h)
+    dQ_ref, dK_ref, dV_ref = O.xattn_bwd(Q, K, K, off, C, n_q, h, None, dA)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tQ, tK, tdA = (to_dev(x, dtype, gpu) for x in (Q, K, dA))
+    toff = i64_dev(off, gpu)
+    A, lse = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    wb.whale_jagged_xattn_fwd(dm, tQ, tK, tK, toff, 0.0, A, lse)
+    dQ, dK = torch.empty_like(tQ), torch.empty_like(tK)
+    ws = torch.empty(wb.whale_jagged_xattn_bwd_workspace_size(dm, wb._dtype_code(tQ)), dtype=torch.uint8, device=gpu)
+    wb.whale_jagged_xattn_bwd(dm, tQ, tK, tK, toff, 0.0, A, lse, tdA, dQ, dK, None, ws)
+    torch.cuda.synchronize()
+    assert_close("A", A, A_ref, dtype)
+    assert_close("dQ", dQ, dQ_ref, dtype)
+    assert_close("dK+dV", dK, dK_ref + dV_ref, dtype)
+
+
 # bf16 with SiLU at d = 256: the row-streaming kernel (dZ, dA and dH_w in one
 # pass; M = 9001 gives several 32-row blocks per workgroup and a ragged one).
 @pytest.mark.parametrize("dtype,act,M,d", [("f32", O.ACT_SILU, 300, 128), ("bf16", O.ACT_SILU, 300, 128),
@@ -332,4 +367,49 @@ def test_proj_qkv_bwd(gpu, dtype, norm, d, keep, L):
         assert_close("dg_kv", dgb[2], ref["dg_kv"], dtype)
     if norm == O.NORM_LAYER:
         assert_close("db_q", dgb[1], ref["db_q"], dtype)
+        assert_close("db_kv", dgb[3], ref["db_kv"], dtype)
+
+
+@pytest.mark.parametrize("dtype,norm,d,L", [("f32", O.NORM_LAYER, 128, PROJ_L), ("bf16", O.NORM_RMS, 128, PROJ_L),
+                                            ("bf16", O.NORM_LAYER, 256, PROJ_LONG),
+                                            ("bf16", O.NORM_NONE, 256, PROJ_L)],
+                         ids=lambda v: str(len(v)) if isinstance(v, list) else str(v))
+def test_proj_qkv_shared_kv(gpu, dtype, norm, d, L):
+    """Shared key-value form: no W_V, no V; the backward takes one dK."""
+    print(f"\n[proj_qkv shared kv] {dtype} norm={norm} d={d} L={L}", flush=True)
+    B, C, n_q = len(L), 5, 7
+    h = d // 64
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Hw, Hs = draw(81, (M, d), dtype), draw(82, (T, d), dtype)
+    Wq, Wk = weights(83, d, d, dtype), weights(84, d, d, dtype)
+    dQ, dK = draw(85, (M, d), dtype), draw(86, (T, d), dtype)
+    g = 1 + 0.2 * draw(87, (2, d), "f32")
+    bt = 0.2 * draw(88, (2, d), "f32")
+    Q_ref, K_ref, V_ref = O.proj_qkv(Hw, Hs, norm, 1e-5, g[0], bt[0], g[1], bt[1], Wq, Wk, None)
+    assert V_ref is K_ref
+    ref = O.proj_qkv_bwd(Hw, Hs, norm, 1e-5, g[0], bt[0], g[1], bt[1], Wq, Wk, None, dQ, dK, None)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tHw, tHs = to_dev(Hw, dtype, gpu), to_dev(Hs, dtype, gpu)
+    tWq, tWk = to_dev(Wq, dtype, gpu), to_dev(Wk, dtype, gpu)
+    tg = [f32_dev(x, gpu) for x in (g[0], bt[0], g[1], bt[1])]
+    Q, K = torch.empty_like(tHw), torch.empty_like(tHs)
+    sq, skv = torch.empty((M, 2), device=gpu), torch.empty((T, 2), device=gpu)
+    wb.whale_proj_qkv(dm, tHw, tHs, norm, 1e-5, *tg, tWq, tWk, None, Q, K, None, sq, skv, None, None)
+    dHw, dHs = torch.empty_like(tHw), torch.empty_like(tHs)
+    dWq, dWk = torch.empty((d, d), device=gpu), torch.empty((d, d), device=gpu)
+    dgb = [torch.empty(d, device=gpu) for _ in range(4)]
+    ws = torch.empty(wb.whale_proj_qkv_bwd_workspace_size(dm, wb._dtype_code(tHw)), dtype=torch.uint8, device=gpu)
+    wb.whale_proj_qkv_bwd(dm, tHw, tHs, norm, 1e-5, *tg, sq, skv, tWq, tWk, None, to_dev(dQ, dtype, gpu),
+                          to_dev(dK, dtype, gpu), None, None, dHw, dHs, dWq, dWk, None, *dgb, ws)
+    torch.cuda.synchronize()
+    assert_close("Q", Q, Q_ref, dtype)
+    assert_close("K", K, K_ref, dtype)
+    assert_close("dH_w", dHw, ref["dH_w"], dtype)
+    assert_close("dH_s", dHs, ref["dH_s"], dtype)
+    assert_close("dW_Q", dWq, ref["dW_Q"], dtype)
+    assert_close("dW_K", dWk, ref["dW_K"], dtype)
+    if norm != O.NORM_NONE:
+        assert_close("dg_kv", dgb[2], ref["dg_kv"], dtype)
+    if norm == O.NORM_LAYER:
         assert_close("db_kv", dgb[3], ref["db_kv"], dtype)

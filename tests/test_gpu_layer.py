@@ -29,10 +29,10 @@ def dev_params(p, dtype, gpu):
             for k, v in p.items()}
 
 
-def run_layers(cfg, gpu, requests=None, backward=False, dy_mask=None):
+def run_layers(cfg, gpu, requests=None, backward=False, dy_mask=None, tied=False):
     """Run cfg.layers stacked layers on the GPU for `requests` (all by default).
     Returns per-layer outputs (host fp64) and, if backward, the gradients of
-    the last layer."""
+    the last layer.  tied: shared key-value layers (no W_V)."""
     L = synth.lengths(cfg)
     reqs = list(range(cfg.B)) if requests is None else list(requests)
     H_w = synth.gather(cfg, lambda c, b: synth.h_w_rows(c, b, 0), reqs)
@@ -45,6 +45,8 @@ def run_layers(cfg, gpu, requests=None, backward=False, dy_mask=None):
         tHs = torch.from_numpy(H_s).to(gpu).to(tdt(cfg.dtype))
         del H_s
         p = dev_params(synth.layer_params(cfg, ell, random_affine=backward), cfg.dtype, gpu)
+        if tied:
+            del p["W_V"]
         layer = FusionLayer(p, cfg.C, cfg.n_q, cfg.h, ffn=cfg.ffn)
         out = layer.forward(x, tHs, toff, int(L[reqs].max()), save=backward)
         x = out["Y"]
@@ -62,7 +64,7 @@ def run_layers(cfg, gpu, requests=None, backward=False, dy_mask=None):
     return res, outs
 
 
-def oracle_layers(cfg, requests, backward=False):
+def oracle_layers(cfg, requests, backward=False, tied=False):
     L = synth.lengths(cfg)
     H_w = synth.gather(cfg, lambda c, b: synth.h_w_rows(c, b, 0), requests)
     off = synth.offsets_of(L[list(requests)])
@@ -70,6 +72,8 @@ def oracle_layers(cfg, requests, backward=False):
     for ell in range(cfg.layers):
         H_s = np.concatenate([synth.h_s_rows(cfg, b, L[b], ell) for b in requests])
         p = synth.layer_params(cfg, ell, random_affine=backward)
+        if tied:
+            del p["W_V"]
         if backward and ell == cfg.layers - 1:
             dY = np.concatenate([synth.dy_rows(cfg, b) for b in requests])
             g = O.layer_bwd(x, H_s, off, cfg.C, cfg.n_q, cfg.h, p, dY, ffn=cfg.ffn)
@@ -101,6 +105,20 @@ def test_config_reduced(gpu, key):
         for k in GRADS:
             assert_close(k, res["grads"][k], g_ref[k], cfg.dtype)
         for k in ("dg_q", "db_q", "dg_kv", "db_kv", "dg_f", "db_f"):
+            assert_close(k, res["grads"][k], g_ref[k], cfg.dtype)
+
+
+@pytest.mark.parametrize("key", ["c1", "c5"])
+def test_shared_kv_layer_reduced(gpu, key):
+    """Shared key-value layers: forward and every gradient against the oracle."""
+    cfg = synth.scaled(synth.CONFIGS[key], **REDUCED[key])
+    print(f"\n[shared kv layer] {cfg.name} B={cfg.B} L={synth.lengths(cfg).tolist()}", flush=True)
+    res, _ = run_layers(cfg, gpu, backward=True, tied=True)
+    y_ref, g_ref = oracle_layers(cfg, list(range(cfg.B)), backward=True, tied=True)
+    assert_close("Y", res["Y"], y_ref, cfg.dtype)
+    assert "dW_V" not in res["grads"] and "dW_V" not in g_ref
+    for k in GRADS + ("dg_q", "db_q", "dg_kv", "db_kv", "dg_f", "db_f"):
+        if k != "dW_V":
             assert_close(k, res["grads"][k], g_ref[k], cfg.dtype)
 
 

@@ -64,6 +64,15 @@ def test_host_validation_rejects_before_launch():
     # LayerNorm without its statistics buffer
     assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 0, 1e-5, fake, fake, fake, fake, fake, fake, fake, fake,
                               fake, fake, None, fake, None, None, None) == 1
+    # Shared key-value form: W_V and V must be NULL together; a NULL dV needs V == K
+    assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 2, 1e-5, None, None, None, None, fake, fake, None, fake,
+                              fake, fake, None, None, None, None, None) == 1
+    other = ctypes.c_void_p(512)
+    assert lib.whale_jagged_xattn_bwd(ctypes.byref(d), 1, fake, fake, other, fake, 0.0, fake, fake, fake, fake, fake,
+                                      None, fake, 1 << 30, None) == 2
+    assert lib.whale_proj_qkv_bwd(ctypes.byref(d), 1, fake, fake, 2, 1e-5, None, None, None, None, None, None, None,
+                                  None, fake, fake, None, fake, fake, fake, None, fake, fake, fake, fake, None, None,
+                                  None, None, None, fake, 1 << 30, None) == 1
 
 
 def test_workspace_sizes_are_host_only_and_monotone():
