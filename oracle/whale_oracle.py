@@ -57,6 +57,12 @@ reason in the design notes of the repository):
       whose output serves as both keys and values; the layer then has no
       W_V, and the gradient of that one tensor is the sum of its gradients
       in the two roles.  A layer whose parameters hold no W_V is tied.
+  R11 serving with a different number of candidates per request: request b
+      has C_b >= 0 candidates, given as prefix sums cand_offsets [B+1], and
+      owns query rows n_q*cand_offsets[b] .. n_q*cand_offsets[b+1]-1.  Each
+      of them attends the history of request b exactly as in Eq. (4); the
+      K/V of a request are the same whichever candidates query them
+      (Footnote 1, [PV ref]).
 
 Layouts (row-vector convention y = x W^T, weights stored [out, in]):
   H_w, Q, A, F, Y : [M, d] with M = B*C*n_q, row m = (b*C + c)*n_q + i
@@ -174,14 +180,18 @@ def proj_qkv_bwd(H_w, H_s, norm, eps, g_q, b_q, g_kv, b_kv, W_Q, W_K, W_V, dQ, d
 
 # ---------------------------------------------------------------- a3
 
-def _request_rows(b, C, n_q):
+def _request_rows(b, C, n_q, cand_offsets=None):
+    if cand_offsets is not None:                       # R11
+        return slice(n_q * int(cand_offsets[b]), n_q * int(cand_offsets[b + 1]))
     return slice(b * C * n_q, (b + 1) * C * n_q)
 
 
-def xattn_fwd(Q, K, V, offsets, C, n_q, h, scale=None):
+def xattn_fwd(Q, K, V, offsets, C, n_q, h, scale=None, cand_offsets=None):
     """Eq. (4): every interaction token of every candidate of request b
     attends, with an unmasked softmax over dot products, to the whole history
-    of request b [PV km], [PD 2], [GS 2.1].  Returns (A [M,d], lse [M,h])."""
+    of request b [PV km], [PD 2], [GS 2.1].  Returns (A [M,d], lse [M,h]).
+    cand_offsets [B+1] (R11) gives each request its own number of candidates;
+    C is then unused."""
     Q, K, V = _f64(Q), _f64(K), _f64(V)
     offsets = np.asarray(offsets, dtype=np.int64)
     B = len(offsets) - 1
@@ -192,7 +202,7 @@ def xattn_fwd(Q, K, V, offsets, C, n_q, h, scale=None):
     A = np.zeros((M, d))
     lse = np.full((M, h), -np.inf)
     for b in range(B):
-        rows = _request_rows(b, C, n_q)
+        rows = _request_rows(b, C, n_q, cand_offsets)
         lo, hi = offsets[b], offsets[b + 1]
         if hi == lo:
             continue                                   # R9

@@ -153,6 +153,36 @@ def test_candidate_independence():
             np.testing.assert_allclose(A1, A[rows], rtol=1e-13, atol=1e-14)
 
 
+def test_variable_candidates_match_sdpa_per_request():
+    """Serving form (a different candidate count per request, zero included):
+    every query row against torch's attention over its own request's history,
+    and the whole against per-request calls with a fixed count."""
+    n_q, d, h = 3, 8, 2
+    C_b = [2, 0, 5, 1]
+    L = [4, 6, 1, 3]
+    coff = np.concatenate([[0], np.cumsum(C_b)])
+    off = np.concatenate([[0], np.cumsum(L)])
+    M, T = n_q * int(coff[-1]), int(off[-1])
+    Q, K, V = rnd(41, M, d), rnd(42, T, d), rnd(43, T, d)
+    A, lse = O.xattn_fwd(Q, K, V, off, None, n_q, h, cand_offsets=coff)
+    dh = d // h
+    for b in range(len(C_b)):
+        rows = slice(n_q * coff[b], n_q * coff[b + 1])
+        lo, hi = off[b], off[b + 1]
+        for j in range(h):
+            cols = slice(j * dh, (j + 1) * dh)
+            q, k, v = t64(Q[rows, cols]), t64(K[lo:hi, cols]), t64(V[lo:hi, cols])
+            ref = TF.scaled_dot_product_attention(q[None], k[None], v[None])[0].numpy()
+            np.testing.assert_allclose(A[rows, cols], ref, rtol=1e-12, atol=1e-13)
+            s = (q @ k.T).numpy() / math.sqrt(dh)
+            np.testing.assert_allclose(lse[rows, j], torch.logsumexp(torch.tensor(s), 1).numpy(),
+                                       rtol=1e-13, atol=1e-13)
+        if C_b[b]:
+            A1, l1 = O.xattn_fwd(Q[rows], K[lo:hi], V[lo:hi], [0, hi - lo], C_b[b], n_q, h)
+            np.testing.assert_array_equal(A1, A[rows])
+            np.testing.assert_array_equal(l1, lse[rows])
+
+
 def test_empty_history():
     c = small_case(seed=19, lengths=(4, 0, 3))
     A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
