@@ -37,12 +37,16 @@ XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_pp_kernel<64>",
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 
-def flops(cfg, T, H, gate_sep=False, shared_kv=False):
+def flops(cfg, T, H, gate_sep=False, shared_kv=False, M=None, pairs=None):
     """Algorithmic FLOPs of one layer (forward, backward) for T history rows.
-    With shared keys and values the history side has one projection, not two."""
-    M, d, QR = cfg.M, cfg.d, cfg.C * cfg.n_q
+    With shared keys and values the history side has one projection, not two.
+    M (query rows) and pairs (query row, history row of the same request)
+    default to the fixed-count layout: B*C*n_q and C*n_q*T."""
+    d = cfg.d
+    M = cfg.M if M is None else M
+    pairs = cfg.C * cfg.n_q * T if pairs is None else pairs
     Hu = 2 * H if gate_sep else H
-    attn_f = 4.0 * QR * d * T
+    attn_f = 4.0 * d * pairs
     kv_f = (2.0 if shared_kv else 4.0) * T * d * d
     gemm_f = 2.0 * M * d * d + kv_f + 2.0 * M * 2 * d * d + 2.0 * M * d * Hu + 2.0 * M * H * d
     return {"attn_fwd": attn_f, "gemm_fwd": gemm_f, "fwd": attn_f + gemm_f,
@@ -81,6 +85,8 @@ def main():
     ap.add_argument("--cpu-requests", type=int, default=4)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--fwd-only", action="store_true", help="time the forward only")
+    ap.add_argument("--serving", action="store_true",
+                    help="forward only, each request with its own candidate count C_b ~ U{16..112} (mean 64)")
     ap.add_argument("--shared-kv", action="store_true",
                     help="shared key-value layer: one history-side projection whose output serves as K and V")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -119,6 +125,16 @@ def main():
           for k, v in p.items()}
     lay = FusionLayer(tp, cfg.C, cfg.n_q, cfg.h)
     max_L = int(L.max())
+    fwd_kw = {"save": not args.fwd_only}
+    if args.serving:
+        # Serving: forward only; request b scores C_b candidates against its
+        # one history (K/V formed once per request).
+        args.fwd_only = True
+        Cb = synth.candidate_counts(cfg, 16, 112)
+        tHw = torch.from_numpy(np.concatenate([synth.h_w_rows_n(cfg, b, int(Cb[b])) for b in range(cfg.B)])).to(
+            dev).to(bf)
+        fwd_kw = {"save": False, "cand_offsets": torch.from_numpy(synth.offsets_of(Cb)).to(dev),
+                  "max_C": int(Cb.max())}
 
     calls = ["proj_qkv", "xattn_fwd", "fusion_mlp", "swiglu_ffn", "ffn_bwd", "fusion_bwd", "xattn_bwd", "proj_bwd"]
 
@@ -136,7 +152,7 @@ def main():
     def step(tm=None):
         # forward, call by call (same sequence as FusionLayer.forward/backward)
         if tm: tm.mark("start")
-        out = lay.forward(tHw, tHs, toff, max_L, save=True)
+        out = lay.forward(tHw, tHs, toff, max_L, **fwd_kw)
         if tm: tm.mark("fwd_end")
         if not args.fwd_only:
             lay.backward(tdY)
@@ -146,7 +162,8 @@ def main():
     # Per-call timing uses a wrapped binding: record an event after every call.
     per_call = {c: [] for c in calls}
     orig = {}
-    names = {"whale_proj_qkv": "proj_qkv", "whale_jagged_xattn_fwd": "xattn_fwd", "whale_fusion_mlp": "fusion_mlp",
+    names = {"whale_proj_qkv": "proj_qkv", "whale_jagged_xattn_fwd": "xattn_fwd",
+             "whale_jagged_xattn_fwd_varc": "xattn_fwd", "whale_fusion_mlp": "fusion_mlp",
              "whale_swiglu_ffn": "swiglu_ffn", "whale_swiglu_ffn_bwd": "ffn_bwd",
              "whale_fusion_mlp_bwd": "fusion_bwd", "whale_jagged_xattn_bwd": "xattn_bwd",
              "whale_proj_qkv_bwd": "proj_bwd"}
@@ -198,7 +215,10 @@ def main():
         per_call[n].append(e0.elapsed_time(e1))
     avg = {n: float(np.mean(v)) for n, v in per_call.items() if v}
 
-    f = flops(cfg, T, cfg.H, shared_kv=args.shared_kv)
+    if args.serving:
+        f = flops(cfg, T, cfg.H, shared_kv=args.shared_kv, M=int(tHw.shape[0]), pairs=cfg.n_q * float(np.dot(Cb, L)))
+    else:
+        f = flops(cfg, T, cfg.H, shared_kv=args.shared_kv)
     step_flops = f["fwd"] + (0.0 if args.fwd_only else f["bwd"])
     fwd_ms = sum(avg[c] for c in ("proj_qkv", "xattn_fwd", "fusion_mlp", "swiglu_ffn"))
     value = step_flops / (ms * 1e-3) / 1e12
@@ -209,9 +229,11 @@ def main():
     kname = "xattn_fwd_pp_kernel<64>"
     tr = XATTN_FWD_TRAFFIC
     traffic = None
-    if tr is not None and tr["kernel"] == kname and not args.shared_kv:
+    if tr is not None and tr["kernel"] == kname and not (args.shared_kv or args.serving):
         traffic = int(1024 * (tr["fetch_kib"] * tr["fetch_scale"] + tr["write_kib"] * tr["write_scale"]))
     M, d = cfg.M, cfg.d
+    if args.serving:
+        M = int(tHw.shape[0])
     algo_bytes = 2 * (M * d + (1 if args.shared_kv else 2) * T * d + M * d) + 4 * M * cfg.h
     roof = {"bound": "mfma", "kernel": kname, "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
@@ -221,7 +243,8 @@ def main():
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "fusion layer fwd+bwd" if not args.fwd_only else "fusion layer fwd",
+        "config": {"workload": ("fusion layer fwd, serving, C_b ~ U{16..112}" if args.serving else
+                                "fusion layer fwd+bwd" if not args.fwd_only else "fusion layer fwd"),
                    "B": cfg.B, "C": cfg.C, "n_q": cfg.n_q, "d": cfg.d, "h": cfg.h, "H": cfg.H, "L_b": int(L[0]),
                    "T": T, "gate": "shared", "norm": "layer", "kv": "shared" if args.shared_kv else "separate"},
         "requests_per_s": round(cfg.B / (ms * 1e-3), 1),

@@ -23,7 +23,7 @@ STATUS = ["WHALE_OK", "WHALE_ERR_NULL", "WHALE_ERR_SHAPE", "WHALE_ERR_DTYPE", "W
 # Every symbol declared in include/whalefuse.h.
 EXPORTS = [
     "whale_status_string", "whale_version",
-    "whale_proj_qkv", "whale_jagged_xattn_fwd", "whale_fusion_mlp",
+    "whale_proj_qkv", "whale_jagged_xattn_fwd", "whale_jagged_xattn_fwd_varc", "whale_fusion_mlp",
     "whale_swiglu_ffn_workspace_size", "whale_swiglu_ffn",
     "whale_jagged_xattn_bwd_workspace_size", "whale_jagged_xattn_bwd",
     "whale_fusion_mlp_bwd_workspace_size", "whale_fusion_mlp_bwd",
@@ -50,6 +50,7 @@ _SIGS = {
     "whale_version": (ctypes.c_char_p, []),
     "whale_proj_qkv": (_I, [_D, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "whale_jagged_xattn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P]),
+    "whale_jagged_xattn_fwd_varc": (_I, [_D, _I, _P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_fusion_mlp": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P]),
     "whale_swiglu_ffn_workspace_size": (_S, [_D, _I, _I, ctypes.c_int32]),
     "whale_swiglu_ffn": (_I, [_D, _I, _P, _I, _F, _P, _P, _P, _I, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _S, _P]),
@@ -140,6 +141,13 @@ def whale_jagged_xattn_fwd(d_, Q, K, V, offsets, scale, A, lse, stream=None):
     rc = load().whale_jagged_xattn_fwd(ctypes.byref(d_), _dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), _ptr(offsets),
                                        float(scale), _ptr(A), _ptr(lse), _stream(stream))
     _check("whale_jagged_xattn_fwd", rc)
+
+
+def whale_jagged_xattn_fwd_varc(d_, Q, K, V, offsets, cand_offsets, scale, A, lse, stream=None):
+    rc = load().whale_jagged_xattn_fwd_varc(ctypes.byref(d_), _dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V),
+                                            _ptr(offsets), _ptr(cand_offsets), float(scale), _ptr(A), _ptr(lse),
+                                            _stream(stream))
+    _check("whale_jagged_xattn_fwd_varc", rc)
 
 
 def whale_fusion_mlp(d_, A, H_w, W_F, act, F, Z_saved, stream=None):

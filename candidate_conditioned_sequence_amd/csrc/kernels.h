@@ -7,8 +7,12 @@
 struct XattnArgs {
   const void* Q; const void* K; const void* V; const int64_t* offsets;
   void* A; float* lse;
-  int B, QR /* C*n_q */, d, h, dh;
+  int B, QR /* C*n_q (the largest over requests with cand_offsets) */, d, h, dh;
   float scale;
+  // Optional candidate offsets [B+1]: request b owns query rows
+  // n_q*cand_offsets[b] .. n_q*cand_offsets[b+1]-1 (nullptr: b*QR .. (b+1)*QR-1).
+  const int64_t* cand_offsets;
+  int n_q;
 };
 hipError_t launch_xattn_fwd(const XattnArgs& a, bool bf16_data, hipStream_t st);
 

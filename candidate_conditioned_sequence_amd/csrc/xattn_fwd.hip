@@ -71,7 +71,7 @@ template <typename T, int DH, int QPW, int kNW>
 __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, T* __restrict__ A, float* __restrict__ lse,
-    int d, int h, int QR, int nqb, float c, int nblocks) {
+    int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q) {
   using TT = FwdTile<T, DH, kNW>;
   constexpr int NQ = QPW / 32, KS = DH / 16, NE = DH / 32, QB = kNW * QPW;
   constexpr int KLD = TT::KLD, CPR = TT::CPR, NCH = TT::NCH;
@@ -86,7 +86,12 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
-  const int64_t qrow0 = (int64_t)b * QR;
+  // Query rows of request b: C*n_q of them, or n_q per candidate from the
+  // candidate offsets when requests carry different numbers of candidates.
+  const int64_t c0 = coffs ? coffs[b] : 0;
+  const int64_t qrow0 = coffs ? c0 * n_q : (int64_t)b * QR;
+  const int QRb = coffs ? (int)((coffs[b + 1] - c0) * n_q) : QR;
+  if (qbi * QB >= QRb) return;                 // the whole block is past them (uniform)
   const int qbase = qbi * QB + w * QPW;
 
   // Q fragments: B operand of S^T = K Q^T, lane = query column.
@@ -97,7 +102,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     const T* src = Q + (qrow0 + q) * d + j * DH + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[qb][ks] = (q < QR) ? ld8<T>(src + 16 * ks) : zero8<T>();
+      qf[qb][ks] = (q < QRb) ? ld8<T>(src + 16 * ks) : zero8<T>();
       if (kFold) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) qf[qb][ks][u] = from_f<T>(to_f(qf[qb][ks][u]) * c);
@@ -296,7 +301,7 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     const int q = qbase + 32 * qb + l32;
     const float ltot = half_sum((lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]));
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (q < QR) {
+    if (q < QRb) {
       T* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
 #pragma unroll
       for (int e = 0; e < NE; ++e)
@@ -349,7 +354,7 @@ template <int DH>
 __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const int64_t* __restrict__ offsets, bf16* __restrict__ A, float* __restrict__ lse,
-    int d, int h, int QR, int nqb, float c, int nblocks) {
+    int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q) {
   constexpr int NQ = kPPQ / 32, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8;
   constexpr int NCH = kBN * CPR / (4 * 64);      // chunks per thread of one tensor (4 waves per tensor)
@@ -371,7 +376,11 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int grp = wv >> 2;                                // 0 = A, 1 = B
   const int gtid = tid & 255;                             // thread index within the group
-  const int64_t qrow0 = (int64_t)b * QR;
+  // Query rows of request b (see xattn_fwd_kernel).
+  const int64_t c0 = coffs ? coffs[b] : 0;
+  const int64_t qrow0 = coffs ? c0 * n_q : (int64_t)b * QR;
+  const int QRb = coffs ? (int)((coffs[b + 1] - c0) * n_q) : QR;
+  if (qbi * kPPQB >= QRb) return;              // the whole block is past them (uniform)
   const int qbase = qbi * kPPQB + wv * kPPQ;
 
   bf16x8 qf[NQ][KS];
@@ -381,7 +390,7 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     const bf16* src = Q + (qrow0 + q) * d + j * DH + 8 * hh;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      qf[qb][ks] = (q < QR) ? ld8<bf16>(src + 16 * ks) : zero8<bf16>();
+      qf[qb][ks] = (q < QRb) ? ld8<bf16>(src + 16 * ks) : zero8<bf16>();
 #pragma unroll
       for (int u = 0; u < 8; ++u) qf[qb][ks][u] = (bf16)((float)qf[qb][ks][u] * c);
     }
@@ -584,7 +593,7 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     const int q = qbase + 32 * qb + l32;
     const float ltot = half_sum((lsum[qb][0] + lsum[qb][1]) + (lsum[qb][2] + lsum[qb][3]));
     const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
-    if (q < QR) {
+    if (q < QRb) {
       bf16* dst = A + (qrow0 + q) * d + j * DH + 4 * hh;
 #pragma unroll
       for (int e = 0; e < NE; ++e)
@@ -609,7 +618,7 @@ hipError_t launch_fwd_pp(const XattnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((xattn_fwd_pp_kernel<DH>), dim3((unsigned)nblk), dim3(kPPW * 64), 0, st,
                      (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.offsets, (bf16*)a.A, a.lse,
-                     a.d, a.h, a.QR, nqb, c, (int)nblk);
+                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q);
   return hipGetLastError();
 }
 
@@ -622,7 +631,7 @@ hipError_t launch_fwd_t(const XattnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((xattn_fwd_kernel<T, DH, QPW, kNW>), dim3((unsigned)nblk), dim3(kNW * 64), 0, st,
                      (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (T*)a.A, a.lse,
-                     a.d, a.h, a.QR, nqb, c, (int)nblk);
+                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q);
   return hipGetLastError();
 }
 

@@ -39,10 +39,21 @@ class FusionLayer:
         B = H_w.shape[0] // (self.C * self.n_q)
         return wb.dims(B, self.C, self.n_q, self.d, self.h, max_L, total_L)
 
-    def forward(self, H_w, H_s, offsets, max_L, save=True, stream=None):
+    def forward(self, H_w, H_s, offsets, max_L, save=True, stream=None, cand_offsets=None, max_C=None):
+        """cand_offsets (device int64 [B+1]) with its host hint max_C: the
+        serving form, request b having cand_offsets[b+1] - cand_offsets[b]
+        candidates (forward only).  The row-wise calls then see the query
+        rows as one batch and only the attention call sees the requests."""
         p, dev, dt = self.p, H_w.device, H_w.dtype
         M, T, d = H_w.shape[0], H_s.shape[0], self.d
-        dm = self.dims(H_w, max_L, T)
+        if cand_offsets is not None:
+            if save:
+                raise ValueError("the form with candidate offsets is forward only (save=False)")
+            B = offsets.shape[0] - 1
+            dm = wb.dims(1, M // self.n_q, self.n_q, d, self.h, T, T)
+            dm_att = wb.dims(B, max_C, self.n_q, d, self.h, max_L, T)
+        else:
+            dm = dm_att = self.dims(H_w, max_L, T)
         nn = self.norm != wb.NORM_NONE
         Q, K = _empty((M, d), dt, dev), _empty((T, d), dt, dev)
         V = None if self.tied_kv else _empty((T, d), dt, dev)
@@ -58,7 +69,10 @@ class FusionLayer:
         if self.tied_kv:
             V = K
         A, lse = _empty((M, d), dt, dev), _empty((M, self.h), torch.float32, dev)
-        wb.whale_jagged_xattn_fwd(dm, Q, K, V, offsets, self.scale, A, lse, stream)
+        if cand_offsets is not None:
+            wb.whale_jagged_xattn_fwd_varc(dm_att, Q, K, V, offsets, cand_offsets, self.scale, A, lse, stream)
+        else:
+            wb.whale_jagged_xattn_fwd(dm, Q, K, V, offsets, self.scale, A, lse, stream)
         F = _empty((M, d), dt, dev)
         Z = _empty((M, d), dt, dev) if (save and self.act == wb.ACT_SILU) else None
         wb.whale_fusion_mlp(dm, A, H_w, p["W_F"], self.act, F, Z, stream)

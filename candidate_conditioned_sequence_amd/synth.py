@@ -18,7 +18,7 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 # tensor ids for the seed key
-T_LEN, T_HW, T_HS, T_DY = 0, 1, 2, 3
+T_LEN, T_HW, T_HS, T_DY, T_CAND = 0, 1, 2, 3, 4
 T_WQ, T_WK, T_WV, T_WF, T_WU, T_WG, T_WD = 10, 11, 12, 13, 14, 15, 16
 T_GQ, T_BQ, T_GKV, T_BKV, T_GF, T_BF = 20, 21, 22, 23, 24, 25
 
@@ -129,6 +129,17 @@ def h_w_rows(cfg, b, layer=0):
     """H_w rows of request b: [C*n_q, d], N(0,1)."""
     r = _rng(cfg, layer, T_HW, b)
     return quantize(cfg, r.standard_normal((cfg.C * cfg.n_q, cfg.d), dtype=np.float32))
+
+
+def candidate_counts(cfg, lo, hi):
+    """Serving form: a candidate count per request, uniform in [lo, hi] (int64 [B])."""
+    return _rng(cfg, 0, T_CAND).integers(lo, hi + 1, size=cfg.B, dtype=np.int64)
+
+
+def h_w_rows_n(cfg, b, n_cand, layer=0):
+    """H_w rows of request b with n_cand candidates: [n_cand*n_q, d], N(0,1)."""
+    r = _rng(cfg, layer, T_HW, b)
+    return quantize(cfg, r.standard_normal((n_cand * cfg.n_q, cfg.d), dtype=np.float32))
 
 
 def h_s_rows(cfg, b, L_b, layer=0):

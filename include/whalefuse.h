@@ -151,6 +151,25 @@ whale_status_t whale_jagged_xattn_fwd(const whale_dims_t* dims, whale_dtype_t dt
                                       void* A, float* lse, hipStream_t stream);
 
 /*
+ * a3 for serving, with a different number of candidates per request
+ * ([PV ref] major comment on §5.1 / Footnote 1: K/V are formed once per
+ * request and amortised over however many candidates it scores).
+ * cand_offsets (device int64 [B+1], cand_offsets[0] = 0, non-decreasing)
+ * gives request b the C_b = cand_offsets[b+1] - cand_offsets[b] >= 0
+ * candidates whose query rows are n_q*cand_offsets[b] .. n_q*cand_offsets[b+1]-1
+ * of Q, A and lse ([n_q*cand_offsets[B], d] and [.., h]).  dims->C is a
+ * host shape hint: the largest C_b (the caller guarantees every C_b <=
+ * dims->C; rows of a larger request past it are not written).  Otherwise as
+ * whale_jagged_xattn_fwd: the same kernels, each row attending its own
+ * request's history.  A request with C_b = 0 has no rows; micro-batches of
+ * one request's candidates can each be run against the same K/V.
+ */
+whale_status_t whale_jagged_xattn_fwd_varc(const whale_dims_t* dims, whale_dtype_t dtype,
+                                           const void* Q, const void* K, const void* V,
+                                           const int64_t* offsets, const int64_t* cand_offsets,
+                                           float scale, void* A, float* lse, hipStream_t stream);
+
+/*
  * a4, Eq. (5): F = H_w + act([A, H_w] W_F^T): one linear layer from the
  * concatenation (attended vector first) to d, plus the residual
  * ([GS 2.1]; [PV ref] minor comment on Eq. (5); [PV km]).  act is SiLU or

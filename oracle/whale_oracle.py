@@ -320,15 +320,16 @@ def swiglu_ffn_bwd(F, norm, eps, g_f, b_f, W_U, gate, W_D, dY):
 # ---------------------------------------------------------------- whole layer
 
 def layer_fwd(H_w, H_s, offsets, C, n_q, h, p, norm=NORM_LAYER, eps=1e-5,
-              act=ACT_SILU, gate=GATE_SHARED, ffn=True, scale=None):
+              act=ACT_SILU, gate=GATE_SHARED, ffn=True, scale=None, cand_offsets=None):
     """One fusion layer: a1..a5 in order [GS 2.1].  `p` holds W_Q, W_K, W_V,
     W_F, W_U, W_D and the norm parameters g_q, b_q, g_kv, b_kv, g_f, b_f;
-    without W_V the layer shares one tensor as keys and values (R10).
+    without W_V the layer shares one tensor as keys and values (R10), and
+    with cand_offsets each request has its own number of candidates (R11).
     Returns a dict with every intermediate; 'Y' is the layer output (F when
     ffn is False)."""
     Q, K, V = proj_qkv(H_w, H_s, norm, eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"],
                        p["W_Q"], p["W_K"], p.get("W_V"))
-    A, lse = xattn_fwd(Q, K, V, offsets, C, n_q, h, scale)
+    A, lse = xattn_fwd(Q, K, V, offsets, C, n_q, h, scale, cand_offsets)
     F, Z = fusion_mlp(A, H_w, p["W_F"], act)
     out = {"Q": Q, "K": K, "V": V, "A": A, "lse": lse, "F": F, "Z": Z}
     if ffn:

@@ -413,3 +413,54 @@ def test_proj_qkv_shared_kv(gpu, dtype, norm, d, L):
         assert_close("dg_kv", dgb[2], ref["dg_kv"], dtype)
     if norm == O.NORM_LAYER:
         assert_close("db_kv", dgb[3], ref["db_kv"], dtype)
+
+
+# Serving form: a different number of candidates per request (zero included).
+# The first case runs the ping-pong kernel (largest C_b * n_q >= 1024) with
+# requests whose query count is not a multiple of its 512-query blocks; the
+# others run the general kernel.
+VARC_CASES = [
+    ("bf16", 256, 4, 32, [64, 0, 17, 40, 1], [900, 50, 0, 1300, 257]),
+    ("bf16", 128, 4, 16, [16, 3, 0, 9], [300, 1, 65, 0]),
+    ("f32", 64, 2, 8, [3, 0, 5, 1], [100, 7, 0, 65]),
+]
+
+
+@pytest.mark.parametrize("case", VARC_CASES, ids=lambda c: f"{c[0]}-d{c[1]}h{c[2]}-nq{c[3]}-B{len(c[4])}")
+def test_xattn_fwd_varc(gpu, case):
+    dtype, d, h, n_q, C_b, L = case
+    print(f"\n[xattn_fwd_varc] {case}", flush=True)
+    B = len(L)
+    coff, off = offsets(C_b), offsets(L)
+    M, T = n_q * int(coff[-1]), int(off[-1])
+    Q, K, V = draw(91, (M, d), dtype), draw(92, (T, d), dtype), draw(93, (T, d), dtype)
+    A_ref, lse_ref = O.xattn_fwd(Q, K, V, off, None, n_q, h, cand_offsets=coff)
+    dm = wb.dims(B, max(C_b), n_q, d, h, max(L), T)
+    tQ, tK, tV = (to_dev(x, dtype, gpu) for x in (Q, K, V))
+    A, lse = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    wb.whale_jagged_xattn_fwd_varc(dm, tQ, tK, tV, i64_dev(off, gpu), i64_dev(coff, gpu), 0.0, A, lse)
+    torch.cuda.synchronize()
+    assert_close("A", A, A_ref, dtype)
+    fin = np.isfinite(lse_ref)
+    got = host(lse)
+    assert np.array_equal(np.isfinite(got), fin)
+    assert_close("lse", got[fin], lse_ref[fin], "f32" if dtype == "f32" else "bf16")
+
+
+def test_xattn_fwd_varc_equal_counts_match_fixed_call_bitwise(gpu):
+    """With every C_b = C the serving form runs the same arithmetic as the
+    fixed-count call: identical bits."""
+    d, h, n_q, C, L = 256, 4, 32, 48, [700, 1, 333]
+    B = len(L)
+    off = offsets(L)
+    M, T = B * C * n_q, int(off[-1])
+    Q, K, V = draw(94, (M, d), "bf16"), draw(95, (T, d), "bf16"), draw(96, (T, d), "bf16")
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tQ, tK, tV = (to_dev(x, "bf16", gpu) for x in (Q, K, V))
+    toff = i64_dev(off, gpu)
+    A0, l0 = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    A1, l1 = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    wb.whale_jagged_xattn_fwd(dm, tQ, tK, tV, toff, 0.0, A0, l0)
+    wb.whale_jagged_xattn_fwd_varc(dm, tQ, tK, tV, toff, i64_dev(offsets([C] * B), gpu), 0.0, A1, l1)
+    torch.cuda.synchronize()
+    assert torch.equal(A0, A1) and torch.equal(l0, l1)

@@ -122,6 +122,29 @@ def test_shared_kv_layer_reduced(gpu, key):
             assert_close(k, res["grads"][k], g_ref[k], cfg.dtype)
 
 
+def test_serving_layer_variable_candidates(gpu):
+    """Serving forward with a different number of candidates per request (one
+    with none, one with an empty history): the row-wise calls see all query
+    rows as one batch, the attention call the candidate offsets."""
+    cfg = synth.scaled(synth.CONFIGS["c3"], B=5)
+    C_b, L = [64, 5, 0, 33, 2], [3000, 200, 100, 1500, 0]
+    coff, off = synth.offsets_of(C_b), synth.offsets_of(L)
+    n_q, d = cfg.n_q, cfg.d
+    M, T = n_q * int(coff[-1]), int(off[-1])
+    r = np.random.default_rng(51)
+    H_w = synth.round_bf16(r.standard_normal((M, d)).astype(np.float32))
+    H_s = synth.round_bf16(r.standard_normal((T, d)).astype(np.float32))
+    p = synth.layer_params(cfg)
+    print(f"\n[serving layer] C_b={C_b} L={L}", flush=True)
+    layer = FusionLayer(dev_params(p, cfg.dtype, gpu), cfg.C, n_q, cfg.h, ffn=cfg.ffn)
+    out = layer.forward(torch.from_numpy(H_w).to(gpu).to(torch.bfloat16),
+                        torch.from_numpy(H_s).to(gpu).to(torch.bfloat16), torch.from_numpy(off).to(gpu), max(L),
+                        save=False, cand_offsets=torch.from_numpy(coff).to(gpu), max_C=max(C_b))
+    torch.cuda.synchronize()
+    y_ref = O.layer_fwd(H_w, H_s, off, None, n_q, cfg.h, p, ffn=cfg.ffn, cand_offsets=coff)["Y"]
+    assert_close("Y", out["Y"], y_ref, cfg.dtype)
+
+
 def _rows(cfg, L, reqs, sample):
     """Row slices of the sampled requests inside the full-size layout."""
     per = cfg.C * cfg.n_q

@@ -183,6 +183,24 @@ def test_variable_candidates_match_sdpa_per_request():
             np.testing.assert_array_equal(l1, lse[rows])
 
 
+def test_variable_candidates_layer_is_per_request_layers():
+    """A layer with a different candidate count per request equals the same
+    layer run request by request with that request's fixed count."""
+    C_b, L = [3, 1, 0, 2], [4, 2, 3, 5]
+    coff = np.concatenate([[0], np.cumsum(C_b)])
+    x, p, _, kw = _layer_case(43, lengths=L)
+    n_q, h, off = kw["n_q"], kw["h"], kw["offsets"]
+    r = np.random.default_rng(44)
+    H_w = r.standard_normal((n_q * int(coff[-1]), x["H_w"].shape[1]))
+    Y = O.layer_fwd(H_w, x["H_s"], off, None, n_q, h, p, cand_offsets=coff)["Y"]
+    for b in range(len(C_b)):
+        if C_b[b] == 0:
+            continue
+        rows = slice(n_q * coff[b], n_q * coff[b + 1])
+        Y1 = O.layer_fwd(H_w[rows], x["H_s"][off[b]:off[b + 1]], [0, L[b]], C_b[b], n_q, h, p)["Y"]
+        np.testing.assert_allclose(Y[rows], Y1, rtol=1e-12, atol=1e-12)
+
+
 def test_empty_history():
     c = small_case(seed=19, lengths=(4, 0, 3))
     A, lse = O.xattn_fwd(c["Q"], c["K"], c["V"], c["off"], c["C"], c["n_q"], c["h"])
