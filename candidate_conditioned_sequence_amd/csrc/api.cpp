@@ -209,9 +209,14 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
   return WHALE_OK;
 }
 
-whale_status_t whale_jagged_xattn_fwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
-                                      const void* V, const int64_t* offsets, float scale, void* A, float* lse,
-                                      hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Both forward attention calls: cand_offsets null for C candidates per request.
+whale_status_t xattn_fwd_call(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                              const void* V, const int64_t* offsets, const int64_t* cand_offsets, float scale,
+                              void* A, float* lse, hipStream_t stream) {
   Shape s;
   whale_status_t rc = check_dims(dims, dtype, &s);
   if (rc != WHALE_OK) return rc;
@@ -222,26 +227,26 @@ whale_status_t whale_jagged_xattn_fwd(const whale_dims_t* dims, whale_dtype_t dt
   a.Q = Q; a.K = K; a.V = V; a.offsets = offsets; a.A = A; a.lse = lse;
   a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
-  a.cand_offsets = nullptr; a.n_q = s.n_q;
+  a.cand_offsets = cand_offsets; a.n_q = s.n_q;
   return ret(launch_xattn_fwd(a, dtype == WHALE_BF16, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+whale_status_t whale_jagged_xattn_fwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                                      const void* V, const int64_t* offsets, float scale, void* A, float* lse,
+                                      hipStream_t stream) {
+  return xattn_fwd_call(dims, dtype, Q, K, V, offsets, nullptr, scale, A, lse, stream);
 }
 
 whale_status_t whale_jagged_xattn_fwd_varc(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q,
                                            const void* K, const void* V, const int64_t* offsets,
                                            const int64_t* cand_offsets, float scale, void* A, float* lse,
                                            hipStream_t stream) {
-  Shape s;
-  whale_status_t rc = check_dims(dims, dtype, &s);
-  if (rc != WHALE_OK) return rc;
-  if (!Q || !A || !offsets || !cand_offsets) return WHALE_ERR_NULL;
-  if (s.T > 0 && (!K || !V)) return WHALE_ERR_NULL;
-  if (!(scale >= 0.f) || !std::isfinite(scale)) return WHALE_ERR_SHAPE;
-  XattnArgs a;
-  a.Q = Q; a.K = K; a.V = V; a.offsets = offsets; a.A = A; a.lse = lse;
-  a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh;
-  a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
-  a.cand_offsets = cand_offsets; a.n_q = s.n_q;
-  return ret(launch_xattn_fwd(a, dtype == WHALE_BF16, stream));
+  if (!cand_offsets) return WHALE_ERR_NULL;
+  return xattn_fwd_call(dims, dtype, Q, K, V, offsets, cand_offsets, scale, A, lse, stream);
 }
 
 whale_status_t whale_fusion_mlp(const whale_dims_t* dims, whale_dtype_t dtype, const void* A, const void* H_w,
