@@ -145,6 +145,43 @@ def test_serving_layer_variable_candidates(gpu):
     assert_close("Y", out["Y"], y_ref, cfg.dtype)
 
 
+def test_serving_forward_graph_capture(gpu):
+    """The serving forward (candidate offsets, host shape hints) captured in a
+    HIP graph: every replay, with eager work between replays, gives the eager
+    result bit for bit."""
+    cfg = synth.scaled(synth.CONFIGS["c3"], B=4)
+    C_b, L = [40, 0, 17, 64], [900, 30, 0, 1500]
+    coff, off = synth.offsets_of(C_b), synth.offsets_of(L)
+    n_q, d = cfg.n_q, cfg.d
+    M, T = n_q * int(coff[-1]), int(off[-1])
+    r = np.random.default_rng(61)
+    tHw = torch.from_numpy(synth.round_bf16(r.standard_normal((M, d)).astype(np.float32))).to(gpu).to(torch.bfloat16)
+    tHs = torch.from_numpy(synth.round_bf16(r.standard_normal((T, d)).astype(np.float32))).to(gpu).to(torch.bfloat16)
+    toff, tcoff = torch.from_numpy(off).to(gpu), torch.from_numpy(coff).to(gpu)
+    layer = FusionLayer(dev_params(synth.layer_params(cfg), cfg.dtype, gpu), cfg.C, n_q, cfg.h, ffn=cfg.ffn)
+
+    def fwd():
+        return layer.forward(tHw, tHs, toff, max(L), save=False, cand_offsets=tcoff, max_C=max(C_b))["Y"]
+
+    print(f"\n[serving graph capture] C_b={C_b} L={L}", flush=True)
+    eager = fwd().clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fwd()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        y = fwd()
+    for _ in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager)
+        assert torch.equal(fwd(), eager)
+        torch.cuda.synchronize()
+
+
 def _rows(cfg, L, reqs, sample):
     """Row slices of the sampled requests inside the full-size layout."""
     per = cfg.C * cfg.n_q
