@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0
 # from profiles/xattn_fwd_pp_kernel_c3_L10k_hbm_traffic.md; must be re-measured
 # (or set to None) whenever that kernel changes.
 XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_pp_kernel<64>",
-                     "fetch_kib": 709742, "fetch_scale": 2.000, "write_kib": 144115, "write_scale": 1.000}
+                     "fetch_kib": 706662, "fetch_scale": 2.000, "write_kib": 140220, "write_scale": 1.000}
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 
