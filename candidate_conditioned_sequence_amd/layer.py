@@ -49,6 +49,9 @@ class FusionLayer:
         if cand_offsets is not None:
             if save:
                 raise ValueError("the form with candidate offsets is forward only (save=False)")
+            if max_C is None or M % self.n_q != 0 or cand_offsets.shape != offsets.shape:
+                raise ValueError("candidate offsets need max_C, n_q rows per candidate and one entry per "
+                                 "history offset")
             B = offsets.shape[0] - 1
             dm = wb.dims(1, M // self.n_q, self.n_q, d, self.h, T, T)
             dm_att = wb.dims(B, max_C, self.n_q, d, self.h, max_L, T)
