@@ -53,6 +53,24 @@ def flops(cfg, T, H, gate_sep=False, shared_kv=False, M=None, pairs=None):
             "attn_bwd": 2.5 * attn_f, "gemm_bwd": 2.0 * gemm_f, "bwd": 2.5 * attn_f + 2.0 * gemm_f}
 
 
+def mfma_probe(torch, wb, dev, blocks=2048, iters=2000, reps=5):
+    """bf16 MFMA rate the GPU sustains with no memory traffic (TFLOP/s, best
+    of `reps` launches): 8 waves per SIMD of four independent MFMA chains."""
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    wb.whale_mfma_peak_probe(out, iters, blocks)
+    torch.cuda.synchronize()
+    flop = float(blocks) * 4 * iters * 4 * 32 * 32 * 16 * 2
+    best = 0.0
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        wb.whale_mfma_peak_probe(out, iters, blocks)
+        e1.record()
+        torch.cuda.synchronize()
+        best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    return {"tflops": round(best, 1), "blocks": blocks, "iters": iters, "kernel": "mfma_peak_kernel"}
+
+
 def cpu_baseline(cfg, p, L, n_req, shared_kv=False):
     """fp64 oracle, forward + backward of the first n_req requests."""
     from candidate_conditioned_sequence_amd import synth
@@ -105,6 +123,7 @@ def main():
 
     wb.load()
     dev = torch.device("cuda:0")
+    probe = mfma_probe(torch, wb, dev)
     cfg = synth.CONFIGS["c3L10k"]
     L = synth.lengths(cfg)
     T = int(L.sum())
@@ -238,7 +257,8 @@ def main():
     roof = {"bound": "mfma", "kernel": kname, "achieved": round(attn_tflops, 1),
             "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic, "traffic_unit": "bytes per launch", "algorithmic_bytes": algo_bytes,
-            "algorithmic_flops": f["attn_fwd"]}
+            "algorithmic_flops": f["attn_fwd"],
+            "measured_peak": probe["tflops"], "frac_of_measured_peak": round(attn_tflops / probe["tflops"], 4)}
     res = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
@@ -255,6 +275,7 @@ def main():
         "attn_fwd": {"ms": round(attn_ms, 3), "tflops": round(attn_tflops, 1)},
         "per_call_ms": {k: round(v, 3) for k, v in avg.items()},
         "roofline": roof,
+        "mfma_probe": probe,
         "wall_s": round(wall, 2),
     }
     if not args.no_cpu:

@@ -29,6 +29,7 @@ EXPORTS = [
     "whale_fusion_mlp_bwd_workspace_size", "whale_fusion_mlp_bwd",
     "whale_swiglu_ffn_bwd_workspace_size", "whale_swiglu_ffn_bwd",
     "whale_proj_qkv_bwd_workspace_size", "whale_proj_qkv_bwd",
+    "whale_mfma_peak_probe",
 ]
 
 
@@ -51,6 +52,7 @@ _SIGS = {
     "whale_proj_qkv": (_I, [_D, _I, _P, _P, _I, _F, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "whale_jagged_xattn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_jagged_xattn_fwd_varc": (_I, [_D, _I, _P, _P, _P, _P, _P, _F, _P, _P, _P]),
+    "whale_mfma_peak_probe": (_I, [_P, ctypes.c_int32, ctypes.c_int32, _P]),
     "whale_fusion_mlp": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P]),
     "whale_swiglu_ffn_workspace_size": (_S, [_D, _I, _I, ctypes.c_int32]),
     "whale_swiglu_ffn": (_I, [_D, _I, _P, _I, _F, _P, _P, _P, _I, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _S, _P]),
@@ -148,6 +150,14 @@ def whale_jagged_xattn_fwd_varc(d_, Q, K, V, offsets, cand_offsets, scale, A, ls
                                             _ptr(offsets), _ptr(cand_offsets), float(scale), _ptr(A), _ptr(lse),
                                             _stream(stream))
     _check("whale_jagged_xattn_fwd_varc", rc)
+
+
+def whale_mfma_peak_probe(out, iters, blocks, stream=None):
+    """Launch the matrix-core rate probe (out: fp32 device tensor of blocks*256)."""
+    if out.numel() < blocks * 256:
+        raise ValueError("out needs blocks * 256 floats")
+    rc = load().whale_mfma_peak_probe(_ptr(out), int(iters), int(blocks), _stream(stream))
+    _check("whale_mfma_peak_probe", rc)
 
 
 def whale_fusion_mlp(d_, A, H_w, W_F, act, F, Z_saved, stream=None):

@@ -292,6 +292,20 @@ whale_status_t whale_proj_qkv_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
                                   float* dg_q, float* db_q, float* dg_kv, float* db_kv,
                                   void* workspace, size_t ws_bytes, hipStream_t stream);
 
+/* ------------------------------------------------------------- diagnostics */
+
+/*
+ * Matrix-core rate probe (not part of the module): blocks workgroups of 256
+ * threads, each wave running iters steps of four independent
+ * v_mfma_f32_32x32x16_bf16 chains on register operands, with no memory
+ * traffic besides one float per thread written to out [blocks * 256].  It
+ * does blocks * 4 * iters * 4 * 32768 FLOPs; timed by the caller, it gives
+ * the bf16 MFMA rate the GPU sustains, a measured ceiling beside the
+ * data-sheet peak.  WHALE_ERR_NULL for out NULL, WHALE_ERR_SHAPE for
+ * iters < 1 or blocks < 1.
+ */
+whale_status_t whale_mfma_peak_probe(float* out, int32_t iters, int32_t blocks, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
