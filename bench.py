@@ -53,9 +53,10 @@ def flops(cfg, T, H, gate_sep=False, shared_kv=False, M=None, pairs=None):
             "attn_bwd": 2.5 * attn_f, "gemm_bwd": 2.0 * gemm_f, "bwd": 2.5 * attn_f + 2.0 * gemm_f}
 
 
-def mfma_probe(torch, wb, dev, blocks=2048, iters=2000, reps=5):
+def mfma_probe(torch, wb, dev, blocks=2048, iters=10000, reps=5):
     """bf16 MFMA rate the GPU sustains with no memory traffic (TFLOP/s, best
-    of `reps` launches): 8 waves per SIMD of four independent MFMA chains."""
+    of `reps` launches of about 5 ms): 8 waves per SIMD of four independent
+    MFMA chains.  Run after the warm-up, with the clock already under load."""
     out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
     wb.whale_mfma_peak_probe(out, iters, blocks)
     torch.cuda.synchronize()
@@ -123,7 +124,6 @@ def main():
 
     wb.load()
     dev = torch.device("cuda:0")
-    probe = mfma_probe(torch, wb, dev)
     cfg = synth.CONFIGS["c3L10k"]
     L = synth.lengths(cfg)
     T = int(L.sum())
@@ -216,6 +216,7 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    probe = mfma_probe(torch, wb, dev)
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     record["on"] = True
     t0 = time.perf_counter()
