@@ -64,6 +64,10 @@ def test_host_validation_rejects_before_launch():
     # LayerNorm without its statistics buffer
     assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 0, 1e-5, fake, fake, fake, fake, fake, fake, fake, fake,
                               fake, fake, None, fake, None, None, None) == 1
+    # Matrix-core probe: NULL output, no iterations or no workgroups
+    assert lib.whale_mfma_peak_probe(None, 10, 1, None) == 1
+    assert lib.whale_mfma_peak_probe(fake, 0, 1, None) == 2
+    assert lib.whale_mfma_peak_probe(fake, 10, 0, None) == 2
     # Shared key-value form: W_V and V must be NULL together; a NULL dV needs V == K
     assert lib.whale_proj_qkv(ctypes.byref(d), 1, fake, fake, 2, 1e-5, None, None, None, None, fake, fake, None, fake,
                               fake, fake, None, None, None, None, None) == 1
