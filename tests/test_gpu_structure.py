@@ -156,3 +156,24 @@ def test_forward_replays_from_a_captured_graph(gpu):
         assert torch.equal(y, eager), f"replay {i}"
         _ = (x[0].float() * 2).sum()      # unrelated eager work between replays
         torch.cuda.synchronize()
+
+
+def test_mfma_probe_does_the_products_it_counts(gpu):
+    """The matrix-core probe's per-wave output sums to 4 * iters * sum(A B),
+    with A and B the register operands it builds: its FLOP count is real."""
+    blocks, iters = 3, 7
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=gpu)
+    wb.whale_mfma_peak_probe(out, iters, blocks)
+    torch.cuda.synchronize()
+    lane = np.arange(64)
+    A = np.zeros((32, 16))
+    Bm = np.zeros((16, 32))
+    for u in range(8):
+        # the kernel's fp32 product 1e-3f * x, rounded to bf16
+        a = synth.round_bf16(np.float32(1e-3) * (lane + u).astype(np.float32)).astype(np.float64)
+        b = synth.round_bf16(np.float32(1e-3) * (lane - u).astype(np.float32)).astype(np.float64)
+        A[lane % 32, 8 * (lane // 32) + u] = a
+        Bm[8 * (lane // 32) + u, lane % 32] = b
+    want = 4 * iters * (A @ Bm).sum()
+    got = out.double().cpu().numpy().reshape(-1, 64).sum(1)
+    np.testing.assert_allclose(got, want, rtol=1e-4)
