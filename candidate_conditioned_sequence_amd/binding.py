@@ -30,7 +30,9 @@ EXPORTS = [
     "whale_swiglu_ffn_bwd_workspace_size", "whale_swiglu_ffn_bwd",
     "whale_proj_qkv_bwd_workspace_size", "whale_proj_qkv_bwd",
     "whale_mfma_peak_probe",
+    "whale_validate_offsets", "whale_debug_checks", "whale_debug_status",
 ]
+BAD_FIRST, BAD_ORDER, BAD_MAX_L, BAD_TOTAL, BAD_CAND_FIRST, BAD_CAND_ORDER, BAD_MAX_C = 1, 2, 4, 8, 16, 32, 64
 
 
 class WhaleDims(ctypes.Structure):
@@ -53,6 +55,9 @@ _SIGS = {
     "whale_jagged_xattn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_jagged_xattn_fwd_varc": (_I, [_D, _I, _P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_mfma_peak_probe": (_I, [_P, ctypes.c_int32, ctypes.c_int32, _P]),
+    "whale_validate_offsets": (_I, [_D, _P, _P, _P, _P]),
+    "whale_debug_checks": (ctypes.c_int32, [ctypes.c_int32]),
+    "whale_debug_status": (_I, [_P, ctypes.c_int32, _P]),
     "whale_fusion_mlp": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P]),
     "whale_swiglu_ffn_workspace_size": (_S, [_D, _I, _I, ctypes.c_int32]),
     "whale_swiglu_ffn": (_I, [_D, _I, _P, _I, _F, _P, _P, _P, _I, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _S, _P]),
@@ -233,3 +238,24 @@ def whale_proj_qkv_bwd(d_, H_w, H_s, norm, eps, g_q, b_q, g_kv, b_kv, stats_q, s
                                    _ptr(dH_s), _ptr(dW_Q), _ptr(dW_K), _ptr(dW_V), _ptr(dg_q), _ptr(db_q),
                                    _ptr(dg_kv), _ptr(db_kv), _ptr(workspace), ws, _stream(stream))
     _check("whale_proj_qkv_bwd", rc)
+
+
+def whale_validate_offsets(d_, offsets, cand_offsets, flag, stream=None):
+    """flag: int32 device tensor with at least one element (receives the bitmask)."""
+    if flag.dtype != torch.int32:
+        raise TypeError("flag must be an int32 tensor")
+    rc = load().whale_validate_offsets(ctypes.byref(d_), _ptr(offsets), _ptr(cand_offsets), _ptr(flag),
+                                       _stream(stream))
+    _check("whale_validate_offsets", rc)
+
+
+def whale_debug_checks(enable):
+    """Turn debug mode on or off; returns the previous setting (0 / 1)."""
+    return int(load().whale_debug_checks(1 if enable else 0))
+
+
+def whale_debug_status(flag, reset=False, stream=None):
+    if flag.dtype != torch.int32:
+        raise TypeError("flag must be an int32 tensor")
+    rc = load().whale_debug_status(_ptr(flag), 1 if reset else 0, _stream(stream))
+    _check("whale_debug_status", rc)

@@ -29,7 +29,7 @@ whale_status_t check_dims(const whale_dims_t* dims, whale_dtype_t dtype, Shape* 
   if ((int64_t)x.max_L > x.total_L) return WHALE_ERR_SHAPE;
   if (x.total_L > (int64_t)x.B * x.max_L) return WHALE_ERR_SHAPE;
   const int dh = x.d / x.h;
-  if (dh != 32 && dh != 64) return WHALE_ERR_UNSUPPORTED;
+  if (dh != 32 && dh != 64 && dh != 128) return WHALE_ERR_UNSUPPORTED;
   if (x.d != 64 && x.d != 128 && x.d != 256 && x.d != 512) return WHALE_ERR_UNSUPPORTED;
   s->M = M;
   s->T = x.total_L;
@@ -133,14 +133,32 @@ const char* whale_status_string(whale_status_t s) {
     case WHALE_ERR_NULL: return "WHALE_ERR_NULL: a required pointer is NULL";
     case WHALE_ERR_SHAPE: return "WHALE_ERR_SHAPE: inconsistent sizes or values";
     case WHALE_ERR_DTYPE: return "WHALE_ERR_DTYPE: unknown data type";
-    case WHALE_ERR_UNSUPPORTED: return "WHALE_ERR_UNSUPPORTED: shape not implemented (d_h must be 32 or 64, d <= 512, H % 64 == 0)";
+    case WHALE_ERR_UNSUPPORTED:
+      return "WHALE_ERR_UNSUPPORTED: shape not implemented (d_h must be 32, 64 or 128, d one of 64, 128, 256, 512, "
+             "H % 64 == 0)";
     case WHALE_ERR_WORKSPACE: return "WHALE_ERR_WORKSPACE: workspace too small";
     case WHALE_ERR_LAUNCH: return "WHALE_ERR_LAUNCH: kernel launch failed";
   }
   return "WHALE_ERR_UNKNOWN";
 }
 
-const char* whale_version(void) { return "0.1.0"; }
+const char* whale_version(void) { return "0.2.0"; }
+
+whale_status_t whale_validate_offsets(const whale_dims_t* dims, const int64_t* offsets, const int64_t* cand_offsets,
+                                      int32_t* flag, hipStream_t stream) {
+  // Only the sizes the check reads need to be sane here; widths do not matter.
+  if (dims == nullptr || !offsets || !flag) return WHALE_ERR_NULL;
+  const whale_dims_t& x = *dims;
+  if (x.B <= 0 || x.C <= 0 || x.max_L < 0 || x.total_L < 0) return WHALE_ERR_SHAPE;
+  return ret(launch_validate_offsets(offsets, cand_offsets, x.B, x.max_L, x.total_L, x.C, flag, nullptr, stream));
+}
+
+int32_t whale_debug_checks(int32_t enable) { return set_debug_checks(enable != 0); }
+
+whale_status_t whale_debug_status(int32_t* flag, int32_t reset, hipStream_t stream) {
+  if (!flag) return WHALE_ERR_NULL;
+  return ret(launch_debug_status(flag, reset, stream));
+}
 
 // ------------------------------------------------------------------ forward
 
@@ -213,6 +231,21 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
 
 namespace {
 
+// Debug mode (WHALE_DEBUG_CHECKS, or whale_debug_checks(1)): validate the
+// offsets against the hints into the library's flag on this GPU, and hand the
+// flag to the kernels, which skip their work when it is set.  Off: *guard =
+// nullptr and nothing is launched.
+whale_status_t debug_guard(const Shape& s, const int64_t* offsets, const int64_t* cand_offsets,
+                           const int32_t** guard, hipStream_t stream) {
+  *guard = nullptr;
+  if (!debug_checks_on()) return WHALE_OK;
+  int32_t* f = debug_flags_device();
+  if (f == nullptr) return WHALE_ERR_LAUNCH;
+  WHALE_TRY(launch_validate_offsets(offsets, cand_offsets, s.B, s.max_L, s.T, s.C, f, f + 1, stream));
+  *guard = f;
+  return WHALE_OK;
+}
+
 // Both forward attention calls: cand_offsets null for C candidates per request.
 whale_status_t xattn_fwd_call(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
                               const void* V, const int64_t* offsets, const int64_t* cand_offsets, float scale,
@@ -228,6 +261,8 @@ whale_status_t xattn_fwd_call(const whale_dims_t* dims, whale_dtype_t dtype, con
   a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
   a.cand_offsets = cand_offsets; a.n_q = s.n_q;
+  whale_status_t g = debug_guard(s, offsets, cand_offsets, &a.guard, stream);
+  if (g != WHALE_OK) return g;
   return ret(launch_xattn_fwd(a, dtype == WHALE_BF16, stream));
 }
 
@@ -379,6 +414,8 @@ whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dt
   a.partial = a.splits > 1 ? (float*)c.take((size_t)a.splits * 2 * s.T * s.d * 4) : nullptr;
   a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh; a.max_L = s.max_L; a.T = s.T;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
+  whale_status_t g = debug_guard(s, offsets, nullptr, &a.guard, stream);
+  if (g != WHALE_OK) return g;
   return ret(launch_xattn_bwd(a, dtype == WHALE_BF16, stream));
 }
 

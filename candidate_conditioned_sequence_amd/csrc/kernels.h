@@ -13,6 +13,10 @@ struct XattnArgs {
   // n_q*cand_offsets[b] .. n_q*cand_offsets[b+1]-1 (nullptr: b*QR .. (b+1)*QR-1).
   const int64_t* cand_offsets;
   int n_q;
+  // Debug mode: a device flag written by the offset validator just before;
+  // every kernel of the call returns at once when it is non-zero.  nullptr
+  // otherwise.
+  const int32_t* guard = nullptr;
 };
 hipError_t launch_xattn_fwd(const XattnArgs& a, bool bf16_data, hipStream_t st);
 
@@ -25,6 +29,7 @@ struct XattnBwdArgs {
   int B, QR, d, h, dh, max_L, splits;
   int64_t T;
   float scale;
+  const int32_t* guard = nullptr;   // as in XattnArgs
 };
 hipError_t launch_xattn_bwd(const XattnBwdArgs& a, bool bf16_data, hipStream_t st);
 int xattn_bwd_splits(int B, int h, int QR, int max_L, int dh);
@@ -157,6 +162,29 @@ struct WgradArgs {
 };
 hipError_t launch_wgrad(const WgradArgs& a, bool bf16_data, hipStream_t st);
 int wgrad_splits(int64_t M, int N, int K);
+
+// ------------------------------------------------- offset validation (debug)
+// Bits of the validator's flag (0 = the offsets satisfy the hints).
+enum : int32_t {
+  kBadFirst = 1,        // offsets[0] != 0
+  kBadOrder = 2,        // offsets decrease somewhere
+  kBadMaxL = 4,         // some L_b > max_L
+  kBadTotal = 8,        // offsets[B] != total_L
+  kBadCandFirst = 16,   // cand_offsets[0] != 0
+  kBadCandOrder = 32,   // cand_offsets decrease somewhere
+  kBadMaxC = 64         // some C_b > C
+};
+// One workgroup: flag[0] = violations found; sticky[0] |= the same (sticky may
+// be null).  cand_offsets may be null.
+hipError_t launch_validate_offsets(const int64_t* offsets, const int64_t* cand_offsets, int B, int max_L,
+                                   int64_t total_L, int C, int32_t* flag, int32_t* sticky, hipStream_t st);
+// The library's debug flags on the current GPU ([0] last check, [1] sticky),
+// or nullptr if the address cannot be obtained.
+int32_t* debug_flags_device();
+// dst[0] = sticky flag; reset != 0 clears both flags afterwards.
+hipError_t launch_debug_status(int32_t* dst, int reset, hipStream_t st);
+bool debug_checks_on();
+int set_debug_checks(int on);
 
 // ---------------------------------------------------------------- misc
 // dst[c][col0 + r] = src[r][c] for a [rows, cols] matrix (data type), dst row stride ldd.

@@ -66,12 +66,14 @@ WHALE_DEV void p_ds_pack(const f32x16& s, const f32x16& dp, x8_t<T> (&pf)[2], x8
 // score MFMA; -D likewise starts the dP MFMA, so P = exp2(acc) and
 // dS = P * acc' need no other VALU work.  fp32 keeps Q exact and forms t with
 // one fused multiply-add.
+// (d_h = 128: one workgroup per CU, for the register room; likewise below.)
 template <typename T, int DH, int NWQ>
-__global__ __launch_bounds__(NWQ * 64, 2) void bwd_dq_kernel(
+__global__ __launch_bounds__(NWQ * 64, DH >= 128 ? 1 : 2) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const T* __restrict__ dA, const T* __restrict__ A,
     const float* __restrict__ lse, float* __restrict__ Dbuf, T* __restrict__ dQ, int d, int h, int QR, int nqb,
-    float c, float scale, int nblocks) {
+    float c, float scale, int nblocks, const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = NWQ * 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (NWQ * 64);
   static_assert(NCH >= 1 && BN * CPR % (NWQ * 64) == 0, "tile/threads mismatch");
@@ -234,11 +236,13 @@ __global__ __launch_bounds__(NWQ * 64, 2) void bwd_dq_kernel(
 // split are loaded as copies of its last row with -lse2 = -inf, so P = 0 and
 // dS = 0 for them.
 template <typename T, int DH, int NWK>
-__global__ __launch_bounds__(NWK * 64, 2) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const T* __restrict__ dA, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ part,
-    int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks) {
+    int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks,
+    const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int QT = 64, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (NWK * 64);
   constexpr int KB = NWK * 32;   // history rows per workgroup
@@ -440,7 +444,9 @@ __global__ __launch_bounds__(NWK * 64, 2) void bwd_dkdv_kernel(
 // form) only the first half of each split holds data, already dK + dV.
 template <typename T>
 __global__ __launch_bounds__(256) void kv_split_reduce_kernel(const float* __restrict__ part, int splits, int64_t n,
-                                                              T* __restrict__ dK, T* __restrict__ dV) {
+                                                              T* __restrict__ dK, T* __restrict__ dV,
+                                                              const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= (dV ? 2 * n : n)) return;
   float s = 0.f;
@@ -464,7 +470,7 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
       const int64_t nblk = (int64_t)a.B * a.h * nqb;
       hipLaunchKernelGGL((bwd_dq_kernel<T, DH, NWQ>), dim3((unsigned)nblk), dim3(NWQ * 64), 0, st, (const T*)a.Q,
                          (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, (const T*)a.A, a.lse, a.Dbuf,
-                         (T*)a.dQ, a.d, a.h, a.QR, nqb, c, a.scale, (int)nblk);
+                         (T*)a.dQ, a.d, a.h, a.QR, nqb, c, a.scale, (int)nblk, a.guard);
     };
     bool done = false;
     if constexpr (DH == 64) {
@@ -487,7 +493,8 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
       const int64_t nblk = (int64_t)a.B * a.h * nkt;
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, NWK>), dim3((unsigned)nblk, a.splits), dim3(NWK * 64), 0, st,
                          (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf,
-                         (T*)a.dK, (T*)a.dV, part, a.d, a.h, a.QR, nkt, qchunk, c, a.scale, a.T, (int)nblk);
+                         (T*)a.dK, (T*)a.dV, part, a.d, a.h, a.QR, nkt, qchunk, c, a.scale, a.T, (int)nblk,
+                         a.guard);
     };
     bool done = false;
     if constexpr (DH == 64) {
@@ -499,7 +506,7 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
     const int64_t n = a.T * a.d;
     const int64_t nr = a.dV ? 2 * n : n;
     hipLaunchKernelGGL(kv_split_reduce_kernel<T>, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, st, a.partial,
-                       a.splits, n, (T*)a.dK, (T*)a.dV);
+                       a.splits, n, (T*)a.dK, (T*)a.dV, a.guard);
     return hipGetLastError();
   }
 }
@@ -509,6 +516,7 @@ hipError_t bwd_dh(const XattnBwdArgs& a, hipStream_t st) {
   switch (a.dh) {
     case 32: return bwd_t<T, 32>(a, st);
     case 64: return bwd_t<T, 64>(a, st);
+    case 128: return bwd_t<T, 128>(a, st);
   }
   return hipErrorInvalidValue;
 }

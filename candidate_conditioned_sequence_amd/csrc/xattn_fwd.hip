@@ -67,13 +67,18 @@ struct FwdTile {
 // accumulator input of the score MFMA, so the common path spends no VALU
 // instruction between the MFMA output and the exponential.  fp32 keeps Q
 // exact and forms t with a separate multiply and subtract.
+// d_h = 128 keeps one workgroup per CU (its operands and accumulators need
+// more than the 256 registers two workgroups would leave each wave).
 template <typename T, int DH, int QPW, int kNW>
-__global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
+__global__ __launch_bounds__(kNW * 64, DH >= 128 ? 1 : 2) void xattn_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, T* __restrict__ A, float* __restrict__ lse,
-    int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q) {
+    int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q,
+    const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   using TT = FwdTile<T, DH, kNW>;
   constexpr int NQ = QPW / 32, KS = DH / 16, NE = DH / 32, QB = kNW * QPW;
+  constexpr int KBR = DH >= 128 ? 1 : 2;       // key blocks whose K operands are read at once
   constexpr int KLD = TT::KLD, CPR = TT::CPR, NCH = TT::NCH;
   constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Ks[2][kBN * KLD];
@@ -167,26 +172,32 @@ __global__ __launch_bounds__(kNW * 64, 2) void xattn_fwd_kernel(
     // Scores of two 32-row key blocks, accumulated onto -ref (bf16) or 0.
     // All K operands are read first (one LDS wait), then the 16 MFMAs are
     // issued at raised wave priority, so the other wave's softmax fills in.
+    // (d_h = 128 reads and multiplies one key block at a time, which halves
+    // the live K operands.)
     __builtin_amdgcn_s_setprio(1);
     f32x16 s[2][NQ];
-    x8_t<T> ka[2][KS];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb0 = 0; kb0 < 2; kb0 += KBR) {
+      x8_t<T> ka[KBR][KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ka[kb][ks] = ld8<T>(&Ks[buf][(32 * kb + l32) * KLD + 16 * ks + 8 * hh]);
+      for (int i = 0; i < KBR; ++i)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+        for (int ks = 0; ks < KS; ++ks)
+          ka[i][ks] = ld8<T>(&Ks[buf][(32 * (kb0 + i) + l32) * KLD + 16 * ks + 8 * hh]);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+      for (int i = 0; i < KBR; ++i) {
 #pragma unroll
-        for (int qb = 0; qb < NQ; ++qb) {
-          if (ks == 0) s[kb][qb] = bias[qb];
-          mma32(s[kb][qb], ka[kb][ks], qf[qb][ks]);
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int qb = 0; qb < NQ; ++qb) {
+            if (ks == 0) s[kb0 + i][qb] = bias[qb];
+            mma32(s[kb0 + i][qb], ka[i][ks], qf[qb][ks]);
+          }
         }
       }
+      __builtin_amdgcn_sched_group_barrier(0x0100, KBR * KS, 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, KBR * KS * NQ, 0);
     }
-    __builtin_amdgcn_sched_group_barrier(0x0100, 2 * KS, 0);
-    __builtin_amdgcn_sched_group_barrier(0x0008, 2 * KS * NQ, 0);
     __builtin_amdgcn_s_setprio(0);
     if (!kFold) {
 #pragma unroll
@@ -354,7 +365,9 @@ template <int DH>
 __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const int64_t* __restrict__ offsets, bf16* __restrict__ A, float* __restrict__ lse,
-    int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q) {
+    int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q,
+    const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int NQ = kPPQ / 32, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8;
   constexpr int NCH = kBN * CPR / (4 * 64);      // chunks per thread of one tensor (4 waves per tensor)
@@ -618,7 +631,7 @@ hipError_t launch_fwd_pp(const XattnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((xattn_fwd_pp_kernel<DH>), dim3((unsigned)nblk), dim3(kPPW * 64), 0, st,
                      (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.offsets, (bf16*)a.A, a.lse,
-                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q);
+                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q, a.guard);
   return hipGetLastError();
 }
 
@@ -631,7 +644,7 @@ hipError_t launch_fwd_t(const XattnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((xattn_fwd_kernel<T, DH, QPW, kNW>), dim3((unsigned)nblk), dim3(kNW * 64), 0, st,
                      (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (T*)a.A, a.lse,
-                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q);
+                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q, a.guard);
   return hipGetLastError();
 }
 
@@ -644,6 +657,7 @@ hipError_t launch_fwd_dh(const XattnArgs& a, hipStream_t st) {
   switch (a.dh) {
     case 32: return wide ? launch_fwd_t<T, 32, 64, 4>(a, st) : launch_fwd_t<T, 32, 32, 4>(a, st);
     case 64: return wide ? launch_fwd_t<T, 64, 64, 4>(a, st) : launch_fwd_t<T, 64, 32, 4>(a, st);
+    case 128: return launch_fwd_t<T, 128, 32, 4>(a, st);
   }
   return hipErrorInvalidValue;
 }

@@ -46,6 +46,23 @@ class FusionLayer:
         rows as one batch and only the attention call sees the requests."""
         p, dev, dt = self.p, H_w.device, H_w.dtype
         M, T, d = H_w.shape[0], H_s.shape[0], self.d
+        # Host-side shape checks only (nothing is read from the device): the
+        # kernels index H_w, H_s and the offsets by these sizes.
+        if H_w.dim() != 2 or H_s.dim() != 2 or H_w.shape[1] != d or H_s.shape[1] != d:
+            raise ValueError(f"H_w and H_s must be [rows, {d}]")
+        for name, o in (("offsets", offsets), ("cand_offsets", cand_offsets)):
+            if o is not None and (o.dtype != torch.int64 or o.dim() != 1 or not o.is_contiguous()
+                                  or o.device != dev):
+                raise ValueError(f"{name} must be a contiguous int64 vector on {dev}")
+        if not 0 <= int(max_L) <= T:
+            raise ValueError(f"max_L = {max_L} must lie in [0, {T}] (T = rows of H_s)")
+        if cand_offsets is None:
+            per = self.C * self.n_q
+            if M == 0 or M % per != 0:
+                raise ValueError(f"H_w has {M} rows, not a positive multiple of C*n_q = {per}")
+            if offsets.shape[0] != M // per + 1:
+                raise ValueError(f"offsets has {offsets.shape[0]} entries for B = {M // per} requests "
+                                 f"(B + 1 expected)")
         if cand_offsets is not None:
             if save:
                 raise ValueError("the form with candidate offsets is forward only (save=False)")

@@ -45,13 +45,17 @@
  *     device memory on the host or synchronises.  The host shape hints
  *     dims->max_L and dims->total_L stand in for any device-to-host read of
  *     the offsets ("shape hint tensors", [GS 2.2]).  The caller guarantees
- *     that the offsets are consistent with them (every L_b <= max_L,
- *     offsets[B] == total_L); this is not checked on the device.
+ *     that the offsets are consistent with them (offsets[0] == 0,
+ *     non-decreasing, every L_b <= max_L, offsets[B] == total_L).  Grids are
+ *     sized from the hints and rows indexed by the offsets, so inconsistent
+ *     offsets give wrong results or out-of-range reads.  whale_validate_offsets
+ *     checks them on the device; in debug mode (below) every attention call
+ *     checks them first and skips its kernels when they fail.
  *   - Errors found on the host return before anything is enqueued: a NULL
  *     required pointer (WHALE_ERR_NULL), inconsistent sizes (WHALE_ERR_SHAPE,
  *     e.g. d % h != 0, M == 0), an unknown dtype (WHALE_ERR_DTYPE), a shape
  *     the kernels do not implement (WHALE_ERR_UNSUPPORTED: d_h not in
- *     {32, 64}, d not in {64, 128, 256, 512}, H not a multiple of 64), or a workspace
+ *     {32, 64, 128}, d not in {64, 128, 256, 512}, H not a multiple of 64), or a workspace
  *     smaller than the size query returns (WHALE_ERR_WORKSPACE).  A failed kernel launch returns WHALE_ERR_LAUNCH.
  *   - Results are bitwise reproducible for fixed inputs, dims and device:
  *     no atomics, every reduction runs in a fixed order.
@@ -95,6 +99,53 @@ const char* whale_status_string(whale_status_t status);
 
 /* Library version string, "major.minor.patch". */
 const char* whale_version(void);
+
+/* ------------------------------------------------- offset validation */
+
+/* Bits of the validation flag (0: the offsets satisfy the hints). */
+#define WHALE_BAD_FIRST 1        /* offsets[0] != 0 */
+#define WHALE_BAD_ORDER 2        /* offsets[b+1] < offsets[b] for some b */
+#define WHALE_BAD_MAX_L 4        /* offsets[b+1] - offsets[b] > max_L for some b */
+#define WHALE_BAD_TOTAL 8        /* offsets[B] != total_L */
+#define WHALE_BAD_CAND_FIRST 16  /* cand_offsets[0] != 0 */
+#define WHALE_BAD_CAND_ORDER 32  /* cand_offsets decrease somewhere */
+#define WHALE_BAD_MAX_C 64       /* cand_offsets[b+1] - cand_offsets[b] > C for some b */
+
+/*
+ * Checks the jagged offsets [B+1] (and, if not NULL, the candidate offsets
+ * [B+1] of the serving form) against the host shape hints dims->max_L,
+ * dims->total_L and dims->C, on the device: the shape hints replace any read
+ * of the offsets on the host ([GS 2.2], "shape hint tensors"), so their
+ * consistency can only be checked there.  One small kernel on `stream`
+ * writes the bitmask of the violations found (WHALE_BAD_*) to *flag, an
+ * int32 in device memory owned by the caller (overwritten, not accumulated).
+ * Only dims->B, C, max_L and total_L are read.  Asynchronous: read *flag
+ * after synchronising the stream.  WHALE_ERR_NULL for a NULL dims, offsets
+ * or flag; WHALE_ERR_SHAPE for B <= 0, C <= 0 or negative hints.
+ */
+whale_status_t whale_validate_offsets(const whale_dims_t* dims, const int64_t* offsets, const int64_t* cand_offsets,
+                                      int32_t* flag, hipStream_t stream);
+
+/*
+ * Debug mode, for all GPUs of the process: enable != 0 turns it on, 0 off;
+ * returns the previous setting.  It starts on when the environment variable
+ * WHALE_DEBUG_CHECKS is set to a value other than "" or "0" when the first
+ * call is made.  In debug mode whale_jagged_xattn_fwd, _fwd_varc and _bwd
+ * first run the check of whale_validate_offsets into a flag the library
+ * keeps on each GPU (a small static device array, the only state the library
+ * holds), and their kernels return without touching any output when it
+ * reports a violation: nothing is read past the buffers the hints describe,
+ * and the outputs keep whatever they held.  Calls in debug mode on one GPU
+ * share that flag, so they must not overlap across streams.
+ */
+int32_t whale_debug_checks(int32_t enable);
+
+/*
+ * Debug mode: writes the OR of every check made since the last reset to
+ * *flag (device int32, caller-owned), then clears the library's flags when
+ * reset != 0.  Asynchronous on `stream`.  WHALE_ERR_NULL for a NULL flag.
+ */
+whale_status_t whale_debug_status(int32_t* flag, int32_t reset, hipStream_t stream);
 
 /* ---------------------------------------------------------------- forward */
 

@@ -43,6 +43,13 @@ XATTN_CASES = [
     # query block, every ragged length class)
     ("bf16", 256, 4, 40, 30, [0, 1, 63, 64, 65, 257, 130]),
     ("bf16", 512, 8, 32, 32, [700, 1]),
+    # d_h = 128 (d = 256, h = 2 and d = 512, h = 4): the general kernel with
+    # one key block of K operands at a time
+    ("f32", 256, 2, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 256, 2, 20, 15, [130, 1, 700, 64]),
+    ("bf16", 512, 4, 8, 16, [97, 640]),
+    ("f32", 512, 4, 4, 8, [300, 5]),
+    ("bf16", 256, 2, 40, 30, [1000, 65, 0]),
 ]
 
 
@@ -191,6 +198,12 @@ BWD_CASES = [
     ("bf16", 128, 4, 3, 5, [0, 1, 63, 64, 65, 257]),
     ("bf16", 256, 4, 20, 15, [130, 1, 700, 64]),
     ("bf16", 256, 4, 64, 32, [900, 333]),
+    # d_h = 128
+    ("f32", 256, 2, 3, 5, [0, 1, 63, 64, 65, 257]),
+    ("bf16", 256, 2, 20, 15, [130, 1, 700, 64]),
+    ("bf16", 512, 4, 8, 16, [97, 640]),
+    ("bf16", 256, 2, 64, 32, [900, 333]),
+    ("f32", 512, 4, 4, 8, [300, 5]),
 ]
 
 
@@ -225,6 +238,7 @@ SHARED_KV_CASES = [
     ("bf16", 128, 4, 3, 5, [0, 1, 63, 64, 65, 257]),
     ("bf16", 256, 4, 20, 15, [130, 1, 700, 64]),
     ("bf16", 256, 4, 16, 32, [2100, 2050, 1999, 2100, 7, 2100, 1500, 2048]),
+    ("bf16", 256, 2, 20, 15, [130, 1, 700, 64]),
 ]
 
 

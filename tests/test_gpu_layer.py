@@ -108,6 +108,24 @@ def test_config_reduced(gpu, key):
             assert_close(k, res["grads"][k], g_ref[k], cfg.dtype)
 
 
+@pytest.mark.parametrize("key,h", [("c5", 2), ("c4", 4)])
+def test_layer_head_width_128(gpu, key, h):
+    """Whole layers with d_h = 128 (d = 256, h = 2 forward + backward; d = 512,
+    h = 4 forward of one layer of the stack)."""
+    cfg = synth.scaled(synth.CONFIGS[key], h=h, **REDUCED[key])
+    if key == "c4":
+        cfg = synth.scaled(cfg, layers=1)
+    backward = key == "c5"
+    print(f"\n[layer d_h=128] {cfg.name} d={cfg.d} h={cfg.h} B={cfg.B} L={synth.lengths(cfg).tolist()} "
+          f"bwd={backward}", flush=True)
+    res, _ = run_layers(cfg, gpu, backward=backward)
+    y_ref, g_ref = oracle_layers(cfg, list(range(cfg.B)), backward=backward)
+    assert_close("Y", res["Y"], y_ref, cfg.dtype)
+    if backward:
+        for k in GRADS + ("dg_q", "db_q", "dg_kv", "db_kv", "dg_f", "db_f"):
+            assert_close(k, res["grads"][k], g_ref[k], cfg.dtype)
+
+
 @pytest.mark.parametrize("key", ["c1", "c5"])
 def test_shared_kv_layer_reduced(gpu, key):
     """Shared key-value layers: forward and every gradient against the oracle."""
@@ -206,10 +224,16 @@ def test_config_full_size_forward_sampled(gpu, key):
 
 
 @pytest.mark.timeout(300)
-def test_config_c5_full_size_backward_sampled(gpu):
-    cfg = synth.CONFIGS["c5"]
+@pytest.mark.parametrize("key", ["c5", "c3L10k"])
+def test_config_full_size_backward_sampled(gpu, key):
+    """Forward and backward at full size in the launch configuration the
+    benchmark times (c3L10k is the benchmarked step itself: B = 128, every
+    L_b = 10000), checked on sampled requests."""
+    cfg = synth.CONFIGS[key]
     L = synth.lengths(cfg)
     sample = synth.sample_requests(L, 2)
+    if len(sample) < 2:                        # equal lengths: first and last request
+        sample = [0, cfg.B - 1]
     print(f"\n[layer full bwd] {cfg.name} B={cfg.B} T={int(L.sum())} sample={sample} L={L[sample].tolist()}",
           flush=True)
     res, _ = run_layers(cfg, gpu, backward=True, dy_mask=set(sample))
@@ -219,5 +243,10 @@ def test_config_c5_full_size_backward_sampled(gpu):
     assert_close("Y[sampled]", host(res["Y"])[m], y_ref, cfg.dtype)
     assert_close("dH_w[sampled]", host(g["dH_w"])[m], g_ref["dH_w"], cfg.dtype)
     assert_close("dH_s[sampled]", host(g["dH_s"])[t], g_ref["dH_s"], cfg.dtype)
+    # requests outside the sample got a zero upstream gradient: their
+    # input gradients are exactly zero
+    others = np.setdiff1d(np.arange(cfg.B), sample)[:3]
+    mo, to = _rows(cfg, L, list(range(cfg.B)), list(others))
+    assert not host(g["dH_w"])[mo].any() and not host(g["dH_s"])[to].any()
     for k in ("dW_Q", "dW_K", "dW_V", "dW_F", "dW_U", "dW_D", "dg_q", "db_q", "dg_kv", "db_kv", "dg_f", "db_f"):
         assert_close(k, g[k], g_ref[k], cfg.dtype)

@@ -53,9 +53,12 @@ def test_host_validation_rejects_before_launch():
     for bad in (_dims(h=3), _dims(max_L=200, total_L=150), _dims(max_L=10, total_L=150), _dims(B=0)):
         assert lib.whale_jagged_xattn_fwd(ctypes.byref(bad), 1, fake, fake, fake, fake, 0.0, fake, None, None) == 2
     assert lib.whale_jagged_xattn_fwd(ctypes.byref(d), 1, fake, fake, fake, fake, -1.0, fake, None, None) == 2
-    # unsupported head width (d_h = 128) and width above 512
-    for bad in (_dims(d=256, h=2), _dims(d=1024, h=16)):
+    # unsupported head widths (d_h = 16, 256) and width above 512
+    for bad in (_dims(d=64, h=4), _dims(d=512, h=2), _dims(d=1024, h=16)):
         assert lib.whale_jagged_xattn_fwd(ctypes.byref(bad), 1, fake, fake, fake, fake, 0.0, fake, None, None) == 4
+    # d_h = 128 passes the host checks (it fails on the NULL output instead)
+    assert lib.whale_jagged_xattn_fwd(ctypes.byref(_dims(d=256, h=2)), 1, fake, fake, fake, fake, 0.0, None, None,
+                                      None) == 1
     # FFN hidden width not a multiple of 64, workspace too small
     assert lib.whale_swiglu_ffn(ctypes.byref(d), 1, fake, 0, 1e-5, fake, fake, fake, 0, 100, fake, fake, None, fake,
                                 None, fake, 1 << 30, None) == 4
@@ -90,3 +93,47 @@ def test_workspace_sizes_are_host_only_and_monotone():
     assert lib.whale_swiglu_ffn_bwd_workspace_size(ctypes.byref(small), 1, 0, 512) > 0
     assert lib.whale_swiglu_ffn_workspace_size(ctypes.byref(small), 1, 1, 512) == \
         lib.whale_swiglu_ffn_workspace_size(ctypes.byref(small), 1, 0, 512)
+
+
+def test_validator_host_checks():
+    lib = wb.load()
+    fake = ctypes.c_void_p(256)
+    d = _dims()
+    assert lib.whale_validate_offsets(None, fake, None, fake, None) == 1
+    assert lib.whale_validate_offsets(ctypes.byref(d), None, None, fake, None) == 1
+    assert lib.whale_validate_offsets(ctypes.byref(d), fake, None, None, None) == 1
+    for bad in (_dims(B=0), _dims(C=0), _dims(max_L=-1)):
+        assert lib.whale_validate_offsets(ctypes.byref(bad), fake, None, fake, None) == 2
+    assert lib.whale_debug_status(None, 0, None) == 1
+
+
+def test_debug_switch_round_trip():
+    prev = wb.whale_debug_checks(True)
+    try:
+        assert wb.whale_debug_checks(False) == 1
+        assert wb.whale_debug_checks(False) == 0
+    finally:
+        wb.whale_debug_checks(prev)
+
+
+def test_layer_rejects_inconsistent_shapes_on_the_host():
+    """FusionLayer.forward checks sizes on the host before any call (CPU
+    tensors suffice: the checks run first)."""
+    import torch
+    from candidate_conditioned_sequence_amd.layer import FusionLayer
+    d, C, n_q = 64, 2, 3
+    p = {k: torch.zeros(d, d) for k in ("W_Q", "W_K", "W_V")}
+    p.update(W_F=torch.zeros(d, 2 * d), W_U=torch.zeros(4 * d, d), W_D=torch.zeros(d, 4 * d))
+    lay = FusionLayer(p, C, n_q, 2)
+    Hw, Hs = torch.zeros(2 * C * n_q, d), torch.zeros(10, d)
+    off = torch.tensor([0, 4, 10])
+    with pytest.raises(ValueError, match="multiple of C\\*n_q"):
+        lay.forward(Hw[:-1], Hs, off, 6)
+    with pytest.raises(ValueError, match="B \\+ 1 expected"):
+        lay.forward(Hw, Hs, off[:2], 6)
+    with pytest.raises(ValueError, match="int64"):
+        lay.forward(Hw, Hs, off.to(torch.int32), 6)
+    with pytest.raises(ValueError, match="max_L"):
+        lay.forward(Hw, Hs, off, 11)
+    with pytest.raises(ValueError, match="rows"):
+        lay.forward(Hw[:, :32], Hs, off, 6)

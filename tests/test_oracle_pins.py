@@ -299,7 +299,7 @@ def test_swiglu_closed_forms():
 
 # ------------------------------------------------------------ backward
 
-def _layer_case(seed, lengths=(3, 1, 0), norm=O.NORM_LAYER, gate=O.GATE_SHARED, ffn=True):
+def _layer_case(seed, lengths=(3, 1, 0), norm=O.NORM_LAYER, gate=O.GATE_SHARED, ffn=True, act=O.ACT_SILU):
     B, C, n_q, d, h, H = len(lengths), 2, 2, 8, 2, 12
     off = np.concatenate([[0], np.cumsum(lengths)])
     r = np.random.default_rng(seed)
@@ -313,7 +313,7 @@ def _layer_case(seed, lengths=(3, 1, 0), norm=O.NORM_LAYER, gate=O.GATE_SHARED, 
         p[k] = 0.3 * r.standard_normal(d)
     x = dict(H_w=r.standard_normal((B * C * n_q, d)), H_s=r.standard_normal((int(off[-1]), d)))
     dY = r.standard_normal((B * C * n_q, d))
-    kw = dict(offsets=off, C=C, n_q=n_q, h=h, norm=norm, gate=gate, ffn=ffn)
+    kw = dict(offsets=off, C=C, n_q=n_q, h=h, norm=norm, gate=gate, ffn=ffn, act=act)
     return x, p, dY, kw
 
 
@@ -322,11 +322,20 @@ GRAD_OF = {"H_w": "dH_w", "H_s": "dH_s", "W_Q": "dW_Q", "W_K": "dW_K", "W_V": "d
            "g_kv": "dg_kv", "b_kv": "db_kv", "g_f": "dg_f", "b_f": "db_f"}
 
 
-@pytest.mark.parametrize("norm,gate,ffn", [(O.NORM_LAYER, O.GATE_SHARED, True),
-                                           (O.NORM_RMS, O.GATE_SEPARATE, True),
-                                           (O.NORM_LAYER, O.GATE_SHARED, False)])
-def test_layer_gradients_match_finite_differences(norm, gate, ffn):
-    x, p, dY, kw = _layer_case(21, norm=norm, gate=gate, ffn=ffn)
+# Every branch of the oracle's backward: the three norms, both gates, both
+# fusion activations, with and without the FFN.
+FD_CASES = [(O.NORM_LAYER, O.GATE_SHARED, True, O.ACT_SILU),
+            (O.NORM_RMS, O.GATE_SEPARATE, True, O.ACT_SILU),
+            (O.NORM_LAYER, O.GATE_SHARED, False, O.ACT_SILU),
+            (O.NORM_LAYER, O.GATE_SEPARATE, True, O.ACT_NONE),
+            (O.NORM_NONE, O.GATE_SHARED, True, O.ACT_NONE),
+            (O.NORM_NONE, O.GATE_SEPARATE, True, O.ACT_SILU),
+            (O.NORM_RMS, O.GATE_SHARED, False, O.ACT_NONE)]
+
+
+@pytest.mark.parametrize("norm,gate,ffn,act", FD_CASES)
+def test_layer_gradients_match_finite_differences(norm, gate, ffn, act):
+    x, p, dY, kw = _layer_case(21, norm=norm, gate=gate, ffn=ffn, act=act)
 
     def loss():
         out = O.layer_fwd(x["H_w"], x["H_s"], p=p, **kw)
@@ -337,7 +346,8 @@ def test_layer_gradients_match_finite_differences(norm, gate, ffn):
     for name, gname in GRAD_OF.items():
         if not ffn and name in ("W_U", "W_D", "g_f", "b_f"):
             continue
-        if norm == O.NORM_RMS and name in ("b_q", "b_kv", "b_f"):
+        if (norm == O.NORM_RMS and name in ("b_q", "b_kv", "b_f")) or (norm == O.NORM_NONE and name[:2] in ("g_", "b_")):
+            # parameters the norm does not use: exactly zero gradient
             np.testing.assert_array_equal(g[gname], 0)
             continue
         arr = x[name] if name in x else p[name]
@@ -353,29 +363,138 @@ def test_layer_gradients_match_finite_differences(norm, gate, ffn):
         np.testing.assert_allclose(g[gname], num, rtol=1e-6, atol=1e-7, err_msg=name)
 
 
-def test_gradients_match_torch_autograd():
-    x, p, dY, kw = _layer_case(23, lengths=(6, 2, 5))
-    g = O.layer_bwd(x["H_w"], x["H_s"], p=p, dY=dY, **kw)
-    T = {k: t64(v).requires_grad_() for k, v in {**x, **p}.items()}
+def _torch_norm(x, kind, g, b):
+    d = x.shape[1]
+    if kind == O.NORM_LAYER:
+        return TF.layer_norm(x, (d,), g, b, 1e-5)
+    if kind == O.NORM_RMS:
+        return TF.rms_norm(x, (d,), g, 1e-5)
+    return x
+
+
+def _torch_layer(T, kw, tied=False):
+    """The fusion layer written with torch fp64 ops (SDPA per request and
+    head), independent of the oracle, for autograd."""
     C, n_q, h, off = kw["C"], kw["n_q"], kw["h"], kw["offsets"]
+    norm, gate, act, ffn = kw["norm"], kw["gate"], kw["act"], kw["ffn"]
     d = T["H_w"].shape[1]
-    Xq = TF.layer_norm(T["H_w"], (d,), T["g_q"], T["b_q"], 1e-5)
-    Xs = TF.layer_norm(T["H_s"], (d,), T["g_kv"], T["b_kv"], 1e-5)
-    Q, K, V = Xq @ T["W_Q"].T, Xs @ T["W_K"].T, Xs @ T["W_V"].T
+    Xq = _torch_norm(T["H_w"], norm, T["g_q"], T["b_q"])
+    Xs = _torch_norm(T["H_s"], norm, T["g_kv"], T["b_kv"])
+    Q, K = Xq @ T["W_Q"].T, Xs @ T["W_K"].T
+    V = K if tied else Xs @ T["W_V"].T
     dh = d // h
     A_rows = []
     for b in range(len(off) - 1):
         q = Q[b * C * n_q:(b + 1) * C * n_q].reshape(-1, h, dh).transpose(0, 1)
         k = K[off[b]:off[b + 1]].reshape(-1, h, dh).transpose(0, 1)
         v = V[off[b]:off[b + 1]].reshape(-1, h, dh).transpose(0, 1)
+        if k.shape[1] == 0:
+            A_rows.append(torch.zeros(C * n_q, d, dtype=torch.float64))
+            continue
         A_rows.append(TF.scaled_dot_product_attention(q, k, v).transpose(0, 1).reshape(-1, d))
     A = torch.cat(A_rows)
-    F = T["H_w"] + TF.silu(torch.cat([A, T["H_w"]], 1) @ T["W_F"].T)
-    U = TF.layer_norm(F, (d,), T["g_f"], T["b_f"], 1e-5) @ T["W_U"].T
-    Y = F + (TF.silu(U) * U) @ T["W_D"].T
+    Z = torch.cat([A, T["H_w"]], 1) @ T["W_F"].T
+    F = T["H_w"] + (TF.silu(Z) if act == O.ACT_SILU else Z)
+    if not ffn:
+        return F
+    U = _torch_norm(F, norm, T["g_f"], T["b_f"]) @ T["W_U"].T
+    if gate == O.GATE_SHARED:
+        G = TF.silu(U) * U
+    else:
+        Hh = U.shape[1] // 2
+        G = TF.silu(U[:, :Hh]) * U[:, Hh:]
+    return F + G @ T["W_D"].T
+
+
+@pytest.mark.parametrize("norm,gate,ffn,act", FD_CASES)
+def test_gradients_match_torch_autograd(norm, gate, ffn, act):
+    x, p, dY, kw = _layer_case(23, lengths=(6, 2, 5), norm=norm, gate=gate, ffn=ffn, act=act)
+    g = O.layer_bwd(x["H_w"], x["H_s"], p=p, dY=dY, **kw)
+    T = {k: t64(v).requires_grad_() for k, v in {**x, **p}.items()}
+    Y = _torch_layer(T, kw)
     (Y * t64(dY)).sum().backward()
     for name, gname in GRAD_OF.items():
-        np.testing.assert_allclose(g[gname], T[name].grad.numpy(), rtol=1e-10, atol=1e-11, err_msg=name)
+        if not ffn and name in ("W_U", "W_D", "g_f", "b_f"):
+            continue
+        want = T[name].grad
+        want = np.zeros(T[name].shape) if want is None else want.numpy()   # unused by this norm kind
+        np.testing.assert_allclose(g[gname], want, rtol=1e-10, atol=1e-11, err_msg=name)
+
+
+@pytest.mark.parametrize("act", [O.ACT_SILU, O.ACT_NONE])
+def test_fusion_mlp_bwd_matches_autograd(act):
+    """fusion_mlp_bwd on its own, for both activations (the calls the GPU
+    tests compare against)."""
+    r = np.random.default_rng(71)
+    M, d = 9, 6
+    A, Hw, Wf, dF = r.standard_normal((M, d)), r.standard_normal((M, d)), r.standard_normal((d, 2 * d)), \
+        r.standard_normal((M, d))
+    dA, dHw, dWf = O.fusion_mlp_bwd(A, Hw, Wf, act, dF)
+    tA, tH, tW = (t64(v).requires_grad_() for v in (A, Hw, Wf))
+    Z = torch.cat([tA, tH], 1) @ tW.T
+    F = tH + (TF.silu(Z) if act == O.ACT_SILU else Z)
+    (F * t64(dF)).sum().backward()
+    for got, want in ((dA, tA.grad), (dHw, tH.grad), (dWf, tW.grad)):
+        np.testing.assert_allclose(got, want.numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("kind", [O.NORM_LAYER, O.NORM_RMS, O.NORM_NONE])
+def test_norm_bwd_matches_autograd(kind):
+    r = np.random.default_rng(73)
+    x, g, b, dy = r.standard_normal((7, 10)) * 2 + 0.5, 1 + 0.3 * r.standard_normal(10), r.standard_normal(10), \
+        r.standard_normal((7, 10))
+    dx, dg, db = O.norm_bwd(x, kind, g, 1e-5, dy)
+    tx, tg, tb = (t64(v).requires_grad_() for v in (x, g, b))
+    (_torch_norm(tx, kind, tg, tb) * t64(dy)).sum().backward()
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dg, np.zeros(10) if tg.grad is None else tg.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(db, np.zeros(10) if tb.grad is None else tb.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("norm", [O.NORM_LAYER, O.NORM_RMS, O.NORM_NONE])
+@pytest.mark.parametrize("gate", [O.GATE_SHARED, O.GATE_SEPARATE])
+def test_swiglu_ffn_bwd_matches_autograd(norm, gate):
+    r = np.random.default_rng(79)
+    M, d, H = 8, 6, 10
+    F, dY = r.standard_normal((M, d)), r.standard_normal((M, d))
+    g, b = 1 + 0.3 * r.standard_normal(d), 0.3 * r.standard_normal(d)
+    Wu = r.standard_normal(((2 if gate == O.GATE_SEPARATE else 1) * H, d)) * 0.5
+    Wd = r.standard_normal((d, H)) * 0.5
+    out = O.swiglu_ffn_bwd(F, norm, 1e-5, g, b, Wu, gate, Wd, dY)
+    tF, tg, tb, tU, tD = (t64(v).requires_grad_() for v in (F, g, b, Wu, Wd))
+    U = _torch_norm(tF, norm, tg, tb) @ tU.T
+    G = TF.silu(U) * U if gate == O.GATE_SHARED else TF.silu(U[:, :H]) * U[:, H:]
+    ((tF + G @ tD.T) * t64(dY)).sum().backward()
+    for k, t in (("dF", tF), ("dW_U", tU), ("dW_D", tD), ("dg_f", tg), ("db_f", tb)):
+        want = np.zeros(t.shape) if t.grad is None else t.grad.numpy()
+        np.testing.assert_allclose(out[k], want, rtol=1e-11, atol=1e-12, err_msg=k)
+
+
+@pytest.mark.parametrize("norm", [O.NORM_LAYER, O.NORM_RMS, O.NORM_NONE])
+@pytest.mark.parametrize("tied", [False, True])
+def test_proj_qkv_bwd_matches_autograd(norm, tied):
+    r = np.random.default_rng(83)
+    M, T, d = 7, 9, 8
+    Hw, Hs = r.standard_normal((M, d)), r.standard_normal((T, d))
+    gq, bq, gk, bk = (1 + 0.3 * r.standard_normal(d) if i % 2 == 0 else 0.3 * r.standard_normal(d) for i in range(4))
+    Wq, Wk, Wv = (r.standard_normal((d, d)) * 0.4 for _ in range(3))
+    dQ, dK, dV = r.standard_normal((M, d)), r.standard_normal((T, d)), r.standard_normal((T, d))
+    out = O.proj_qkv_bwd(Hw, Hs, norm, 1e-5, gq, bq, gk, bk, Wq, Wk, None if tied else Wv, dQ, dK,
+                         None if tied else dV)
+    t = {k: t64(v).requires_grad_() for k, v in dict(H_w=Hw, H_s=Hs, g_q=gq, b_q=bq, g_kv=gk, b_kv=bk, W_Q=Wq,
+                                                      W_K=Wk, W_V=Wv).items()}
+    Q = _torch_norm(t["H_w"], norm, t["g_q"], t["b_q"]) @ t["W_Q"].T
+    Xs = _torch_norm(t["H_s"], norm, t["g_kv"], t["b_kv"])
+    K = Xs @ t["W_K"].T
+    loss = (Q * t64(dQ)).sum() + (K * t64(dK)).sum()
+    if not tied:
+        loss = loss + ((Xs @ t["W_V"].T) * t64(dV)).sum()
+    loss.backward()
+    names = ["H_w", "H_s", "W_Q", "W_K", "g_q", "b_q", "g_kv", "b_kv"] + ([] if tied else ["W_V"])
+    for n in names:
+        want = np.zeros(t[n].shape) if t[n].grad is None else t[n].grad.numpy()
+        np.testing.assert_allclose(out[GRAD_OF[n]], want, rtol=1e-11, atol=1e-12, err_msg=n)
+    assert tied == ("dW_V" not in out)
 
 
 def test_shared_kv_layer_matches_finite_differences_and_autograd():
