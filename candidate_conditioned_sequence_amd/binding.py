@@ -31,6 +31,7 @@ EXPORTS = [
     "whale_proj_qkv_bwd_workspace_size", "whale_proj_qkv_bwd",
     "whale_mfma_peak_probe",
     "whale_validate_offsets", "whale_debug_checks", "whale_debug_status",
+    "whale_jagged_xattn_bwd_noalloc",
 ]
 BAD_FIRST, BAD_ORDER, BAD_MAX_L, BAD_TOTAL, BAD_CAND_FIRST, BAD_CAND_ORDER, BAD_MAX_C = 1, 2, 4, 8, 16, 32, 64
 
@@ -56,6 +57,7 @@ _SIGS = {
     "whale_jagged_xattn_fwd_varc": (_I, [_D, _I, _P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_mfma_peak_probe": (_I, [_P, ctypes.c_int32, ctypes.c_int32, _P]),
     "whale_validate_offsets": (_I, [_D, _P, _P, _P, _P]),
+    "whale_jagged_xattn_bwd_noalloc": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P]),
     "whale_debug_checks": (ctypes.c_int32, [ctypes.c_int32]),
     "whale_debug_status": (_I, [_P, ctypes.c_int32, _P]),
     "whale_fusion_mlp": (_I, [_D, _I, _P, _P, _P, _I, _P, _P, _P]),
@@ -259,3 +261,13 @@ def whale_debug_status(flag, reset=False, stream=None):
         raise TypeError("flag must be an int32 tensor")
     rc = load().whale_debug_status(_ptr(flag), 1 if reset else 0, _stream(stream))
     _check("whale_debug_status", rc)
+
+
+def whale_jagged_xattn_bwd_noalloc(d_, Q, K, V, offsets, scale, A, lse, dA, dQ, dK, dV, stream=None):
+    rc = load().whale_jagged_xattn_bwd_noalloc(ctypes.byref(d_), _dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V),
+                                               _ptr(offsets), float(scale), _ptr(A), _ptr(lse), _ptr(dA), _ptr(dQ),
+                                               _ptr(dK), _ptr(dV), _stream(stream))
+    _check("whale_jagged_xattn_bwd_noalloc", rc)
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20   # the static scratch of whale_jagged_xattn_bwd_noalloc, per GPU

@@ -392,19 +392,31 @@ size_t whale_jagged_xattn_bwd_workspace_size(const whale_dims_t* dims, whale_dty
   return c.used;
 }
 
-whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
-                                      const void* V, const int64_t* offsets, float scale, const void* A,
-                                      const float* lse, const void* dA, void* dQ, void* dK, void* dV,
-                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
-  Shape s;
-  whale_status_t rc = check_dims(dims, dtype, &s);
+}  // extern "C"
+
+namespace {
+
+// Host checks of the attention backward, everything but the workspace.
+whale_status_t xattn_bwd_check(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                               const void* V, const int64_t* offsets, float scale, const void* A, const float* lse,
+                               const void* dA, void* dQ, void* dK, void* dV, Shape* s) {
+  whale_status_t rc = check_dims(dims, dtype, s);
   if (rc != WHALE_OK) return rc;
-  if (!Q || !offsets || !A || !lse || !dA || !dQ || !workspace) return WHALE_ERR_NULL;
-  if (s.T > 0 && (!K || !V || !dK)) return WHALE_ERR_NULL;
+  if (!Q || !offsets || !A || !lse || !dA || !dQ) return WHALE_ERR_NULL;
+  if (s->T > 0 && (!K || !V || !dK)) return WHALE_ERR_NULL;
   // dV = NULL: shared key-value form, V must be K; dK receives dK + dV.
-  if (s.T > 0 && !dV && V != K) return WHALE_ERR_SHAPE;
+  if (s->T > 0 && !dV && V != K) return WHALE_ERR_SHAPE;
   if (!(scale >= 0.f) || !std::isfinite(scale)) return WHALE_ERR_SHAPE;
-  if (ws_bytes < whale_jagged_xattn_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
+  return WHALE_OK;
+}
+
+// The launches, with the workspace carved from `workspace` (already checked
+// to hold whale_jagged_xattn_bwd_workspace_size bytes).  Every byte of it
+// that a kernel reads is written earlier in the same call, so its previous
+// contents never matter.
+whale_status_t xattn_bwd_launch(const Shape& s, whale_dtype_t dtype, const void* Q, const void* K, const void* V,
+                                const int64_t* offsets, float scale, const void* A, const float* lse,
+                                const void* dA, void* dQ, void* dK, void* dV, void* workspace, hipStream_t stream) {
   Carve c(workspace);
   XattnBwdArgs a;
   a.Q = Q; a.K = K; a.V = V; a.offsets = offsets; a.A = A; a.lse = lse; a.dA = dA;
@@ -417,6 +429,37 @@ whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dt
   whale_status_t g = debug_guard(s, offsets, nullptr, &a.guard, stream);
   if (g != WHALE_OK) return g;
   return ret(launch_xattn_bwd(a, dtype == WHALE_BF16, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                                      const void* V, const int64_t* offsets, float scale, const void* A,
+                                      const float* lse, const void* dA, void* dQ, void* dK, void* dV,
+                                      void* workspace, size_t ws_bytes, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = xattn_bwd_check(dims, dtype, Q, K, V, offsets, scale, A, lse, dA, dQ, dK, dV, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!workspace) return WHALE_ERR_NULL;
+  if (ws_bytes < whale_jagged_xattn_bwd_workspace_size(dims, dtype)) return WHALE_ERR_WORKSPACE;
+  return xattn_bwd_launch(s, dtype, Q, K, V, offsets, scale, A, lse, dA, dQ, dK, dV, workspace, stream);
+}
+
+whale_status_t whale_jagged_xattn_bwd_noalloc(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q,
+                                              const void* K, const void* V, const int64_t* offsets, float scale,
+                                              const void* A, const float* lse, const void* dA, void* dQ, void* dK,
+                                              void* dV, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = xattn_bwd_check(dims, dtype, Q, K, V, offsets, scale, A, lse, dA, dQ, dK, dV, &s);
+  if (rc != WHALE_OK) return rc;
+  // The shape's workspace must fit the library's static scratch; the size is
+  // known from the dims alone, so this is decided before touching the device.
+  if (whale_jagged_xattn_bwd_workspace_size(dims, dtype) > static_scratch_bytes()) return WHALE_ERR_WORKSPACE;
+  void* ws = static_scratch_device();   // this GPU's copy (looked up once per GPU)
+  if (ws == nullptr) return WHALE_ERR_LAUNCH;
+  return xattn_bwd_launch(s, dtype, Q, K, V, offsets, scale, A, lse, dA, dQ, dK, dV, ws, stream);
 }
 
 size_t whale_fusion_mlp_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype) {

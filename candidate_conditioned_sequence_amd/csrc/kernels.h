@@ -186,6 +186,12 @@ hipError_t launch_debug_status(int32_t* dst, int reset, hipStream_t st);
 bool debug_checks_on();
 int set_debug_checks(int on);
 
+// ------------------------------------------- static scratch (no-alloc call)
+// Size of the static device scratch, and its address on the current GPU
+// (looked up once per GPU; nullptr if the lookup fails).
+size_t static_scratch_bytes();
+void* static_scratch_device();
+
 // ---------------------------------------------------------------- misc
 // dst[c][col0 + r] = src[r][c] for a [rows, cols] matrix (data type), dst row stride ldd.
 hipError_t launch_transpose(const void* src, int rows, int cols, void* dst, int ldd, int col0,

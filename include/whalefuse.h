@@ -285,6 +285,28 @@ whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dt
  * dW_F = dZ^T [A, H_w] (fp32 [d, 2d]); dA = dZ W_F[:, :d];
  * dH_w = dF + dZ W_F[:, d:].  Z_saved is required for SiLU, ignored for none.
  */
+/*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): whale_jagged_xattn_bwd
+ * without a workspace argument.  Same arguments otherwise, same kernels and
+ * the same results bit for bit.  The workspace comes from a static device
+ * array of 32 MiB (33554432 bytes) that each GPU the library runs on holds
+ * from module load until the process ends; the call itself allocates
+ * nothing.  A shape whose
+ * whale_jagged_xattn_bwd_workspace_size exceeds that returns
+ * WHALE_ERR_WORKSPACE before anything is enqueued (the fixed-count layout
+ * needs M*h*4 bytes, plus S*2*T*d*4 when the dK/dV query split S > 1 is
+ * chosen for short histories).  Every call on a GPU shares that GPU's array:
+ * calls that overlap on one GPU (different streams, or graphs replayed
+ * concurrently) race and give wrong results.  Nothing in the array needs to
+ * start at zero: each byte a kernel reads is written earlier in the call.
+ */
+whale_status_t whale_jagged_xattn_bwd_noalloc(const whale_dims_t* dims, whale_dtype_t dtype,
+                                              const void* Q, const void* K, const void* V,
+                                              const int64_t* offsets, float scale, const void* A,
+                                              const float* lse, const void* dA, void* dQ, void* dK,
+                                              void* dV, hipStream_t stream);
+
 size_t whale_fusion_mlp_bwd_workspace_size(const whale_dims_t* dims, whale_dtype_t dtype);
 whale_status_t whale_fusion_mlp_bwd(const whale_dims_t* dims, whale_dtype_t dtype,
                                     const void* A, const void* H_w, const void* W_F,

@@ -137,3 +137,16 @@ def test_layer_rejects_inconsistent_shapes_on_the_host():
         lay.forward(Hw, Hs, off, 11)
     with pytest.raises(ValueError, match="rows"):
         lay.forward(Hw[:, :32], Hs, off, 6)
+
+
+def test_noalloc_backward_rejects_shapes_beyond_its_scratch():
+    """The no-alloc backward decides on the host, from the dims alone, that a
+    workspace larger than its static scratch does not fit."""
+    lib = wb.load()
+    fake = ctypes.c_void_p(256)
+    big = _dims(B=2048, C=64, n_q=32, d=256, h=4, max_L=100, total_L=1000)     # M*h*4 = 64 MiB
+    assert lib.whale_jagged_xattn_bwd_workspace_size(ctypes.byref(big), 1) > wb.NOALLOC_SCRATCH_BYTES
+    assert lib.whale_jagged_xattn_bwd_noalloc(ctypes.byref(big), 1, fake, fake, fake, fake, 0.0, fake, fake, fake,
+                                              fake, fake, fake, None) == 5
+    assert lib.whale_jagged_xattn_bwd_noalloc(ctypes.byref(_dims()), 1, None, fake, fake, fake, 0.0, fake, fake,
+                                              fake, fake, fake, fake, None) == 1
