@@ -389,6 +389,8 @@ size_t whale_jagged_xattn_bwd_workspace_size(const whale_dims_t* dims, whale_dty
   c.take((size_t)s.M * s.h * 4);
   const int splits = xattn_bwd_splits(s.B, s.h, s.QR, s.max_L, s.dh);
   if (splits > 1) c.take((size_t)splits * 2 * s.T * s.d * 4);
+  if (xattn_bwd_kv_schedule(s.max_L, s.dh, dtype == WHALE_BF16))
+    c.take((size_t)xattn_bwd_kv_qpartial_floats(s.M, s.d, s.max_L) * 4);
   return c.used;
 }
 
@@ -424,6 +426,11 @@ whale_status_t xattn_bwd_launch(const Shape& s, whale_dtype_t dtype, const void*
   a.Dbuf = (float*)c.take((size_t)s.M * s.h * 4);
   a.splits = xattn_bwd_splits(s.B, s.h, s.QR, s.max_L, s.dh);
   a.partial = a.splits > 1 ? (float*)c.take((size_t)a.splits * 2 * s.T * s.d * 4) : nullptr;
+  a.kv_schedule = xattn_bwd_kv_schedule(s.max_L, s.dh, dtype == WHALE_BF16);
+  if (a.kv_schedule) {
+    const int64_t qf = xattn_bwd_kv_qpartial_floats(s.M, s.d, s.max_L);
+    a.qpartial = qf > 0 ? (float*)c.take((size_t)qf * 4) : nullptr;
+  }
   a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh; a.max_L = s.max_L; a.T = s.T;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
   whale_status_t g = debug_guard(s, offsets, nullptr, &a.guard, stream);

@@ -30,9 +30,17 @@ struct XattnBwdArgs {
   int64_t T;
   float scale;
   const int32_t* guard = nullptr;   // as in XattnArgs
+  // KV-parallel schedule of the whole backward (one kernel forms dK, dV and
+  // dQ); qpartial [nkt, M, d] fp32 holds its dQ block partials when a
+  // history spans more than one 128-row block.
+  bool kv_schedule = false;
+  float* qpartial = nullptr;
 };
 hipError_t launch_xattn_bwd(const XattnBwdArgs& a, bool bf16_data, hipStream_t st);
 int xattn_bwd_splits(int B, int h, int QR, int max_L, int dh);
+// Schedule choice (env WHALE_XATTN_BWD_SCHEDULE = "kv" / "q" forces one).
+bool xattn_bwd_kv_schedule(int max_L, int dh, bool bf16_data);
+int64_t xattn_bwd_kv_qpartial_floats(int64_t M, int d, int max_L);
 
 // ---------------------------------------------------------------- norms
 // Row statistics (mean, rstd) of x [rows, n]; mean = 0 for RMSNorm.

@@ -21,6 +21,8 @@
 // of the next product, with the A operand read column-wise from the same
 // row-major LDS tile (transposing LDS reads) in the matching row order.
 // Deterministic: no atomics.
+#include <algorithm>
+#include <cstdlib>
 #include <type_traits>
 
 #include "common.h"
@@ -235,23 +237,38 @@ __global__ __launch_bounds__(NWQ * 64, DH >= 128 ? 1 : 2) void bwd_dq_kernel(
 // starting values.  bf16 folds c into the K fragments.  Query rows past the
 // split are loaded as copies of its last row with -lse2 = -inf, so P = 0 and
 // dS = 0 for them.
-template <typename T, int DH, int NWK>
+//
+// FQ (the KV-parallel schedule of the whole backward): the same kernel also
+// forms dQ, so the separate dQ kernel and its recomputation of S and dP are
+// not needed.  The workgroup's K rows (unscaled, rows past the history zero)
+// stay in LDS; every query tile's dS (this wave's 32 keys x 64 queries) goes
+// to LDS as [key][query], and after a barrier wave w forms dQ^T blocks of the
+// tile over all KB keys: A = K^T and B = dS^T, both by transposing reads with
+// the same key order.  When the history fits one block (nkt == 1) the tile's
+// dQ is complete and is stored (scaled, in the data type) straight to dQ;
+// otherwise it is this block's fp32 partial, stored to qpart[kt] for a
+// fixed-order sum over blocks.  D must be in Dbuf beforehand (rowdot kernel).
+template <typename T, int DH, int NWK, bool FQ = false>
 __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const T* __restrict__ dA, const float* __restrict__ lse,
     const float* __restrict__ Dbuf, T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ part,
     int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks,
-    const int32_t* __restrict__ guard) {
+    const int32_t* __restrict__ guard, T* __restrict__ dQ = nullptr, float* __restrict__ qpart = nullptr,
+    int64_t M_rows = 0) {
   if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int QT = 64, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (NWK * 64);
   constexpr int KB = NWK * 32;   // history rows per workgroup
+  constexpr int SLD = QT + 8;    // dS row stride (FQ)
   static_assert(NCH >= 1 && QT * CPR % (NWK * 64) == 0, "tile/threads mismatch");
   constexpr bool kFold = sizeof(T) == 2;
   __shared__ __attribute__((aligned(32))) T Qs[2][QT * KLD];
   __shared__ __attribute__((aligned(32))) T Gs[2][QT * KLD];
   __shared__ __attribute__((aligned(16))) float nl_s[2][QT];   // -lse2 (bf16) or lse2 (fp32)
   __shared__ __attribute__((aligned(16))) float nd_s[2][QT];   // -D
+  __shared__ __attribute__((aligned(32))) T Kl[FQ ? KB * KLD : 8];   // FQ: K rows of the block
+  __shared__ __attribute__((aligned(32))) T Sl[FQ ? KB * SLD : 8];   // FQ: dS of the tile, [key][query]
 
   const int split = blockIdx.y;
   const int lid = xcd_remap(blockIdx.x, nblocks);
@@ -260,14 +277,34 @@ __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
   const int j = bj % h, b = bj / h;
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
-  if (kt * KB >= L) return;                        // workgroup-uniform
   const int q_begin = split * qchunk;
   const int q_end = min(QR, q_begin + qchunk);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
+  if constexpr (FQ) {
+    // An empty history has dQ = 0; with dQ stored directly nobody else writes
+    // it (with partials the sum over no blocks gives 0).
+    if (L == 0 && kt == 0 && qpart == nullptr) {
+      for (int i = tid; i < (q_end - q_begin) * CPR; i += NWK * 64) {
+        const int64_t row = (int64_t)b * QR + q_begin + i / CPR;
+        st8<T>(dQ + row * d + j * DH + 8 * (i % CPR), zero8<T>());
+      }
+      return;
+    }
+  }
+  if (kt * KB >= L) return;                        // workgroup-uniform
   const int wu = __builtin_amdgcn_readfirstlane(w);   // wave index as a scalar
   const int key = kt * KB + w * 32 + l32;
   const bool kok = key < L;
   const int64_t qrow0 = (int64_t)b * QR;
+  if constexpr (FQ) {
+    // K rows of the block, unscaled; rows past the history are zero, so their
+    // (meaningless) dS adds nothing to dQ.  Visible after the first barrier.
+    for (int i = tid; i < KB * CPR; i += NWK * 64) {
+      const int row = i / CPR, e0 = 8 * (i % CPR);
+      const int kk = kt * KB + row;
+      st8<T>(&Kl[row * KLD + e0], kk < L ? ld8<T>(K + (lo + kk) * d + j * DH + e0) : zero8<T>());
+    }
+  }
 
   x8_t<T> kf[KS], vf[KS];
   {
@@ -385,6 +422,21 @@ __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
       }
       p_ds_pack<T>(s, dp, pf[qb], dsf[qb]);
     }
+    if constexpr (FQ) {
+      // This wave's dS into Sl[key][query]: element u of dsf[qb][mm] is query
+      // 32 qb + 16 mm + 4 hh + u (u < 4) or + 8 + (u - 4) (the accumulator rows).
+      T* srow = &Sl[(w * 32 + l32) * SLD + 4 * hh];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+          x4_t<T> a4, b4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) { a4[u] = dsf[qb][mm][u]; b4[u] = dsf[qb][mm][u + 4]; }
+          st4<T>(srow + 32 * qb + 16 * mm, a4);
+          st4<T>(srow + 32 * qb + 16 * mm + 8, b4);
+        }
+    }
 #pragma unroll
     for (int e = 0; e < NE; ++e)
 #pragma unroll
@@ -396,6 +448,40 @@ __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
         }
     store_tile(buf ^ 1);
     __syncthreads();
+    if constexpr (FQ) {
+      // dQ^T of the tile: block (e, qb) over the KB keys of the workgroup.
+      const int qt0 = q_begin + t * QT;
+      for (int blk = wu; blk < 2 * NE; blk += NWK) {
+        const int e = blk % NE, qb = blk / NE;
+        f32x16 acc = zero16();
+#pragma unroll
+        for (int ks = 0; ks < KB / 16; ++ks)
+          mma32(acc, lds_colA<T>(Kl, KLD, 16 * ks, 32 * e, lane), lds_colA<T>(Sl, SLD, 16 * ks, 32 * qb, lane));
+        const int q = qt0 + 32 * qb + l32;
+        if (q < q_end) {
+          if (qpart == nullptr) {
+            T* dst = dQ + (qrow0 + q) * d + j * DH + 32 * e + 4 * hh;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              x4_t<T> o;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) o[u] = from_f<T>(acc[4 * g + u] * scale);
+              st4<T>(dst + 8 * g, o);
+            }
+          } else {
+            float* dst = qpart + ((int64_t)kt * M_rows + qrow0 + q) * d + j * DH + 32 * e + 4 * hh;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              f32x4 o;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) o[u] = acc[4 * g + u] * scale;
+              *reinterpret_cast<f32x4*>(dst + 8 * g) = o;
+            }
+          }
+        }
+      }
+      __syncthreads();   // Sl is rewritten by the next tile
+    }
   }
 
   if (!kok) return;
@@ -455,8 +541,105 @@ __global__ __launch_bounds__(256) void kv_split_reduce_kernel(const float* __res
   else dV[i - n] = from_f<T>(s);
 }
 
+// D[m, j] = <dA[m, j], A[m, j]> for the KV-parallel schedule, in exactly the
+// order the dQ kernel's prologue uses (two fused-multiply-add chains over the
+// alternating 8-column groups, then their sum), so that both schedules see
+// the same D.
+template <typename T, int DH>
+__global__ __launch_bounds__(256) void rowdot_kernel(const T* __restrict__ A, const T* __restrict__ dA,
+                                                     float* __restrict__ D, int64_t Mh, int d, int h,
+                                                     const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= Mh) return;
+  const int64_t m = i / h;
+  const int j = (int)(i % h);
+  const T* a = A + m * d + j * DH;
+  const T* g = dA + m * d + j * DH;
+  float c0 = 0.f, c1 = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < DH / 16; ++ks) {
+    const x8_t<T> a0 = ld8<T>(a + 16 * ks), g0 = ld8<T>(g + 16 * ks);
+    const x8_t<T> a1 = ld8<T>(a + 16 * ks + 8), g1 = ld8<T>(g + 16 * ks + 8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      c0 = fmaf(to_f(a0[u]), to_f(g0[u]), c0);
+      c1 = fmaf(to_f(a1[u]), to_f(g1[u]), c1);
+    }
+  }
+  D[i] = c0 + c1;
+}
+
+// dQ = sum over the key blocks of the request (fixed order) of the fp32
+// partials qpart [nkt, M, d]; request b has ceil(L_b / kb) blocks.
+template <typename T>
+__global__ __launch_bounds__(256) void dq_reduce_kernel(const float* __restrict__ qpart,
+                                                        const int64_t* __restrict__ offsets, int QR, int kb,
+                                                        int64_t M, int d, T* __restrict__ dQ,
+                                                        const int32_t* __restrict__ guard) {
+  if (guard != nullptr && *guard != 0) return;
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= M * d) return;
+  const int64_t b = (i / d) / QR;
+  const int L = (int)(offsets[b + 1] - offsets[b]);
+  const int nk = (L + kb - 1) / kb;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < nk; ++k) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(qpart + (int64_t)k * M * d + i);
+    acc[0] += v[0]; acc[1] += v[1]; acc[2] += v[2]; acc[3] += v[3];
+  }
+  x4_t<T> o;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) o[u] = from_f<T>(acc[u]);
+  st4<T>(dQ + i, o);
+}
+
+// The KV-parallel schedule: D, then one kernel for dK, dV and dQ, then the
+// fixed-order sums of the dK/dV query splits and of the dQ block partials.
+template <typename T, int DH>
+hipError_t bwd_kv_t(const XattnBwdArgs& a, hipStream_t st) {
+  constexpr int NWK = 4, KB = NWK * 32;
+  const float c = a.scale * kLog2e;
+  const int64_t M = (int64_t)a.B * a.QR;
+  const int64_t Mh = M * a.h;
+  hipLaunchKernelGGL((rowdot_kernel<T, DH>), dim3((unsigned)((Mh + 255) / 256)), dim3(256), 0, st, (const T*)a.A,
+                     (const T*)a.dA, a.Dbuf, Mh, a.d, a.h, a.guard);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int qchunk = (a.QR + a.splits - 1) / a.splits;
+  qchunk = (qchunk + 63) / 64 * 64;
+  float* part = a.splits > 1 ? a.partial : nullptr;
+  const int nkt = std::max(1, (a.max_L + KB - 1) / KB);   // >= 1: empty histories still zero their dQ
+  float* qpart = nkt > 1 ? a.qpartial : nullptr;
+  const int64_t nblk = (int64_t)a.B * a.h * nkt;
+  hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, NWK, true>), dim3((unsigned)nblk, a.splits), dim3(NWK * 64), 0, st,
+                     (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf,
+                     (T*)a.dK, (T*)a.dV, part, a.d, a.h, a.QR, nkt, qchunk, c, a.scale, a.T, (int)nblk, a.guard,
+                     (T*)a.dQ, qpart, M);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.splits > 1 && a.T > 0) {
+    const int64_t n = a.T * a.d;
+    const int64_t nr = a.dV ? 2 * n : n;
+    hipLaunchKernelGGL(kv_split_reduce_kernel<T>, dim3((unsigned)((nr + 255) / 256)), dim3(256), 0, st, a.partial,
+                       a.splits, n, (T*)a.dK, (T*)a.dV, a.guard);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (qpart != nullptr) {
+    const int64_t n4 = M * a.d / 4;
+    hipLaunchKernelGGL(dq_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, qpart, a.offsets,
+                       a.QR, KB, M, a.d, (T*)a.dQ, a.guard);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
 template <typename T, int DH>
 hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
+  if constexpr (!(sizeof(T) == 4 && DH == 128)) {   // fp32 at d_h = 128: too much LDS for the fused kernel
+    if (a.kv_schedule) return bwd_kv_t<T, DH>(a, st);
+  }
   const float c = a.scale * kLog2e;
   hipError_t e;
   {
@@ -522,6 +705,23 @@ hipError_t bwd_dh(const XattnBwdArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+// Which schedule runs (see kernels.h).  Measured on MI355X (design notes):
+// the KV-parallel schedule wins only while a history fits one 128-row key
+// block, where it needs no dQ partials; past that the partials' traffic
+// costs more than the two recomputed products it saves.
+bool xattn_bwd_kv_schedule(int max_L, int dh, bool bf16_data) {
+  if (!bf16_data && dh > 64) return false;          // not built: LDS
+  const char* e = getenv("WHALE_XATTN_BWD_SCHEDULE");
+  if (e != nullptr && e[0] == 'k') return true;      // "kv": forced
+  if (e != nullptr && e[0] == 'q') return false;     // "q": forced
+  return max_L <= 128;
+}
+
+int64_t xattn_bwd_kv_qpartial_floats(int64_t M, int d, int max_L) {
+  const int nkt = (max_L + 127) / 128;
+  return nkt > 1 ? (int64_t)nkt * M * d : 0;
+}
 
 int xattn_bwd_splits(int B, int h, int QR, int max_L, int dh) {
   (void)dh;

@@ -478,3 +478,58 @@ def test_xattn_fwd_varc_equal_counts_match_fixed_call_bitwise(gpu):
     wb.whale_jagged_xattn_fwd_varc(dm, tQ, tK, tV, toff, i64_dev(offsets([C] * B), gpu), 0.0, A1, l1)
     torch.cuda.synchronize()
     assert torch.equal(A0, A1) and torch.equal(l0, l1)
+
+
+# The two schedules of the attention backward: the hybrid (Q-parallel dQ
+# kernel + KV-parallel dK/dV kernel) and the KV-parallel one (one kernel forms
+# dK, dV and dQ; dQ block partials summed in a fixed order when a history
+# spans several 128-row blocks).  WHALE_XATTN_BWD_SCHEDULE forces one.  Both
+# against the oracle; dK and dV bit for bit equal across the schedules (same
+# accumulation code, same D).
+KV_SCHED_CASES = [
+    # dtype, d, h, C, n_q, lengths, tied
+    ("bf16", 256, 4, 64, 32, [100, 128, 1, 0, 64], False),      # one block per history: the automatic choice
+    ("bf16", 128, 4, 16, 16, [1000, 333, 129, 0], False),       # several blocks: dQ partials
+    ("f32", 128, 2, 3, 5, [0, 1, 63, 64, 65, 257], False),      # query splits, partials
+    ("bf16", 256, 2, 20, 15, [130, 1, 700, 64], False),         # d_h = 128
+    ("bf16", 128, 4, 8, 16, [120, 5, 77], False),               # d_h = 32
+    ("bf16", 256, 4, 16, 32, [100, 7, 0, 128], True),           # shared key-value form
+]
+
+
+@pytest.mark.parametrize("case", KV_SCHED_CASES, ids=lambda c: f"{c[0]}-d{c[1]}h{c[2]}-C{c[3]}nq{c[4]}-L{c[5]}-t{c[6]}")
+def test_xattn_bwd_kv_schedule(gpu, case, monkeypatch):
+    dtype, d, h, C, n_q, L, tied = case
+    print(f"\n[xattn_bwd schedules] {case}", flush=True)
+    B = len(L)
+    M, off = B * C * n_q, offsets(L)
+    T = int(off[-1])
+    Q, K, dA = draw(81, (M, d), dtype), draw(82, (T, d), dtype), draw(84, (M, d), dtype)
+    V = K if tied else draw(83, (T, d), dtype)
+    dQ_ref, dK_ref, dV_ref = O.xattn_bwd(Q, K, V, off, C, n_q, h, None, dA)
+    if tied:
+        dK_ref, dV_ref = dK_ref + dV_ref, None
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tQ, tK, tdA = (to_dev(x, dtype, gpu) for x in (Q, K, dA))
+    tV = tK if tied else to_dev(V, dtype, gpu)
+    toff = i64_dev(off, gpu)
+    A, lse = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    wb.whale_jagged_xattn_fwd(dm, tQ, tK, tV, toff, 0.0, A, lse)
+    res = {}
+    for sched in ("q", "kv"):
+        monkeypatch.setenv("WHALE_XATTN_BWD_SCHEDULE", sched)
+        dQ, dK = torch.full_like(tQ, float("nan")), torch.full_like(tK, float("nan"))
+        dV = None if tied else torch.full_like(tV, float("nan"))
+        ws = torch.empty(wb.whale_jagged_xattn_bwd_workspace_size(dm, wb._dtype_code(tQ)), dtype=torch.uint8,
+                         device=gpu)
+        wb.whale_jagged_xattn_bwd(dm, tQ, tK, tV, toff, 0.0, A, lse, tdA, dQ, dK, dV, ws)
+        torch.cuda.synchronize()
+        res[sched] = (dQ, dK, dV)
+        print(f"  schedule {sched}:", flush=True)
+        assert_close("dQ", dQ, dQ_ref, dtype)
+        assert_close("dK", dK, dK_ref, dtype)
+        if not tied:
+            assert_close("dV", dV, dV_ref, dtype)
+    assert torch.equal(res["q"][1], res["kv"][1])
+    if not tied:
+        assert torch.equal(res["q"][2], res["kv"][2])
