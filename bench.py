@@ -39,15 +39,16 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 
-# HBM traffic of one xattn_fwd_pp_kernel<64> launch on the headline workload:
+# HBM traffic of one xattn_fwd_pp_kernel<64> launch on the headline workload
+# (profiles/hbm_traffic_c3_L10k_all_kernels.md):
 # rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what
 # the counter reads for a 512 MiB elementwise copy (x2.000 and x1.000), taken
 # on the kernel source whose SHA-256 prefix is recorded here.  When the source
 # differs, the figure no longer describes the kernel and is reported as null.
 XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_pp_kernel<64>", "config": "c3L10k",
                      "source": "candidate_conditioned_sequence_amd/csrc/xattn_fwd.hip",
-                     "source_sha256_16": "0584395df49f5bf5",
-                     "fetch_kib": 706662, "fetch_scale": 2.000, "write_kib": 140220, "write_scale": 1.000}
+                     "source_sha256_16": "13d6088ad67887c7",
+                     "fetch_kib": 706670, "fetch_scale": 2.000, "write_kib": 140375, "write_scale": 1.000}
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 # Per configuration: what one step covers, and the CPU-oracle sample.
