@@ -465,7 +465,10 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     // This group's share of tile u+2 goes out between the score MFMAs (the
     // last two steps reload the last tile, which is never stored).
     load_tile(min(u + 2, ntiles - 1), xl);
-    const uint32_t kaddr = kbase + (uint32_t)(u % kNBUF) * kBufBytes;
+    // (the buffer bases are opaque to the compiler, so every read below uses
+    // one base register and an immediate offset)
+    uint32_t kaddr = kbase + (uint32_t)(u % kNBUF) * kBufBytes;
+    __asm__("" : "+v"(kaddr));
     // Four independent score chains (kb, qb) interleaved: each accumulator
     // recurs every fourth MFMA.
     bf16x8 ka[2][KS];
@@ -491,7 +494,8 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     __builtin_amdgcn_sched_group_barrier(0x0020, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x0008, 8, 0);
     if (u >= 1) {
-      const uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kVBufBytes;
+      uint32_t vaddr = vbase + (uint32_t)((u + kNBUF - 1) % kNBUF) * kVBufBytes;
+      __asm__("" : "+v"(vaddr));
       // Four independent output chains (e, qb) interleaved.
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -526,22 +530,35 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
           for (int r = 0; r < 16; ++r)
             if (32 * kb + acc_row(r, hh) >= nvalid) s[kb][qb][r] = -INFINITY;
     }
-    float tmax[NQ];
-    bool need = u == 0;
+    // Does any score of this lane pass kTau?  A three-input max tree over the
+    // lane's 64 values, no exchange between lanes.  Only then (or on the
+    // first tile) are the column maxima formed and the reference moved: the
+    // same decisions as comparing every column maximum with kTau, for a
+    // third of the instructions.
+    float lm[8];
 #pragma unroll
-    for (int qb = 0; qb < NQ; ++qb) {
-      // four independent max chains, then combined
-      float m4[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) m4[v] = s[v >> 1][qb][8 * (v & 1)];
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-#pragma unroll
-        for (int r = 1; r < 8; ++r) m4[v] = fmaxf(m4[v], s[v >> 1][qb][8 * (v & 1) + r]);
-      tmax[qb] = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
-      need |= tmax[qb] > kTau;
+    for (int g = 0; g < 8; ++g) {
+      const int kb = g >> 2, qb = (g >> 1) & 1, r0 = 8 * (g & 1);
+      float m = fmaxf(fmaxf(s[kb][qb][r0], s[kb][qb][r0 + 1]), s[kb][qb][r0 + 2]);
+      m = fmaxf(fmaxf(m, s[kb][qb][r0 + 3]), s[kb][qb][r0 + 4]);
+      m = fmaxf(fmaxf(m, s[kb][qb][r0 + 5]), s[kb][qb][r0 + 6]);
+      lm[g] = fmaxf(m, s[kb][qb][r0 + 7]);
     }
-    if (__ballot(need)) {
+    const float lmax = fmaxf(fmaxf(fmaxf(lm[0], lm[1]), lm[2]), fmaxf(fmaxf(lm[3], lm[4]), lm[5]));
+    if (__ballot(u == 0 || fmaxf(lmax, fmaxf(lm[6], lm[7])) > kTau)) {
+      float tmax[NQ];
+#pragma unroll
+      for (int qb = 0; qb < NQ; ++qb) {
+        // four independent max chains, then combined
+        float m4[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v) m4[v] = s[v >> 1][qb][8 * (v & 1)];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int r = 1; r < 8; ++r) m4[v] = fmaxf(m4[v], s[v >> 1][qb][8 * (v & 1) + r]);
+        tmax[qb] = half_max(fmaxf(fmaxf(m4[0], m4[1]), fmaxf(m4[2], m4[3])));
+      }
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) {
         const float sh = (u == 0 || tmax[qb] > kTau) ? tmax[qb] : 0.f;
