@@ -63,6 +63,10 @@ reason in the design notes of the repository):
       of them attends the history of request b exactly as in Eq. (4); the
       K/V of a request are the same whichever candidates query them
       (Footnote 1, [PV ref]).
+  R12 HSTU self-attention (NEXT f4, the producer of H_s): causal pointwise
+      SiLU attention normalised by the history length, with a relative
+      position bias and a log2-bucketed time bias shared by all heads (the
+      pages name rab(p, t) without defining it; see hstu_attn_fwd).
 
 Layouts (row-vector convention y = x W^T, weights stored [out, in]):
   H_w, Q, A, F, Y : [M, d] with M = B*C*n_q, row m = (b*C + c)*n_q + i
@@ -367,3 +371,65 @@ def layer_bwd(H_w, H_s, offsets, C, n_q, h, p, dY, norm=NORM_LAYER, eps=1e-5,
     g.update(dg_q=pb["dg_q"], db_q=pb["db_q"], dg_kv=pb["dg_kv"], db_kv=pb["db_kv"])
     g.update(dA=dA, dQ=dQ, dK=dK, dV=dV, dF=dF)
     return g
+
+
+# ---------------------------------------------------------------- HSTU (NEXT f4)
+#
+# The pages describe the HSTU module, the producer of H_s, as sequential
+# attention with relative position-and-time biases [PV km], [GS 2.1], but do
+# not define the bias rab(p, t) (pith.science review page, referee minor
+# comment 2 on Eq. (2), which points to the HSTU paper, reference [34]).
+# Reading R12, the plainest one the pages and that reference support:
+#   * per request b, history rows i, j in [0, L_b), per head: causal
+#     (j <= i) pointwise attention, SiLU of the biased score in place of a
+#     softmax, normalised by the request's length:
+#       A_i = (1 / L_b) * sum_{j <= i} SiLU(scale * <q_i, k_j> + rab(i, j)) v_j
+#   * rab(i, j) = w_pos[min(i - j, NP - 1)] + w_time[bucket(tau_i - tau_j)],
+#     one position table [NP] and one time table [NT] shared by all heads;
+#   * bucket(delta) = min(floor(log2(max(delta, 1))), NT - 1) on the integer
+#     time difference (timestamps are int64; delta <= 1 gives bucket 0).
+
+def time_bucket(delta, n_time):
+    """floor(log2(max(delta, 1))) clipped to n_time - 1, on Python ints."""
+    out = np.zeros(np.shape(delta), dtype=np.int64)
+    flat = np.asarray(delta, dtype=np.int64).reshape(-1)
+    res = out.reshape(-1)
+    for n, dv in enumerate(flat.tolist()):
+        res[n] = min(max(int(dv), 1).bit_length() - 1, n_time - 1)
+    return out
+
+
+def hstu_rab(ts, w_pos, w_time):
+    """rab(i, j) of one request: [L, L] (entries with j > i are unused)."""
+    ts = np.asarray(ts, dtype=np.int64)
+    L = len(ts)
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    p = np.minimum(np.maximum(i - j, 0), len(w_pos) - 1)
+    t = time_bucket(ts[:, None] - ts[None, :], len(w_time))
+    return _f64(w_pos)[p] + _f64(w_time)[t]
+
+
+def hstu_attn_fwd(Q, K, V, offsets, h, timestamps, w_pos, w_time, scale=None):
+    """R12: causal pointwise (SiLU) jagged self-attention with relative
+    position-and-time bias, per request and head.  Q, K, V [T, d]; returns
+    A [T, d]."""
+    Q, K, V = _f64(Q), _f64(K), _f64(V)
+    offsets = np.asarray(offsets, dtype=np.int64)
+    T, d = Q.shape
+    dh = d // h
+    if scale is None or scale == 0.0:
+        scale = 1.0 / np.sqrt(dh)
+    A = np.zeros((T, d))
+    for b in range(len(offsets) - 1):
+        lo, hi = offsets[b], offsets[b + 1]
+        L = hi - lo
+        if L == 0:
+            continue
+        rab = hstu_rab(np.asarray(timestamps)[lo:hi], w_pos, w_time)
+        causal = np.tril(np.ones((L, L)))
+        for j in range(h):
+            cols = slice(j * dh, (j + 1) * dh)
+            s = scale * (Q[lo:hi, cols] @ K[lo:hi, cols].T) + rab
+            A[lo:hi, cols] = ((silu(s) * causal) @ V[lo:hi, cols]) / L
+    return A
