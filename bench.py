@@ -153,6 +153,51 @@ def cpu_baseline(cfg, key, n_req, backward, shared_kv=False):
                       f"{'...' if len(reqs) > 8 else ''}), {cfg.layers} layer(s), {what}, fp64 numpy"}
 
 
+def bench_hstu(args, torch, wb, synth, dev):
+    """HSTU self-attention forward on one configuration's histories: every
+    request attends causally over its own history (pairs = sum L_b (L_b + 1) / 2
+    per head), inputs N(0, 1) bf16 resident in HBM."""
+    key = "c5" if args.config == "c3L10k" else args.config
+    cfg = synth.CONFIGS[key]
+    L = synth.lengths(cfg)
+    off = synth.offsets_of(L)
+    T, d, h = int(off[-1]), cfg.d, cfg.h
+    print(f"[bench] hstu on {key} histories: B={cfg.B} T={T} d={d} h={h}", file=sys.stderr, flush=True)
+    g = torch.Generator(device=dev).manual_seed(0)
+    Q, K, V = (torch.randn(T, d, generator=g, device=dev).to(torch.bfloat16) for _ in range(3))
+    ts = torch.from_numpy(np.concatenate([synth.timestamps(cfg, b, L[b]) for b in range(cfg.B)])).to(dev)
+    wp, wt = (torch.from_numpy(x).to(dev) for x in synth.hstu_tables(cfg, 4096, 32))
+    toff = torch.from_numpy(off).to(dev)
+    dm = wb.dims(cfg.B, 1, 1, d, h, int(L.max()), T)
+    A = torch.empty_like(Q)
+
+    def call():
+        wb.whale_hstu_attn_fwd(dm, Q, K, V, toff, ts, wp, wt, 0.0, A)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        call()
+        e1.record()
+    torch.cuda.synchronize()
+    ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in ev]))
+    pairs = float(np.sum(L * (L + 1) // 2))
+    flop = 4.0 * d * pairs
+    scores = pairs * h
+    tflops = flop / (ms * 1e-3) / 1e12
+    res = {"metric": "HSTU self-attention TFLOP/s (causal pairs) and Gscore/s", "value": round(tflops, 2),
+           "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 3),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+           "config": {"workload": f"HSTU jagged causal self-attention with rab on the {key} histories", "name": key,
+                      "B": cfg.B, "d": d, "h": h, "T": T, "n_pos": 4096, "n_time": 32},
+           "gscore_per_s": round(scores / (ms * 1e-3) / 1e9, 1),
+           "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -166,6 +211,9 @@ def main():
                     help="forward only, each request with its own candidate count C_b ~ U{16..112} (mean 64)")
     ap.add_argument("--shared-kv", action="store_true",
                     help="shared key-value layer: one history-side projection whose output serves as K and V")
+    ap.add_argument("--hstu", action="store_true",
+                    help="time the HSTU self-attention (whale_hstu_attn_fwd) on the history shapes of --config "
+                         "(c5 by default for this mode), position table 4096, time table 32")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy (negation) of 512 MiB fp32, 3 times: the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -182,6 +230,8 @@ def main():
 
     wb.load()
     dev = torch.device("cuda:0")
+    if args.hstu:
+        return bench_hstu(args, torch, wb, synth, dev)
     key = args.config
     cfg = synth.CONFIGS[key]
     backward = SCOPE[key]["backward"] and not (args.fwd_only or args.serving)

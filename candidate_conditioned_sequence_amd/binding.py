@@ -32,6 +32,7 @@ EXPORTS = [
     "whale_mfma_peak_probe",
     "whale_validate_offsets", "whale_debug_checks", "whale_debug_status",
     "whale_jagged_xattn_bwd_noalloc",
+    "whale_hstu_attn_fwd",
 ]
 BAD_FIRST, BAD_ORDER, BAD_MAX_L, BAD_TOTAL, BAD_CAND_FIRST, BAD_CAND_ORDER, BAD_MAX_C = 1, 2, 4, 8, 16, 32, 64
 
@@ -57,6 +58,7 @@ _SIGS = {
     "whale_jagged_xattn_fwd_varc": (_I, [_D, _I, _P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_mfma_peak_probe": (_I, [_P, ctypes.c_int32, ctypes.c_int32, _P]),
     "whale_validate_offsets": (_I, [_D, _P, _P, _P, _P]),
+    "whale_hstu_attn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, _F, _P, _P]),
     "whale_jagged_xattn_bwd_noalloc": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P]),
     "whale_debug_checks": (ctypes.c_int32, [ctypes.c_int32]),
     "whale_debug_status": (_I, [_P, ctypes.c_int32, _P]),
@@ -271,3 +273,11 @@ def whale_jagged_xattn_bwd_noalloc(d_, Q, K, V, offsets, scale, A, lse, dA, dQ, 
 
 
 NOALLOC_SCRATCH_BYTES = 32 << 20   # the static scratch of whale_jagged_xattn_bwd_noalloc, per GPU
+
+
+def whale_hstu_attn_fwd(d_, Q, K, V, offsets, timestamps, w_pos, w_time, scale, A, stream=None):
+    """w_pos, w_time: fp32 device tensors (their lengths are n_pos, n_time)."""
+    rc = load().whale_hstu_attn_fwd(ctypes.byref(d_), _dtype_code(Q), _ptr(Q), _ptr(K), _ptr(V), _ptr(offsets),
+                                    _ptr(timestamps), _ptr(w_pos), int(w_pos.numel()), _ptr(w_time),
+                                    int(w_time.numel()), float(scale), _ptr(A), _stream(stream))
+    _check("whale_hstu_attn_fwd", rc)

@@ -19,7 +19,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-result"]
 SOURCES = ["api.cpp", "xattn_fwd.hip", "xattn_bwd.hip", "gemm.hip", "norm.hip", "rowstream.hip", "mfma_peak.hip",
-           "validate.hip", "scratch.hip"]
+           "validate.hip", "scratch.hip", "hstu.hip"]
 
 
 def _compile(src):

@@ -284,6 +284,28 @@ whale_status_t whale_jagged_xattn_fwd_varc(const whale_dims_t* dims, whale_dtype
   return xattn_fwd_call(dims, dtype, Q, K, V, offsets, cand_offsets, scale, A, lse, stream);
 }
 
+whale_status_t whale_hstu_attn_fwd(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
+                                   const void* V, const int64_t* offsets, const int64_t* timestamps,
+                                   const float* w_pos, int32_t n_pos, const float* w_time, int32_t n_time,
+                                   float scale, void* A, hipStream_t stream) {
+  Shape s;
+  whale_status_t rc = check_dims(dims, dtype, &s);
+  if (rc != WHALE_OK) return rc;
+  if (!offsets || !w_pos || !w_time) return WHALE_ERR_NULL;
+  if (s.T > 0 && (!Q || !K || !V || !A || !timestamps)) return WHALE_ERR_NULL;
+  if (!(scale >= 0.f) || !std::isfinite(scale)) return WHALE_ERR_SHAPE;
+  if (n_pos < 1 || n_pos > hstu_max_pos() || n_time < 1 || n_time > 32) return WHALE_ERR_UNSUPPORTED;
+  HstuArgs a;
+  a.Q = Q; a.K = K; a.V = V; a.offsets = offsets; a.timestamps = timestamps;
+  a.w_pos = w_pos; a.n_pos = n_pos; a.w_time = w_time; a.n_time = n_time; a.A = A;
+  a.B = s.B; a.d = s.d; a.h = s.h; a.dh = s.dh; a.max_L = s.max_L;
+  a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
+  whale_status_t g = debug_guard(s, offsets, nullptr, &a.guard, stream);
+  if (g != WHALE_OK) return g;
+  if (s.T == 0) return WHALE_OK;
+  return ret(launch_hstu_fwd(a, dtype == WHALE_BF16, stream));
+}
+
 whale_status_t whale_fusion_mlp(const whale_dims_t* dims, whale_dtype_t dtype, const void* A, const void* H_w,
                                 const void* W_F, whale_act_t act, void* F, void* Z_saved, hipStream_t stream) {
   Shape s;

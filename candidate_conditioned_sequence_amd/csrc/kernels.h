@@ -42,6 +42,21 @@ int xattn_bwd_splits(int B, int h, int QR, int max_L, int dh);
 bool xattn_bwd_kv_schedule(int max_L, int dh, bool bf16_data);
 int64_t xattn_bwd_kv_qpartial_floats(int64_t M, int d, int max_L);
 
+// ------------------------------------------------ HSTU self-attention
+// A [T, d] = causal SiLU self-attention with relative position / time bias
+// per request and head (see hstu.hip).  n_pos <= hstu_max_pos(),
+// 1 <= n_time <= 32.
+struct HstuArgs {
+  const void* Q; const void* K; const void* V; const int64_t* offsets; const int64_t* timestamps;
+  const float* w_pos; int n_pos; const float* w_time; int n_time;
+  void* A;
+  int B, d, h, dh, max_L;
+  float scale;
+  const int32_t* guard = nullptr;   // as in XattnArgs
+};
+hipError_t launch_hstu_fwd(const HstuArgs& a, bool bf16_data, hipStream_t st);
+int hstu_max_pos();
+
 // ---------------------------------------------------------------- norms
 // Row statistics (mean, rstd) of x [rows, n]; mean = 0 for RMSNorm.
 // kind: 0 LayerNorm, 1 RMSNorm.

@@ -18,7 +18,7 @@ from dataclasses import dataclass, field, replace
 import numpy as np
 
 # tensor ids for the seed key
-T_LEN, T_HW, T_HS, T_DY, T_CAND = 0, 1, 2, 3, 4
+T_LEN, T_HW, T_HS, T_DY, T_CAND, T_TS = 0, 1, 2, 3, 4, 5
 T_WQ, T_WK, T_WV, T_WF, T_WU, T_WG, T_WD = 10, 11, 12, 13, 14, 15, 16
 T_GQ, T_BQ, T_GKV, T_BKV, T_GF, T_BF = 20, 21, 22, 23, 24, 25
 
@@ -196,6 +196,24 @@ def layer_params(cfg, layer=0, gate="shared", random_affine=False):
         else:
             p[name] = np.zeros(d, dtype=np.float32)
     return p
+
+
+def timestamps(cfg, b, L_b):
+    """Event times (int64 seconds) of request b's history: a start in 2023
+    plus integer gaps of floor(exp(N(4, 2))) seconds (median about a minute,
+    from none to days), so time differences cover the log2 buckets from 0 to
+    about 25.  A request of 15000 events spans about 7e6 s, far inside 2^30."""
+    r = _rng(cfg, 0, T_TS, b)
+    start = 1_672_531_200 + int(r.integers(0, 10 ** 7))
+    gaps = np.floor(np.exp(4.0 + 2.0 * r.standard_normal(int(L_b)))).astype(np.int64)
+    return start + np.cumsum(gaps)
+
+
+def hstu_tables(cfg, n_pos, n_time, layer=0):
+    """Relative-bias tables of the HSTU attention: w_pos [n_pos], w_time
+    [n_time], N(0, 0.5) fp32."""
+    r = _rng(cfg, layer, T_TS, 10 ** 6)
+    return (0.5 * r.standard_normal(n_pos)).astype(np.float32), (0.5 * r.standard_normal(n_time)).astype(np.float32)
 
 
 def inputs(cfg, layer=0, requests=None):

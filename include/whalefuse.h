@@ -285,6 +285,38 @@ whale_status_t whale_jagged_xattn_bwd(const whale_dims_t* dims, whale_dtype_t dt
  * dW_F = dZ^T [A, H_w] (fp32 [d, 2d]); dA = dZ W_F[:, :d];
  * dH_w = dF + dZ W_F[:, d:].  Z_saved is required for SiLU, ignored for none.
  */
+/* ------------------------------------------------- HSTU self-attention */
+
+/*
+ * NEXT f4: the HSTU module's jagged self-attention over each request's own
+ * history, which produces the states H_s the fusion attention reads ([PV km]:
+ * a sequential attention block with relative position-and-time biases;
+ * [GS 2.1]).  The pages leave the bias rab(p, t) undefined (pith.science
+ * review page, referee minor comment on Eq. (2), pointing to the HSTU paper,
+ * their reference [34]); this call computes the reading
+ *   A[lo_b + i, head] = (1 / L_b) * sum over j <= i of
+ *                       SiLU(scale * <Q_i, K_j> + w_pos[min(i - j, n_pos - 1)]
+ *                            + w_time[min(floor(log2(max(tau_i - tau_j, 1))), n_time - 1)]) * V_j
+ * for rows i, j of request b (0 <= i, j < L_b; tau = timestamps), per head
+ * (columns head*d_h .. head*d_h + d_h - 1), with both tables shared by all
+ * heads: causal, pointwise (SiLU instead of a softmax), normalised by the
+ * request's length.
+ *
+ * Q, K, V, A: [T, d] in dtype (T = dims->total_L; all rows are history rows);
+ * offsets [B+1] int64; timestamps [T] int64; w_pos [n_pos] and w_time
+ * [n_time] fp32.  scale == 0 selects 1/sqrt(d_h).  Only dims->B, d, h, max_L
+ * and total_L are used (C and n_q must be positive; pass 1).  Contract:
+ * every timestamp of a request differs from the request's first one by less
+ * than 2^30 (time differences are exact in 32-bit integers).  1 <= n_pos <=
+ * 4096 and 1 <= n_time <= 32, else WHALE_ERR_UNSUPPORTED.  An empty request
+ * leaves no rows.  Forward only.
+ */
+whale_status_t whale_hstu_attn_fwd(const whale_dims_t* dims, whale_dtype_t dtype,
+                                   const void* Q, const void* K, const void* V,
+                                   const int64_t* offsets, const int64_t* timestamps,
+                                   const float* w_pos, int32_t n_pos, const float* w_time,
+                                   int32_t n_time, float scale, void* A, hipStream_t stream);
+
 /*
  * For callers that cannot allocate (code under HIP graph capture, tight
  * serving loops, harnesses that forbid hipMalloc): whale_jagged_xattn_bwd

@@ -390,13 +390,17 @@ def layer_bwd(H_w, H_s, offsets, C, n_q, h, p, dY, norm=NORM_LAYER, eps=1e-5,
 #     time difference (timestamps are int64; delta <= 1 gives bucket 0).
 
 def time_bucket(delta, n_time):
-    """floor(log2(max(delta, 1))) clipped to n_time - 1, on Python ints."""
-    out = np.zeros(np.shape(delta), dtype=np.int64)
-    flat = np.asarray(delta, dtype=np.int64).reshape(-1)
-    res = out.reshape(-1)
-    for n, dv in enumerate(flat.tolist()):
-        res[n] = min(max(int(dv), 1).bit_length() - 1, n_time - 1)
-    return out
+    """floor(log2(max(delta, 1))) clipped to n_time - 1.  Below 2^53 the
+    difference is exact in float64 and frexp's exponent e (x = m 2^e with
+    0.5 <= m < 1) gives floor(log2 x) = e - 1 exactly; larger values take
+    Python's integer bit length."""
+    d = np.maximum(np.asarray(delta, dtype=np.int64), 1)
+    _, e = np.frexp(d.astype(np.float64))
+    out = e.astype(np.int64) - 1
+    big = d >= 2 ** 53
+    if big.any():
+        out[big] = [int(v).bit_length() - 1 for v in d[big].tolist()]
+    return np.minimum(out, n_time - 1)
 
 
 def hstu_rab(ts, w_pos, w_time):
