@@ -13,11 +13,15 @@
 //
 // Design (gfx950):
 //  * One workgroup = 4 waves = one (request, head, block of 128 queries);
-//    each wave owns 32 queries.  Blocks are issued in descending order of
-//    their index within a request, so the long rows of the causal triangle
-//    start first.  A block walks the key tiles (64 history rows) up to its
-//    last query; K/V tiles are staged in LDS with the tile's relative
-//    timestamps.
+//    each wave owns 32 queries.  A block walks the key tiles (64 history
+//    rows) up to its last query; K/V tiles are staged in LDS with the tile's
+//    timestamps.  The work of a block grows with its index within the
+//    request, and the work of a request with the square of its length, so
+//    workgroups are issued level by level: every request's last query block
+//    first, then every request's second-to-last, and so on (longest first).
+//    Workgroups go to the XCDs round-robin, so the (request, head) order is
+//    rotated by one per level: a pair lands on a different XCD at each
+//    level, and no XCD collects the long requests.
 //  * S^T = K Q^T with 32x32x16 MFMA (lane = query column, 16 key rows per
 //    lane and 32-row block), then per element: the position bias, the time
 //    bias by an LDS gather at the leading-bit position of the saturated time
@@ -56,7 +60,7 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 2) void hs
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ ts, const float* __restrict__ w_pos,
     int n_pos, const float* __restrict__ w_time, int n_time, T* __restrict__ A, int d, int h, int nqb,
-    float scale, int nblocks, const int32_t* __restrict__ guard) {
+    float scale, int nbh, const int32_t* __restrict__ guard) {
   if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int KS = DH / 16, NE = DH / 32, KLD = DH + 8, CPR = DH / 8;
   constexpr int NCH = kHBN * CPR / 256;
@@ -71,9 +75,9 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 2) void hs
   // leading zeros; Wt[0] (difference 0, leading-bit search -1) = w_time[0].
   __shared__ float Wt[33];
 
-  const int lid = xcd_remap(blockIdx.x, nblocks);
-  const int qbi = nqb - 1 - lid % nqb;
-  const int bj = lid / nqb;
+  const int level = blockIdx.x / nbh;           // nbh = B * h blocks per level
+  const int qbi = nqb - 1 - level;
+  const int bj = (int)((blockIdx.x % nbh + qbi) % nbh);
   const int j = bj % h, b = bj / h;
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
@@ -246,9 +250,10 @@ hipError_t launch_hstu_t(const HstuArgs& a, hipStream_t st) {
   const int nqb = (a.max_L + kHQB - 1) / kHQB;
   const int64_t nblk = (int64_t)a.B * a.h * nqb;
   if (nblk == 0) return hipSuccess;
+  if (nblk * 256 >= (int64_t{1} << 32)) return hipErrorInvalidValue;   // work-item count of one launch
   hipLaunchKernelGGL((hstu_fwd_kernel<T, DH>), dim3((unsigned)nblk), dim3(256), 0, st, (const T*)a.Q,
                      (const T*)a.K, (const T*)a.V, a.offsets, a.timestamps, a.w_pos, a.n_pos, a.w_time, a.n_time,
-                     (T*)a.A, a.d, a.h, nqb, a.scale, (int)nblk, a.guard);
+                     (T*)a.A, a.d, a.h, nqb, a.scale, a.B * a.h, a.guard);
   return hipGetLastError();
 }
 
