@@ -155,6 +155,21 @@ WHALE_DEV int xcd_remap(int id, int n) {
   return x * per + (x < rem ? x : rem) + i;
 }
 
+// Order for grids whose logical id is pair * nb + k, a pair being one
+// (request, head) whose nb blocks read the same rows and whose work grows
+// with the request's length.  With contiguous ranges (xcd_remap) each XCD
+// would take one eighth of the batch, and the lengths of a few neighbouring
+// requests can differ widely; here XCD x takes pairs x, x + 8, x + 16, ...
+// whole and in that order, so a pair's blocks still share one L2 while each
+// XCD sees a spread of the batch.  Pairs past the last full group of eight
+// keep the plain order.  A bijection on [0, npairs * nb).
+WHALE_DEV int pair_xcd_order(int id, int nb, int npairs) {
+  const int full = (npairs / 8) * 8 * nb;   // blocks of complete groups of 8 pairs
+  if (id >= full) return id;
+  const int x = id % 8, i = id / 8;
+  return ((i / nb) * 8 + x) * nb + i % nb;
+}
+
 WHALE_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 // Logistic sigmoid with the hardware reciprocal (about 1 ulp): the IEEE
 // division sequence would cost ten instructions per element in the gate and

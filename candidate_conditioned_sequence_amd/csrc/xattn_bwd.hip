@@ -83,7 +83,7 @@ __global__ __launch_bounds__(NWQ * 64, DH >= 128 ? 1 : 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(32))) T Ks[2][BN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][BN * KLD];
 
-  const int lid = xcd_remap(blockIdx.x, nblocks);
+  const int lid = pair_xcd_order(blockIdx.x, nqb, nblocks / nqb);
   const int qbi = lid % nqb;
   const int bj = lid / nqb;
   const int j = bj % h, b = bj / h;
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
   __shared__ __attribute__((aligned(32))) T Sl[FQ ? KB * SLD : 8];   // FQ: dS of the tile, [key][query]
 
   const int split = blockIdx.y;
-  const int lid = xcd_remap(blockIdx.x, nblocks);
+  const int lid = pair_xcd_order(blockIdx.x, nkt, nblocks / nkt);
   const int kt = lid % nkt;
   const int bj = lid / nkt;
   const int j = bj % h, b = bj / h;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(kNW * 64, DH >= 128 ? 1 : 2) void xattn_fwd_kernel(
   __shared__ __attribute__((aligned(32))) T Ks[2][kBN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][kBN * KLD];
 
-  const int lid = xcd_remap(blockIdx.x, nblocks);
+  const int lid = pair_xcd_order(blockIdx.x, nqb, nblocks / nqb);
   const int qbi = lid % nqb;
   const int bj = lid / nqb;
   const int j = bj % h, b = bj / h;
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   __shared__ __attribute__((aligned(32))) bf16 Ks[kNBUF][kBN * KLD];
   __shared__ __attribute__((aligned(32))) bf16 Vs[kNBUF][kBN * VLD];
 
-  const int lid = xcd_remap(blockIdx.x, nblocks);
+  const int lid = pair_xcd_order(blockIdx.x, nqb, nblocks / nqb);
   const int qbi = lid % nqb;
   const int bj = lid / nqb;
   const int j = bj % h, b = bj / h;
