@@ -56,7 +56,7 @@ __device__ __forceinline__ int leading_zeros_or_m1(uint32_t x) {
 }
 
 template <typename T, int DH>
-__global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 2) void hstu_fwd_kernel(
+__global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hstu_fwd_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const int64_t* __restrict__ ts, const float* __restrict__ w_pos,
     int n_pos, const float* __restrict__ w_time, int n_time, T* __restrict__ A, int d, int h, int nqb,
@@ -172,28 +172,28 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 2) void hs
     // [0, NP - 1]: no clamp, no mask), else edge (clamp and causal mask).
     const bool far = qw - (j0 + kHBN - 1) >= n_pos - 1;
     const bool interior = !far && j0 + kHBN - 1 <= qw && qw + 31 - j0 <= n_pos - 1;
+    // With y = -log2(e) x, SiLU(x) = -ln(2) y / (1 + 2^y): the factor -ln(2)
+    // is applied once to the output, so each element costs one fused
+    // multiply-add, an exp2, an add, a reciprocal and a multiply.  Interior
+    // tiles read the position table at one base address (row offsets become
+    // immediates).  The mode is uniform over the tile, so one branch covers
+    // all 32 elements of the lane and they can be interleaved.
     x8_t<T> pf[2][2];
+    auto elems = [&](auto modec) {
+      constexpr int kMode = decltype(modec)::value;   // 0 edge, 1 interior, 2 far
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // relative timestamps of this lane's 16 rows: 4-row groups
-      uint32_t tj[16];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const uint4 v4 = *reinterpret_cast<const uint4*>(&Ts[buf][32 * kb + 8 * g + 4 * hh]);
-        tj[4 * g + 0] = v4.x;
-        tj[4 * g + 1] = v4.y;
-        tj[4 * g + 2] = v4.z;
-        tj[4 * g + 3] = v4.w;
-      }
-      // With y = -log2(e) x, SiLU(x) = -ln(2) y / (1 + 2^y): the factor
-      // -ln(2) is applied once to the output, so each element costs one
-      // fused multiply-add, an exp2, an add, a reciprocal and a multiply.
-      // Interior tiles read the position table at one base address (row
-      // offsets become immediates).
-      float p[16];
-      auto elems = [&](auto modec) {
-        constexpr int kMode = decltype(modec)::value;   // 0 edge, 1 interior, 2 far
+      for (int kb = 0; kb < 2; ++kb) {
         const float* wrow = kMode == 1 ? &Wp[i - j0 - 32 * kb - 4 * hh - 27] : Wp;
+        uint32_t tj[16];   // timestamps of this lane's 16 rows (4-row groups)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint4 v4 = *reinterpret_cast<const uint4*>(&Ts[buf][32 * kb + 8 * g + 4 * hh]);
+          tj[4 * g + 0] = v4.x;
+          tj[4 * g + 1] = v4.y;
+          tj[4 * g + 2] = v4.z;
+          tj[4 * g + 3] = v4.w;
+        }
+        float p[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jj = j0 + 32 * kb + acc_row(r, hh);
@@ -207,17 +207,16 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 2) void hs
           const float pr = y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(y));
           p[r] = (kMode != 0 || jj <= i) ? pr : 0.f;
         }
-      };
-      if (far) elems(std::integral_constant<int, 2>());
-      else if (interior) elems(std::integral_constant<int, 1>());
-      else elems(std::integral_constant<int, 0>());
-      // packed pairwise into the B operands, in accumulator row order
+        // packed pairwise into the B operands, in accumulator row order
 #pragma unroll
-      for (int mm = 0; mm < 2; ++mm) {
+        for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) pf[kb][mm][u] = from_f<T>(p[8 * mm + u]);
+          for (int u = 0; u < 8; ++u) pf[kb][mm][u] = from_f<T>(p[8 * mm + u]);
       }
-    }
+    };
+    if (far) elems(std::integral_constant<int, 2>());
+    else if (interior) elems(std::integral_constant<int, 1>());
+    else elems(std::integral_constant<int, 0>());
     // O^T[e][q] += V^T[e][key] P^T[key][q]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
