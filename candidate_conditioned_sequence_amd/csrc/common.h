@@ -171,6 +171,8 @@ WHALE_DEV int pair_xcd_order(int id, int nb, int npairs) {
 }
 
 WHALE_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+// max of three (one v_max3_f32: the inner max has no other use)
+WHALE_DEV float max3f(float a, float b, float c) { return fmaxf(fmaxf(a, b), c); }
 // Logistic sigmoid with the hardware reciprocal (about 1 ulp): the IEEE
 // division sequence would cost ten instructions per element in the gate and
 // activation prologues / epilogues.  1 + e^-z = inf gives 0, as it should.

@@ -208,13 +208,18 @@ __global__ __launch_bounds__(kNW * 64, DH >= 128 ? 1 : 2) void xattn_fwd_kernel(
           for (int r = 0; r < 16; ++r) s[kb][qb][r] = scaled_arg<T>(s[kb][qb][r], c, mref[qb]);
     }
     if (nvalid < kBN) {
+      // row 32 kb + acc_row(r, hh) >= nvalid, as 4 hh against a uniform
+      // bound; h4 is opaque, so the 32 row indices are not hoisted out of
+      // the loop into registers of their own
+      int h4 = 4 * hh;
+      __asm__ volatile("" : "+v"(h4));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * kb + acc_row(r, hh) >= nvalid) s[kb][qb][r] = -INFINITY;
+            if (h4 >= nvalid - (32 * kb + acc_row(r, 0))) s[kb][qb][r] = -INFINITY;
     }
 
     // Tile max of t per query column (both lane halves).  The first tile
@@ -522,30 +527,38 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     if (u + 1 < ntiles) store_tile((u + 1) % kNBUF, xs);
     const int nvalid = min(kBN, L - u * kBN);
     if (nvalid < kBN) {
+      // row 32 kb + acc_row(r, hh) >= nvalid, as 4 hh against a uniform
+      // bound; h4 is opaque, so the 32 row indices are not hoisted out of
+      // the loop into registers of their own
+      int h4 = 4 * hh;
+      __asm__ volatile("" : "+v"(h4));
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < NQ; ++qb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (32 * kb + acc_row(r, hh) >= nvalid) s[kb][qb][r] = -INFINITY;
+            if (h4 >= nvalid - (32 * kb + acc_row(r, 0))) s[kb][qb][r] = -INFINITY;
     }
-    // Does any score of this lane pass kTau?  A three-input max tree over the
-    // lane's 64 values, no exchange between lanes.  Only then (or on the
-    // first tile) are the column maxima formed and the reference moved: the
-    // same decisions as comparing every column maximum with kTau, for a
-    // third of the instructions.
-    float lm[8];
+    // Does any score of this lane pass kTau?  A balanced three-input max
+    // tree over the lane's 64 values (32 instructions), no exchange between
+    // lanes.  Only then (or on the first tile) are the column maxima formed
+    // and the reference moved: the same decisions as comparing every column
+    // maximum with kTau.
+    float lv[22];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      const int kb = g >> 2, qb = (g >> 1) & 1, r0 = 8 * (g & 1);
-      float m = fmaxf(fmaxf(s[kb][qb][r0], s[kb][qb][r0 + 1]), s[kb][qb][r0 + 2]);
-      m = fmaxf(fmaxf(m, s[kb][qb][r0 + 3]), s[kb][qb][r0 + 4]);
-      m = fmaxf(fmaxf(m, s[kb][qb][r0 + 5]), s[kb][qb][r0 + 6]);
-      lm[g] = fmaxf(m, s[kb][qb][r0 + 7]);
+    for (int i = 0; i < 21; ++i) {
+      const int a = 3 * i;
+      lv[i] = max3f(s[a >> 5][(a >> 4) & 1][a & 15], s[(a + 1) >> 5][((a + 1) >> 4) & 1][(a + 1) & 15],
+                    s[(a + 2) >> 5][((a + 2) >> 4) & 1][(a + 2) & 15]);
     }
-    const float lmax = fmaxf(fmaxf(fmaxf(lm[0], lm[1]), lm[2]), fmaxf(fmaxf(lm[3], lm[4]), lm[5]));
-    if (__ballot(u == 0 || fmaxf(lmax, fmaxf(lm[6], lm[7])) > kTau)) {
+    lv[21] = s[1][1][15];
+    float l2[8];
+#pragma unroll
+    for (int i = 0; i < 7; ++i) l2[i] = max3f(lv[3 * i], lv[3 * i + 1], lv[3 * i + 2]);
+    l2[7] = lv[21];
+    const float lmax = fmaxf(max3f(l2[0], l2[1], l2[2]), max3f(max3f(l2[3], l2[4], l2[5]), l2[6], l2[7]));
+    if (__ballot(u == 0 || lmax > kTau)) {
       float tmax[NQ];
 #pragma unroll
       for (int qb = 0; qb < NQ; ++qb) {
