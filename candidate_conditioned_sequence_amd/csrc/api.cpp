@@ -200,6 +200,27 @@ whale_status_t whale_proj_qkv(const whale_dims_t* dims, whale_dtype_t dtype, con
     }
     return WHALE_OK;
   }
+  if (bf && s.d == 512 && rs_fwd_groups_ok(s.d, s.d) && rs_fwd_groups_ok(s.d, nkv)) {
+    // d = 512: the same kernels in column groups of 256 (2 for Q, 4 for K
+    // and V); the groups of one row block share an XCD, so the rows are read
+    // from HBM once.  Group 0 writes X_q / X_s and the statistics.
+    RsFwdArgs q{};
+    q.H = (const __bf16*)H_w; q.ldh = s.d; q.W = (const __bf16*)W_Q; q.W2 = (const __bf16*)W_Q; q.nsplit = s.d;
+    q.Y = (__bf16*)Q; q.Y2 = (__bf16*)Q; q.ldy = s.d;
+    q.Xn = nrm ? (__bf16*)X_q : nullptr; q.stats = nrm ? stats_q : nullptr;
+    q.gamma = g_q; q.beta = b_q; q.M = s.M; q.kind = nk; q.eps = eps;
+    q.gate = 0; q.ngroups = s.d / 256; q.Z = nullptr; q.ldz = 0;
+    WHALE_TRY(launch_rs_fwd(q, s.d, 256, stream));
+    if (s.T > 0) {
+      RsFwdArgs kv = q;
+      kv.H = (const __bf16*)H_s; kv.W = (const __bf16*)W_K; kv.W2 = (const __bf16*)(tied ? W_K : W_V);
+      kv.Y = (__bf16*)K; kv.Y2 = (__bf16*)(tied ? K : V);
+      kv.Xn = nrm ? (__bf16*)X_s : nullptr; kv.stats = nrm ? stats_kv : nullptr;
+      kv.gamma = g_kv; kv.beta = b_kv; kv.M = s.T; kv.ngroups = nkv / 256;
+      WHALE_TRY(launch_rs_fwd(kv, s.d, 256, stream));
+    }
+    return WHALE_OK;
+  }
   // Each input is normalised either once into X_q / X_s (statistics computed
   // in the same pass) or, without them, per tile in the GEMM prologue.
   const bool mq = nrm && X_q != nullptr, ms = nrm && X_s != nullptr && s.T > 0;
@@ -366,7 +387,11 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype, c
   GemmArgs b = gemm_defaults();
   b.X = G; b.ldx = H; b.W = W_D; b.ldw = H; b.Y = Y; b.ldy = s.d; b.R = F; b.ldr = s.d;
   b.M = s.M; b.N = s.d; b.K = H; b.pro = PRO_PLAIN; b.epi = EPI_RESID;
-  constexpr int kGroup = 512;   // up-projection columns per row-streaming workgroup
+  // Up-projection columns per row-streaming workgroup.  (At d = 512 the
+  // row-streaming kernel runs in column groups of 256 and measured no faster
+  // than the tiled path once the down projection forms the gate in its
+  // prologue, so d = 512 keeps the tiled path.)
+  constexpr int kGroup = 512;
   if (bf && gate == WHALE_GATE_SHARED && rs_fwd_ok(s.d, kGroup) && H % kGroup == 0 && 256 % (8 * (H / kGroup)) == 0) {
     // Up projection by the row-streaming kernel: Norm_f (statistics saved
     // for the backward), F W_U^T and the tied gate in one pass over F.

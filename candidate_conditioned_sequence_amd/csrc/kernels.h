@@ -122,7 +122,8 @@ inline int64_t gemm_norm_bwd_tiles(int64_t M) { return (M + 63) / 64; }
 // the rows are normalised (gamma, beta over K; beta unused for kind 1) and
 // the normalised rows go to Xn [M, K] and (mean, rstd) to stats [M, 2] when
 // those are given (by column group 0); kind 2 multiplies H as it is.
-// Shapes: rs_fwd_ok(K, N).
+// Shapes: rs_fwd_ok(K, N); at K = 512 (gate 0, norm allowed) also N = 256
+// per column group with ngroups > 1 (rs_fwd_groups_ok(K, ngroups N)).
 struct RsFwdArgs {
   const __bf16* H; int64_t ldh;
   const __bf16* H2; int64_t ldh2;   // gate = 4: columns [256, 512) of the rows
@@ -160,6 +161,7 @@ struct RsBwdArgs {
   int64_t M; int kind;
 };
 bool rs_fwd_ok(int K, int N);
+bool rs_fwd_groups_ok(int K, int Ntot);   // K = 512, Ntot a multiple of 256 (column groups of 256)
 bool rs_bwd_ok(int K, int N);
 int64_t rs_bwd_grid(int64_t M);
 hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st);

@@ -176,8 +176,9 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   constexpr int BLK = kRB * K * 2;                 // bytes per block
   constexpr int NI = BLK / 1024;                   // transfer instructions per block
   constexpr int IPW = NI / NW;                     // ... per wave
-  constexpr int NBUF = (EPI == 3 || EPI == 4) ? 2 : 4;
-  static_assert(NI % NW == 0 && IPW >= 1 && (K == 256 || (K == 512 && EPI == 4)), "panels, whole instructions");
+  constexpr int NBUF = (EPI == 3 || EPI == 4) ? 2 : (K == 512 ? 3 : 4);
+  static_assert(NI % NW == 0 && IPW >= 1 && (K == 256 || (K == 512 && N == 256 && (EPI == 0 || EPI == 4))),
+                "panels, whole instructions");
   __shared__ __attribute__((aligned(1024))) char xs[NBUF][BLK];
   __shared__ __attribute__((aligned(1024))) char zb[EPI == 3 ? NBUF : 1][EPI == 3 ? BLK : 16];
   __shared__ __attribute__((aligned(1024))) char ob[2][kRB * N * 2];
@@ -197,9 +198,12 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
   const bool nrm = EPI != 2 && a.kind != 2;
 
   const int n0 = 32 * w;
-  const bool second = n0 >= a.nsplit;
-  const bf16* Wr = second ? a.W2 + (int64_t)(n0 - a.nsplit + l32) * K
-                          : a.W + (int64_t)(grp * N + n0 + l32) * K;
+  // This wave's 32 output columns in the whole product (column group grp):
+  // W and Y below nsplit, W2 and Y2 from it on.  The gate and its backward
+  // (EPI 1, 2) take every group's rows from W (nsplit = N there).
+  const int gc0 = grp * N + n0;
+  const bool second = (EPI == 1 || EPI == 2) ? false : gc0 >= a.nsplit;
+  const bf16* Wr = second ? a.W2 + (int64_t)(gc0 - a.nsplit + l32) * K : a.W + (int64_t)(gc0 + l32) * K;
   bf16x8 wf[K / 16];
 #pragma unroll
   for (int ks = 0; ks < K / 16; ++ks) wf[ks] = ld8<bf16>(Wr + 16 * ks + 8 * hh);
@@ -221,7 +225,8 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
         st8<bf16>(a.Y + m * a.ldy + col, u);
       }
     } else {
-      st8<bf16>(n < a.nsplit ? a.Y + m * a.ldy + n : a.Y2 + m * a.ldy + (n - a.nsplit), v);
+      const int col = grp * N + n;
+      st8<bf16>(col < a.nsplit ? a.Y + m * a.ldy + col : a.Y2 + m * a.ldy + (col - a.nsplit), v);
     }
   };
 
@@ -262,6 +267,53 @@ __global__ __launch_bounds__(N / 32 * 64) void rs_fwd_kernel(RsFwdArgs a) {
     }
     if (!nrm) return;
     const int64_t m0 = (int64_t)b * kRB;
+    if constexpr (K == 512) {
+      // A block is two panels of 256 columns; instruction j holds half-rows
+      // 2 (j % 16) and 2 (j % 16) + 1 of panel j / 16.  This wave's
+      // instructions j0 = w + NW t (t = 0, 1) and j0 + 16 are the two halves
+      // of the same rows (NW = 8), so a row's statistics reduce over the 32
+      // lanes of its lane half, across the wave's two instructions.
+#pragma unroll
+      for (int t = 0; t < IPW / 2; ++t) {
+        const int j0 = w + NW * t;
+        const int r = 2 * j0 + hh, pos = l32, c = swz(pos, r);
+        const uint32_t la0 = lds_addr(&xs[p][1024 * j0 + 16 * lane]);
+        const uint32_t la1 = la0 + kPanel;
+        const bf16x8 raw0 = lds_ld8(la0), raw1 = lds_ld8(la1);
+        float v[16];
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) { v[u] = to_f(raw0[u]); v[u + 8] = to_f(raw1[u]); }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) s += v[u];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) s += __shfl_xor(s, o);
+        const float mean = a.kind == 0 ? s / K : 0.f;
+        float qs = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) { const float dl = v[u] - mean; qs += dl * dl; }
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) qs += __shfl_xor(qs, o);
+        const float rstd = 1.f / sqrtf(qs / K + a.eps);
+        const int64_t m = min(m0 + r, M - 1);   // (rows past M: row M-1 again, same values)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int col = 256 * half + 8 * c;
+          const f32x4 g0 = lds_ldf4(lds_addr(&gb[0][col])), g1 = lds_ldf4(lds_addr(&gb[0][col + 4]));
+          const f32x4 e0 = lds_ldf4(lds_addr(&gb[1][col])), e1 = lds_ldf4(lds_addr(&gb[1][col + 4]));
+          bf16x8 y;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            y[u] = from_f<bf16>((v[8 * half + u] - mean) * rstd * g0[u] + e0[u]);
+            y[u + 4] = from_f<bf16>((v[8 * half + u + 4] - mean) * rstd * g1[u] + e1[u]);
+          }
+          *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(half ? la1 : la0) = y;
+          if (a.Xn && grp == 0) st8<bf16>(a.Xn + m * K + col, y);
+        }
+        if (a.stats && pos == 0 && grp == 0) *reinterpret_cast<f32x2*>(a.stats + 2 * m) = f32x2{mean, rstd};
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < IPW; ++t) {
       const int j = w + NW * t;
@@ -582,6 +634,8 @@ constexpr int kCUsRS = 256;
 }  // namespace
 
 bool rs_fwd_ok(int K, int N) { return (K == 256 && (N == 256 || N == 512)) || (K == 512 && N == 256); }
+// Plain projection K -> ngroups * N by column groups at K = 512.
+bool rs_fwd_groups_ok(int K, int Ntot) { return K == 512 && Ntot % 256 == 0 && kCUsRS % (8 * (Ntot / 256)) == 0; }
 bool rs_bwd_ok(int K, int N) { return (K == 256 || K == 512) && N == 256; }
 int64_t rs_bwd_grid(int64_t M) {
   const int64_t g = (M + 63) / 64;
@@ -590,7 +644,10 @@ int64_t rs_bwd_grid(int64_t M) {
 
 hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
   if (!rs_fwd_ok(K, N) || a.M < 0 || a.nsplit % 32 != 0 || a.nsplit <= 0) return hipErrorInvalidValue;
-  if (a.ngroups < 1 || kCUsRS % (8 * a.ngroups) != 0 || (a.ngroups > 1 && (!a.gate || a.nsplit != N)))
+  // Column groups: the gated forms (nsplit = N), or the plain projection at
+  // K = 512 (N = 256 per group; nsplit anywhere on the 256-column grid).
+  if (a.ngroups < 1 || kCUsRS % (8 * a.ngroups) != 0 ||
+      (a.ngroups > 1 && !(a.gate != 0 && a.nsplit == N) && !(a.gate == 0 && K == 512 && a.nsplit % N == 0)))
     return hipErrorInvalidValue;
   if (a.M == 0) return hipSuccess;
   // Row-block walkers per column group: a multiple of 8 (one set per XCD).
@@ -610,6 +667,12 @@ hipError_t launch_rs_fwd(const RsFwdArgs& a, int K, int N, hipStream_t st) {
     hipLaunchKernelGGL((rs_fwd_kernel<256, 512, 3>), dim3(g), dim3(1024), 0, st, a);
   else if (a.gate == 4 && K == 512 && N == 256 && a.H2 != nullptr && a.ngroups == 1)
     hipLaunchKernelGGL((rs_fwd_kernel<512, 256, 4>), dim3(g), dim3(512), 0, st, a);
+  else if (a.gate == 0 && K == 512 && N == 256) {
+    // The two 256-column panels of a row come from H itself.
+    RsFwdArgs b = a;
+    b.H2 = a.H + 256; b.ldh2 = a.ldh;
+    hipLaunchKernelGGL((rs_fwd_kernel<512, 256, 0>), dim3(g), dim3(512), 0, st, b);
+  }
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -89,6 +89,10 @@ PROJ_CASES = [
     ("bf16", O.NORM_LAYER, True, 256, PROJ_L), ("bf16", O.NORM_LAYER, False, 256, PROJ_L),
     ("bf16", O.NORM_RMS, True, 256, PROJ_L), ("bf16", O.NORM_NONE, False, 256, PROJ_L),
     ("bf16", O.NORM_LAYER, True, 256, PROJ_LONG), ("bf16", O.NORM_RMS, False, 256, [1, 33, 64]),
+    # d = 512: the row-streaming kernels in column groups of 256 (K = 512
+    # rows as two panels; 2 groups for Q, 4 for K and V)
+    ("bf16", O.NORM_LAYER, True, 512, PROJ_L), ("bf16", O.NORM_RMS, False, 512, PROJ_LONG),
+    ("bf16", O.NORM_NONE, False, 512, [1, 33, 64]),
 ]
 
 
@@ -153,7 +157,8 @@ def test_fusion_mlp(gpu, dtype, act, M, keepz):
 
 # bf16, shared gate, d = 256 and H a multiple of 512: the up projection runs
 # in the row-streaming kernel (column groups of 512; M = 9001 gives its
-# workgroups several 32-row blocks and a ragged last one).
+# workgroups several 32-row blocks and a ragged last one).  d = 512 runs the
+# tiled path.
 @pytest.mark.parametrize("dtype,gate,norm,d,M,H", [("f32", O.GATE_SHARED, O.NORM_LAYER, 128, 200, 512),
                                                    ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 200, 1024),
                                                    ("bf16", O.GATE_SEPARATE, O.NORM_RMS, 128, 200, 512),
@@ -161,7 +166,9 @@ def test_fusion_mlp(gpu, dtype, act, M, keepz):
                                                    ("bf16", O.GATE_SHARED, O.NORM_RMS, 256, 9001, 1024),
                                                    ("bf16", O.GATE_SHARED, O.NORM_NONE, 256, 333, 512),
                                                    ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 77, 2048),
-                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 333, -1024)])
+                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 256, 333, -1024),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_LAYER, 512, 9001, 2048),
+                                                   ("bf16", O.GATE_SHARED, O.NORM_NONE, 512, 333, -1024)])
 def test_swiglu_ffn(gpu, dtype, gate, norm, d, M, H):
     """H < 0: the same with |H| and U not kept (the product goes to the workspace)."""
     keepu = H > 0
@@ -386,7 +393,7 @@ def test_proj_qkv_bwd(gpu, dtype, norm, d, keep, L):
 
 @pytest.mark.parametrize("dtype,norm,d,L", [("f32", O.NORM_LAYER, 128, PROJ_L), ("bf16", O.NORM_RMS, 128, PROJ_L),
                                             ("bf16", O.NORM_LAYER, 256, PROJ_LONG),
-                                            ("bf16", O.NORM_NONE, 256, PROJ_L)],
+                                            ("bf16", O.NORM_NONE, 256, PROJ_L), ("bf16", O.NORM_LAYER, 512, PROJ_L)],
                          ids=lambda v: str(len(v)) if isinstance(v, list) else str(v))
 def test_proj_qkv_shared_kv(gpu, dtype, norm, d, L):
     """Shared key-value form: no W_V, no V; the backward takes one dK."""
