@@ -30,11 +30,12 @@ EXPORTS = [
     "whale_swiglu_ffn_bwd_workspace_size", "whale_swiglu_ffn_bwd",
     "whale_proj_qkv_bwd_workspace_size", "whale_proj_qkv_bwd",
     "whale_mfma_peak_probe",
-    "whale_validate_offsets", "whale_debug_checks", "whale_debug_status",
+    "whale_validate_offsets", "whale_validate_timestamps", "whale_debug_checks", "whale_debug_status",
     "whale_jagged_xattn_bwd_noalloc",
     "whale_hstu_attn_fwd",
 ]
 BAD_FIRST, BAD_ORDER, BAD_MAX_L, BAD_TOTAL, BAD_CAND_FIRST, BAD_CAND_ORDER, BAD_MAX_C = 1, 2, 4, 8, 16, 32, 64
+BAD_TIME = 128
 
 
 class WhaleDims(ctypes.Structure):
@@ -58,6 +59,7 @@ _SIGS = {
     "whale_jagged_xattn_fwd_varc": (_I, [_D, _I, _P, _P, _P, _P, _P, _F, _P, _P, _P]),
     "whale_mfma_peak_probe": (_I, [_P, ctypes.c_int32, ctypes.c_int32, _P]),
     "whale_validate_offsets": (_I, [_D, _P, _P, _P, _P]),
+    "whale_validate_timestamps": (_I, [_D, _P, _P, _P, _P]),
     "whale_hstu_attn_fwd": (_I, [_D, _I, _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P, ctypes.c_int32, _F, _P, _P]),
     "whale_jagged_xattn_bwd_noalloc": (_I, [_D, _I, _P, _P, _P, _P, _F, _P, _P, _P, _P, _P, _P, _P]),
     "whale_debug_checks": (ctypes.c_int32, [ctypes.c_int32]),
@@ -251,6 +253,15 @@ def whale_validate_offsets(d_, offsets, cand_offsets, flag, stream=None):
     rc = load().whale_validate_offsets(ctypes.byref(d_), _ptr(offsets), _ptr(cand_offsets), _ptr(flag),
                                        _stream(stream))
     _check("whale_validate_offsets", rc)
+
+
+def whale_validate_timestamps(d_, offsets, timestamps, flag, stream=None):
+    """flag: int32 device tensor with at least one element (receives the bitmask)."""
+    if flag.dtype != torch.int32:
+        raise TypeError("flag must be an int32 tensor")
+    rc = load().whale_validate_timestamps(ctypes.byref(d_), _ptr(offsets), _ptr(timestamps), _ptr(flag),
+                                          _stream(stream))
+    _check("whale_validate_timestamps", rc)
 
 
 def whale_debug_checks(enable):

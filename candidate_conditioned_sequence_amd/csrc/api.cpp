@@ -153,6 +153,15 @@ whale_status_t whale_validate_offsets(const whale_dims_t* dims, const int64_t* o
   return ret(launch_validate_offsets(offsets, cand_offsets, x.B, x.max_L, x.total_L, x.C, flag, nullptr, stream));
 }
 
+whale_status_t whale_validate_timestamps(const whale_dims_t* dims, const int64_t* offsets, const int64_t* timestamps,
+                                         int32_t* flag, hipStream_t stream) {
+  if (dims == nullptr || !offsets || !timestamps || !flag) return WHALE_ERR_NULL;
+  const whale_dims_t& x = *dims;
+  if (x.B <= 0 || x.C <= 0 || x.max_L < 0 || x.total_L < 0) return WHALE_ERR_SHAPE;
+  WHALE_TRY(launch_validate_offsets(offsets, nullptr, x.B, x.max_L, x.total_L, x.C, flag, nullptr, stream));
+  return ret(launch_validate_timestamps(offsets, timestamps, x.B, x.total_L, flag, nullptr, stream));
+}
+
 int32_t whale_debug_checks(int32_t enable) { return set_debug_checks(enable != 0); }
 
 whale_status_t whale_debug_status(int32_t* flag, int32_t reset, hipStream_t stream) {
@@ -323,6 +332,9 @@ whale_status_t whale_hstu_attn_fwd(const whale_dims_t* dims, whale_dtype_t dtype
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
   whale_status_t g = debug_guard(s, offsets, nullptr, &a.guard, stream);
   if (g != WHALE_OK) return g;
+  if (a.guard != nullptr)   // debug mode: the timestamps' contract too
+    WHALE_TRY(launch_validate_timestamps(offsets, timestamps, s.B, s.T, const_cast<int32_t*>(a.guard),
+                                         const_cast<int32_t*>(a.guard) + 1, stream));
   if (s.T == 0) return WHALE_OK;
   return ret(launch_hstu_fwd(a, dtype == WHALE_BF16, stream));
 }

@@ -197,10 +197,17 @@ enum : int32_t {
   kBadTotal = 8,        // offsets[B] != total_L
   kBadCandFirst = 16,   // cand_offsets[0] != 0
   kBadCandOrder = 32,   // cand_offsets decrease somewhere
-  kBadMaxC = 64         // some C_b > C
+  kBadMaxC = 64,        // some C_b > C
+  kBadTime = 128        // a timestamp differs from its request's first by 2^30 or more
 };
 // One workgroup: flag[0] = violations found; sticky[0] |= the same (sticky may
 // be null).  cand_offsets may be null.
+// Timestamps [total_L] of the HSTU call: every row of request b against the
+// request's first (rows outside [0, total_L) are not read: offsets that leave
+// it are the offsets check's to report).  ORs kBadTime into flag[0] (and
+// sticky[0] when not null).
+hipError_t launch_validate_timestamps(const int64_t* offsets, const int64_t* ts, int B, int64_t total_L,
+                                      int32_t* flag, int32_t* sticky, hipStream_t st);
 hipError_t launch_validate_offsets(const int64_t* offsets, const int64_t* cand_offsets, int B, int max_L,
                                    int64_t total_L, int C, int32_t* flag, int32_t* sticky, hipStream_t st);
 // The library's debug flags on the current GPU ([0] last check, [1] sticky),

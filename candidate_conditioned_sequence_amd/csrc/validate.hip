@@ -57,6 +57,38 @@ __global__ __launch_bounds__(256) void validate_kernel(const int64_t* __restrict
   }
 }
 
+// One workgroup per request (a stride over requests past the grid): each
+// timestamp against the request's first, as unsigned differences (no
+// overflow for any int64 values).  Only the kBadTime bit is set, so the
+// unsynchronised read-modify-write of the flags by several workgroups loses
+// nothing: every writer ORs in the same bit, after validate_kernel has
+// written the rest in stream order.
+__global__ __launch_bounds__(256) void validate_times_kernel(const int64_t* __restrict__ offsets,
+                                                             const int64_t* __restrict__ ts, int B, int64_t total_L,
+                                                             int32_t* __restrict__ flag,
+                                                             int32_t* __restrict__ sticky) {
+  __shared__ int32_t part[4];
+  int32_t bad = 0;
+  for (int b = blockIdx.x; b < B; b += gridDim.x) {
+    const int64_t lo = offsets[b], hi = offsets[b + 1];
+    if (lo < 0 || hi <= lo || hi > total_L) continue;
+    const int64_t t0 = ts[lo];
+    for (int64_t i = lo + threadIdx.x; i < hi; i += 256) {
+      const int64_t t = ts[i];
+      const uint64_t dist = t >= t0 ? (uint64_t)t - (uint64_t)t0 : (uint64_t)t0 - (uint64_t)t;
+      if (dist >= (uint64_t{1} << 30)) bad = kBadTime;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = bad;
+  __syncthreads();
+  if (threadIdx.x == 0 && (part[0] | part[1] | part[2] | part[3]) != 0) {
+    flag[0] |= kBadTime;
+    if (sticky != nullptr) sticky[0] |= kBadTime;
+  }
+}
+
 __global__ void debug_status_kernel(int32_t* __restrict__ flags, int32_t* __restrict__ dst, int reset) {
   if (threadIdx.x == 0) {
     dst[0] = flags[1];
@@ -72,6 +104,14 @@ hipError_t launch_validate_offsets(const int64_t* offsets, const int64_t* cand_o
                                    int64_t total_L, int C, int32_t* flag, int32_t* sticky, hipStream_t st) {
   hipLaunchKernelGGL(validate_kernel, dim3(1), dim3(256), 0, st, offsets, cand_offsets, B, max_L, total_L, C, flag,
                      sticky);
+  return hipGetLastError();
+}
+
+hipError_t launch_validate_timestamps(const int64_t* offsets, const int64_t* ts, int B, int64_t total_L,
+                                      int32_t* flag, int32_t* sticky, hipStream_t st) {
+  if (B <= 0 || total_L <= 0) return hipSuccess;
+  const int g = B < 65536 ? B : 65536;
+  hipLaunchKernelGGL(validate_times_kernel, dim3(g), dim3(256), 0, st, offsets, ts, B, total_L, flag, sticky);
   return hipGetLastError();
 }
 

@@ -110,6 +110,7 @@ const char* whale_version(void);
 #define WHALE_BAD_CAND_FIRST 16  /* cand_offsets[0] != 0 */
 #define WHALE_BAD_CAND_ORDER 32  /* cand_offsets decrease somewhere */
 #define WHALE_BAD_MAX_C 64       /* cand_offsets[b+1] - cand_offsets[b] > C for some b */
+#define WHALE_BAD_TIME 128       /* a timestamp differs from its request's first by 2^30 or more */
 
 /*
  * Checks the jagged offsets [B+1] (and, if not NULL, the candidate offsets
@@ -127,11 +128,26 @@ whale_status_t whale_validate_offsets(const whale_dims_t* dims, const int64_t* o
                                       int32_t* flag, hipStream_t stream);
 
 /*
+ * The same check as whale_validate_offsets (without candidate offsets),
+ * plus the contract of whale_hstu_attn_fwd on the timestamps [total_L]:
+ * every timestamp of request b differs from the request's first one by less
+ * than 2^30 (WHALE_BAD_TIME otherwise).  Rows outside [0, total_L) are never
+ * read: offsets that leave it are reported by the offsets bits.  *flag
+ * (device int32, caller-owned) is overwritten.  Asynchronous on `stream`.
+ * WHALE_ERR_NULL for a NULL dims, offsets, timestamps or flag;
+ * WHALE_ERR_SHAPE as whale_validate_offsets.
+ */
+whale_status_t whale_validate_timestamps(const whale_dims_t* dims, const int64_t* offsets, const int64_t* timestamps,
+                                         int32_t* flag, hipStream_t stream);
+
+/*
  * Debug mode, for all GPUs of the process: enable != 0 turns it on, 0 off;
  * returns the previous setting.  It starts on when the environment variable
  * WHALE_DEBUG_CHECKS is set to a value other than "" or "0" when the first
- * call is made.  In debug mode whale_jagged_xattn_fwd, _fwd_varc and _bwd
- * first run the check of whale_validate_offsets into a flag the library
+ * call is made.  In debug mode whale_jagged_xattn_fwd, _fwd_varc, _bwd and
+ * whale_hstu_attn_fwd (which also checks its timestamps, as
+ * whale_validate_timestamps) first run the check of whale_validate_offsets
+ * into a flag the library
  * keeps on each GPU (a small static device array, the only state the library
  * holds), and their kernels return without touching any output when it
  * reports a violation: nothing is read past the buffers the hints describe,

@@ -1,6 +1,7 @@
 """Device-side validation of the jagged offsets against the host shape hints
-(whale_validate_offsets), and debug mode, in which the attention calls run
-that check first and skip their kernels when it fails.
+(whale_validate_offsets) and of the HSTU call's timestamps
+(whale_validate_timestamps), and debug mode, in which the attention calls
+run those checks first and skip their kernels when they fail.
 
 Bad offsets are only ever handed to the validator itself.  The one test that
 runs attention kernels in debug mode with failing offsets uses offsets whose
@@ -130,5 +131,98 @@ def test_debug_mode_skips_kernels_on_failed_check(gpu):
         wb.whale_debug_status(flag)
         torch.cuda.synchronize()
         assert int(flag.item()) == 0          # cleared by the reset
+    finally:
+        wb.whale_debug_checks(prev)
+
+
+# ---------------------------------------------------------------- timestamps
+# whale_validate_timestamps: the offsets check plus the HSTU call's contract
+# (every timestamp of a request within 2^30 of the request's first).
+
+def check_ts(gpu, off, ts, max_L, total_L):
+    flag = torch.full((1,), -1, dtype=torch.int32, device=gpu)
+    dm = wb.dims(len(off) - 1, 1, 1, 64, 1, max_L, total_L)
+    wb.whale_validate_timestamps(dm, i64_dev(off, gpu), i64_dev(np.asarray(ts, dtype=np.int64), gpu), flag)
+    torch.cuda.synchronize()
+    return int(flag.item())
+
+
+def test_timestamp_contract_boundaries(gpu):
+    """Differences of 2^30 - 1 either way pass; 2^30 either way is flagged;
+    int64 extremes are flagged without overflow; an empty request reads
+    nothing."""
+    print("\n[validate ts] boundaries", flush=True)
+    t0, lim = 1_700_000_000, 2 ** 30
+    off = [0, 3, 3, 6]
+    ok = [t0, t0 + lim - 1, t0 - (lim - 1), 5, 5 + lim - 1, 5]
+    assert check_ts(gpu, off, ok, 3, 6) == 0
+    assert check_ts(gpu, off, [t0, t0 + lim, t0, 5, 5, 5], 3, 6) == wb.BAD_TIME
+    assert check_ts(gpu, off, [t0, t0, t0, 5, 5 - lim, 5], 3, 6) == wb.BAD_TIME
+    i64 = np.iinfo(np.int64)
+    assert check_ts(gpu, off, [i64.max, i64.min, i64.max, 0, 0, 0], 3, 6) == wb.BAD_TIME
+    assert check_ts(gpu, [0, 2], [i64.min, i64.min + lim - 1], 2, 2) == 0
+
+
+def test_timestamp_violation_deep_in_a_long_batch(gpu):
+    """B = 1000 requests of 300 rows (several rows per thread): one bad row
+    in request 777."""
+    print("\n[validate ts] B=1000", flush=True)
+    L = np.full(1000, 300)
+    off = np.concatenate([[0], np.cumsum(L)])
+    ts = np.repeat(np.arange(1000, dtype=np.int64) * 10 ** 12, 300) + np.tile(np.arange(300), 1000)
+    assert check_ts(gpu, off, ts, 300, int(off[-1])) == 0
+    ts[777 * 300 + 211] += 2 ** 30
+    assert check_ts(gpu, off, ts, 300, int(off[-1])) == wb.BAD_TIME
+
+
+def test_timestamp_check_reads_no_row_past_total_L(gpu):
+    """offsets[B] above the total_L hint (and a decreasing pair): the offsets
+    bits are set, and the rows past total_L (not allocated) are not read:
+    the last request is skipped, so no timestamp bit either."""
+    print("\n[validate ts] bad offsets", flush=True)
+    assert check_ts(gpu, [0, 4, 9], np.arange(8), 5, 8) == wb.BAD_TOTAL
+    assert check_ts(gpu, [0, 5, 3, 8], np.arange(8), 5, 8) == wb.BAD_ORDER
+
+
+def _hstu(gpu, dm, Q, K, V, toff, tts, wp, wt):
+    A = torch.full_like(Q, float("nan"))
+    wb.whale_hstu_attn_fwd(dm, Q, K, V, toff, tts, wp, wt, 0.0, A)
+    torch.cuda.synchronize()
+    return A
+
+
+def test_debug_mode_hstu_timestamps(gpu):
+    """Debug mode on the HSTU call: valid timestamps give the same bits as
+    without it and a clean flag; a timestamp 2^30 past its request's first
+    is flagged and the kernel leaves its output untouched."""
+    print("\n[debug mode] hstu timestamps", flush=True)
+    L, d, h = [70, 0, 129], 128, 2
+    off = np.concatenate([[0], np.cumsum(L)])
+    T = int(off[-1])
+    r = np.random.default_rng(8)
+    Q, K, V = (torch.from_numpy(r.standard_normal((T, d)).astype(np.float32)).to(gpu).to(torch.bfloat16)
+               for _ in range(3))
+    ts = np.concatenate([1_700_000_000 + np.cumsum(r.integers(0, 5000, n)) for n in L]).astype(np.int64)
+    wp = torch.from_numpy(0.3 * r.standard_normal(100).astype(np.float32)).to(gpu)
+    wt = torch.from_numpy(0.3 * r.standard_normal(20).astype(np.float32)).to(gpu)
+    dm = wb.dims(len(L), 1, 1, d, h, max(L), T)
+    toff, tts = i64_dev(off, gpu), i64_dev(ts, gpu)
+    ref = _hstu(gpu, dm, Q, K, V, toff, tts, wp, wt)
+    flag = torch.full((1,), -1, dtype=torch.int32, device=gpu)
+    bad = ts.copy()
+    bad[off[2] + 100] = bad[off[2]] + 2 ** 30
+    prev = wb.whale_debug_checks(True)
+    try:
+        wb.whale_debug_status(flag, reset=True)
+        got = _hstu(gpu, dm, Q, K, V, toff, tts, wp, wt)
+        wb.whale_debug_status(flag, reset=True)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == 0
+        assert torch.equal(got, ref)
+        A = _hstu(gpu, dm, Q, K, V, toff, i64_dev(bad, gpu), wp, wt)
+        wb.whale_debug_status(flag, reset=True)
+        torch.cuda.synchronize()
+        assert int(flag.item()) == wb.BAD_TIME
+        assert torch.isnan(A.float()).all()
     finally:
         wb.whale_debug_checks(prev)

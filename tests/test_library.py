@@ -104,6 +104,13 @@ def test_validator_host_checks():
     assert lib.whale_validate_offsets(ctypes.byref(d), fake, None, None, None) == 1
     for bad in (_dims(B=0), _dims(C=0), _dims(max_L=-1)):
         assert lib.whale_validate_offsets(ctypes.byref(bad), fake, None, fake, None) == 2
+    # the timestamps check: every pointer required (no device work is reached)
+    assert lib.whale_validate_timestamps(None, fake, fake, fake, None) == 1
+    assert lib.whale_validate_timestamps(ctypes.byref(d), None, fake, fake, None) == 1
+    assert lib.whale_validate_timestamps(ctypes.byref(d), fake, None, fake, None) == 1
+    assert lib.whale_validate_timestamps(ctypes.byref(d), fake, fake, None, None) == 1
+    for bad in (_dims(B=0), _dims(C=0), _dims(max_L=-1), _dims(total_L=-1)):
+        assert lib.whale_validate_timestamps(ctypes.byref(bad), fake, fake, fake, None) == 2
     assert lib.whale_debug_status(None, 0, None) == 1
 
 
