@@ -38,6 +38,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_ALU_TLANE = 39.3          # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, lane-instructions / s
+HSTU_INSTR_PER_SCORE = 9.5     # HSTU forward, far / interior tiles (ISA count)
 
 # HBM traffic of one xattn_fwd_pp_kernel<64> launch on the headline workload
 # (profiles/hbm_traffic_c3_L10k_all_kernels.md):
@@ -195,7 +197,43 @@ def bench_hstu(args, torch, wb, synth, dev):
                       "B": cfg.B, "d": d, "h": h, "T": T, "n_pos": 4096, "n_time": 32},
            "gscore_per_s": round(scores / (ms * 1e-3) / 1e9, 1),
            "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
+    # Roofline: the kernel is bound by vector ALU issue.  Work per score on
+    # far and interior tiles (the bulk): exp2, reciprocal and six other ALU
+    # instructions, the saturating time difference and half a bf16 pack.
+    # Peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instructions/s.
+    gsc = scores / (ms * 1e-3)
+    achieved = gsc * HSTU_INSTR_PER_SCORE / 1e12
+    res["roofline"] = {"bound": "alu", "kernel": f"hstu_fwd_kernel<bf16,{d // h}>", "call": "whale_hstu_attn_fwd",
+                       "achieved": round(achieved, 2), "peak": PEAK_ALU_TLANE, "unit": "T lane-instr/s",
+                       "frac": round(achieved / PEAK_ALU_TLANE, 4), "traffic": None,
+                       "instr_per_score": HSTU_INSTR_PER_SCORE,
+                       "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
+    if not args.no_cpu:
+        res["cpu_baseline"] = hstu_cpu_baseline(cfg, key, L, d, h)
     print(json.dumps(res))
+
+
+def hstu_cpu_baseline(cfg, key, L, d, h, n_req=25):
+    """The fp64 oracle on the n_req shortest histories of the workload."""
+    from oracle import whale_oracle as O
+    from candidate_conditioned_sequence_amd import synth
+    reqs = [int(b) for b in np.argsort(L, kind="stable")[:n_req]]
+    Ls = L[reqs]
+    off = synth.offsets_of(Ls)
+    T = int(off[-1])
+    r = np.random.default_rng(1)
+    q, k, v = (r.standard_normal((T, d)) for _ in range(3))
+    ts = np.concatenate([synth.timestamps(cfg, b, L[b]) for b in reqs])
+    wp, wt = synth.hstu_tables(cfg, 4096, 32)
+    t0 = time.perf_counter()
+    O.hstu_attn_fwd(q, k, v, off, h, ts, wp, wt)
+    dt = time.perf_counter() - t0
+    pairs = float(np.sum(Ls * (Ls + 1) // 2))
+    return {"value": 4.0 * d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads() or host_cores(),
+            "host_cores": host_cores(), "blas_threads": blas_threads(), "kind": "oracle",
+            "gscore_per_s": pairs * h / dt / 1e9, "seconds": dt,
+            "sample": f"the {len(reqs)} shortest request(s) of the {key} histories (L_b = {Ls.tolist()}), "
+                      f"N(0, 1) inputs, fp64 numpy"}
 
 
 def main():
