@@ -66,8 +66,12 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
   constexpr int NCH = kHBN * CPR / 256;
   constexpr int KBR = DH >= 128 ? 1 : 2;         // key blocks whose K operands are read at once
   static_assert(NCH >= 1 && kHBN * CPR % 256 == 0, "tile/threads mismatch");
+  // K tiles and their timestamps are double buffered, V tiles single
+  // buffered (V is read only by the last product of a tile): 44,676 bytes of
+  // LDS at d_h = 64 in bf16, below the largest size of which the hardware
+  // keeps three workgroups on a CU (measured between 52,000 and 53,892).
   __shared__ __attribute__((aligned(32))) T Ks[2][kHBN * KLD];
-  __shared__ __attribute__((aligned(32))) T Vs[2][kHBN * KLD];
+  __shared__ __attribute__((aligned(32))) T Vs[kHBN * KLD];
   __shared__ __attribute__((aligned(16))) uint32_t Ts[2][kHBN];
   // Both tables are stored times -log2(e) (see the SiLU below).
   __shared__ float Wp[kMaxPos];
@@ -127,19 +131,27 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
     }
     if (tid < kHBN) tr = (uint32_t)(ts[lo + t * kHBN + min(tid, last)] - t0);
   };
-  auto store_tile = [&](int buf) {
+  auto store_k = [&](int buf) {
 #pragma unroll
     for (int c = 0; c < NCH; ++c) {
       const int ch = tid + c * 256;
       const int row = ch / CPR, e0 = 8 * (ch % CPR);
       st8<T>(&Ks[buf][row * KLD + e0], kr[c]);
-      st8<T>(&Vs[buf][row * KLD + e0], vr[c]);
     }
     if (tid < kHBN) Ts[buf][tid] = tr;
   };
+  auto store_v = [&]() {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      const int ch = tid + c * 256;
+      const int row = ch / CPR, e0 = 8 * (ch % CPR);
+      st8<T>(&Vs[row * KLD + e0], vr[c]);
+    }
+  };
 
   load_tile(0);
-  store_tile(0);
+  store_k(0);
+  store_v();
   __syncthreads();
   const float wlast = Wp[n_pos - 1];
   const float sc = kNegLog2e * scale;
@@ -217,6 +229,9 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
     if (far) elems(std::integral_constant<int, 2>());
     else if (interior) elems(std::integral_constant<int, 1>());
     else elems(std::integral_constant<int, 0>());
+    // V of tile t, stored after the previous tile's last barrier, is visible
+    // to every wave from here on.
+    __syncthreads();
     // O^T[e][q] += V^T[e][key] P^T[key][q]
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -224,9 +239,11 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
       for (int e = 0; e < NE; ++e)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm)
-          mma32(oacc[e], lds_colA<T>(&Vs[buf][0], KLD, 32 * kb + 16 * mm, 32 * e, lane), pf[kb][mm]);
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
+          mma32(oacc[e], lds_colA<T>(&Vs[0], KLD, 32 * kb + 16 * mm, 32 * e, lane), pf[kb][mm]);
+    if (t + 1 < ntiles) store_k(buf ^ 1);
+    // Every wave is done with V of tile t (and K of tile t + 1 is visible).
     __syncthreads();
+    if (t + 1 < ntiles) store_v();
   }
 
   if (iok) {
