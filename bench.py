@@ -39,7 +39,7 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
 PEAK_ALU_TLANE = 39.3          # 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, lane-instructions / s
-HSTU_INSTR_PER_SCORE = 9.5     # HSTU forward, far / interior tiles (ISA count)
+HSTU_INSTR_PER_SCORE = 9.5     # HSTU forward, per-element form (fixed reference count)
 
 # HBM traffic of one xattn_fwd_pp_kernel<64> launch on the headline workload
 # (profiles/hbm_traffic_c3_L10k_all_kernels.md):
@@ -197,9 +197,12 @@ def bench_hstu(args, torch, wb, synth, dev):
                       "B": cfg.B, "d": d, "h": h, "T": T, "n_pos": 4096, "n_time": 32},
            "gscore_per_s": round(scores / (ms * 1e-3) / 1e9, 1),
            "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2)}
-    # Roofline: the kernel is bound by vector ALU issue.  Work per score on
-    # far and interior tiles (the bulk): exp2, reciprocal and six other ALU
-    # instructions, the saturating time difference and half a bf16 pack.
+    # Roofline: the kernel is bound by vector ALU issue.  Work per score in
+    # the straightforward per-element form: bias add, fused multiply-add,
+    # exp2, add, reciprocal, multiply, the saturating time difference, its
+    # leading-zero count and address shift, half a bf16 pack (9.5; the
+    # kernel folds the first two into its MFMAs and issues 8.5).  Fixed, so
+    # that the fraction compares kernel versions.
     # Peak: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane-instructions/s.
     gsc = scores / (ms * 1e-3)
     achieved = gsc * HSTU_INSTR_PER_SCORE / 1e12

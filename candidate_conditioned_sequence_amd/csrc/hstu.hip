@@ -77,7 +77,9 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
   __shared__ float Wp[kMaxPos];
   // Wt[1 + c] = w_time[min(31 - c, NT - 1)] for a time difference with c
   // leading zeros; Wt[0] (difference 0, leading-bit search -1) = w_time[0].
+  // Wf is the same plus the last position entry (far tiles).
   __shared__ float Wt[33];
+  __shared__ float Wf[33];
 
   const int level = blockIdx.x / nbh;           // nbh = B * h blocks per level
   const int qbi = nqb - 1 - level;
@@ -95,16 +97,28 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
   constexpr float kNegLog2e = -1.4426950408889634f;
 
   for (int k = tid; k < n_pos; k += 256) Wp[k] = kNegLog2e * w_pos[k];
-  if (tid < 33) Wt[tid] = kNegLog2e * w_time[tid == 0 ? 0 : min(32 - tid, n_time - 1)];
+  if (tid < 33) {
+    Wt[tid] = kNegLog2e * w_time[tid == 0 ? 0 : min(32 - tid, n_time - 1)];
+    Wf[tid] = Wt[tid] + kNegLog2e * w_pos[n_pos - 1];
+  }
 
   const int qw = qbi * kHQB + w * 32;            // first query of this wave
   const int i = qw + l32;                        // this lane's query (row within the request)
   const bool iok = i < L;
+  // Q fragments times sc = -log2(e) scale (for bf16 rounded once, a
+  // relative error near 2^-9, as in the fusion attention): the score MFMA
+  // then yields -log2(e) (scale <q, k> + position bias) directly, its
+  // accumulators starting from the position bias.
+  const float sc = kNegLog2e * scale;
   x8_t<T> qf[KS];
   {
     const T* src = Q + (lo + i) * d + j * DH + 8 * hh;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) qf[ks] = iok ? ld8<T>(src + 16 * ks) : zero8<T>();
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = iok ? ld8<T>(src + 16 * ks) : zero8<T>();
+#pragma unroll
+      for (int u = 0; u < 8; ++u) qf[ks][u] = from_f<T>(to_f(qf[ks][u]) * sc);
+    }
   }
   const uint32_t ti = iok ? (uint32_t)(ts[lo + i] - t0) : 0u;
   f32x16 oacc[NE];
@@ -153,49 +167,59 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
   store_k(0);
   store_v();
   __syncthreads();
-  const float wlast = Wp[n_pos - 1];
-  const float sc = kNegLog2e * scale;
-  const float* wt1 = Wt + 1;
   for (int t = 0; t < ntiles; ++t) {
     const int buf = t & 1;
     if (t + 1 < ntiles) load_tile(t + 1);
     const int j0 = t * kHBN;
-    f32x16 s[2];
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int kb0 = 0; kb0 < 2; kb0 += KBR) {
-      x8_t<T> ka[KBR][KS];
-#pragma unroll
-      for (int u = 0; u < KBR; ++u)
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          ka[u][ks] = ld8<T>(&Ks[buf][(32 * (kb0 + u) + l32) * KLD + 16 * ks + 8 * hh]);
-#pragma unroll
-      for (int u = 0; u < KBR; ++u) {
-        s[kb0 + u] = zero16();
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) mma32(s[kb0 + u], ka[u][ks], qf[ks]);
-      }
-    }
-    __builtin_amdgcn_s_setprio(0);
-
     // Tile-uniform cases for this wave: far (every pair at least NP - 1 rows
-    // apart: the last position entry, no mask), interior (every i - j in
-    // [0, NP - 1]: no clamp, no mask), else edge (clamp and causal mask).
+    // apart: the last position entry, folded into the time table Wf; no
+    // mask), interior (every i - j in [0, NP - 1]: no clamp, no mask), else
+    // edge (clamp and causal mask).
     const bool far = qw - (j0 + kHBN - 1) >= n_pos - 1;
     const bool interior = !far && j0 + kHBN - 1 <= qw && qw + 31 - j0 <= n_pos - 1;
     // With y = -log2(e) x, SiLU(x) = -ln(2) y / (1 + 2^y): the factor -ln(2)
-    // is applied once to the output, so each element costs one fused
-    // multiply-add, an exp2, an add, a reciprocal and a multiply.  Interior
-    // tiles read the position table at one base address (row offsets become
+    // is applied once to the output, so each element costs an add (the time
+    // bias), an exp2, an add, a reciprocal and a multiply.  Interior tiles
+    // read the position table at one base address (row offsets become
     // immediates).  The mode is uniform over the tile, so one branch covers
     // all 32 elements of the lane and they can be interleaved.
     x8_t<T> pf[2][2];
-    auto elems = [&](auto modec) {
+    auto tile = [&](auto modec) {
       constexpr int kMode = decltype(modec)::value;   // 0 edge, 1 interior, 2 far
+      f32x16 s[2];
+      // position bias (times -log2(e)) as the accumulator start, row
+      // j0 + 32 kb + acc_row(r, hh) of the lane's query i
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const float* wrow = kMode == 1 ? &Wp[i - j0 - 32 * kb - 4 * hh - 27] : Wp;
+        if constexpr (kMode == 2) {
+          s[kb] = zero16();
+        } else if constexpr (kMode == 1) {
+          const float* wrow = &Wp[i - j0 - 32 * kb - 4 * hh - 27];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = wrow[27 - 8 * (r >> 2) - (r & 3)];
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[kb][r] = Wp[min(max(i - (j0 + 32 * kb + acc_row(r, hh)), 0), n_pos - 1)];
+        }
+      }
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int kb0 = 0; kb0 < 2; kb0 += KBR) {
+        x8_t<T> ka[KBR][KS];
+#pragma unroll
+        for (int u = 0; u < KBR; ++u)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            ka[u][ks] = ld8<T>(&Ks[buf][(32 * (kb0 + u) + l32) * KLD + 16 * ks + 8 * hh]);
+#pragma unroll
+        for (int u = 0; u < KBR; ++u)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) mma32(s[kb0 + u], ka[u][ks], qf[ks]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      const float* wt1 = (kMode == 2 ? Wf : Wt) + 1;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         uint32_t tj[16];   // timestamps of this lane's 16 rows (4-row groups)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
@@ -209,13 +233,9 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int jj = j0 + 32 * kb + acc_row(r, hh);
-          float bp;
-          if constexpr (kMode == 2) bp = wlast;
-          else if constexpr (kMode == 1) bp = wrow[27 - 8 * (r >> 2) - (r & 3)];
-          else bp = Wp[min(max(i - jj, 0), n_pos - 1)];
           const uint32_t dt = __builtin_elementwise_sub_sat(ti, tj[r]);
           const int lz = leading_zeros_or_m1(dt);
-          const float y = fmaf(s[kb][r], sc, bp + wt1[lz]);
+          const float y = s[kb][r] + wt1[lz];
           const float pr = y * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(y));
           p[r] = (kMode != 0 || jj <= i) ? pr : 0.f;
         }
@@ -226,9 +246,9 @@ __global__ __launch_bounds__(256, (DH >= 128 || sizeof(T) == 4) ? 1 : 3) void hs
           for (int u = 0; u < 8; ++u) pf[kb][mm][u] = from_f<T>(p[8 * mm + u]);
       }
     };
-    if (far) elems(std::integral_constant<int, 2>());
-    else if (interior) elems(std::integral_constant<int, 1>());
-    else elems(std::integral_constant<int, 0>());
+    if (far) tile(std::integral_constant<int, 2>());
+    else if (interior) tile(std::integral_constant<int, 1>());
+    else tile(std::integral_constant<int, 0>());
     // V of tile t, stored after the previous tile's last barrier, is visible
     // to every wave from here on.
     __syncthreads();
