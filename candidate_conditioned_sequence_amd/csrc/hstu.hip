@@ -23,15 +23,17 @@
 //    rotated by one per level: a pair lands on a different XCD at each
 //    level, and no XCD collects the long requests.
 //  * S^T = K Q^T with 32x32x16 MFMA (lane = query column, 16 key rows per
-//    lane and 32-row block), then per element: the position bias, the time
+//    lane and 32-row block), with -log2(e) scale folded into Q and the
+//    position bias as the accumulators' start, then per element: the time
 //    bias by an LDS gather at the leading-bit position of the saturated time
 //    difference (the time table is stored in that order, so no log and no
-//    clip), one fused multiply-add and SiLU.  Each wave classifies each key
-//    tile once: far (every pair at least NP - 1 rows apart: the table's last
-//    entry), interior (every i - j in [0, NP - 1]: a gather at immediate
-//    offsets from one base, no mask) or edge (clamped gather and the causal
-//    mask).  The packed probabilities feed O^T += V^T P^T with V read
-//    column-wise by transposing LDS reads, as in the fusion attention.
+//    clip), one add and SiLU.  Each wave classifies each key tile once,
+//    before its MFMAs: far (every pair at least NP - 1 rows apart: the
+//    table's last entry, folded into a second time table), interior (every
+//    i - j in [0, NP - 1]: a gather at immediate offsets from one base, no
+//    mask) or edge (clamped gather and the causal mask).  The packed
+//    probabilities feed O^T += V^T P^T with V read column-wise by
+//    transposing LDS reads, as in the fusion attention.
 //  * Timestamps are kept as 32-bit tau - tau_first + 2^30, so the time
 //    difference of any pair is exact and below 2^31 when every timestamp of
 //    a request differs from its first by less than 2^30 (the caller's
