@@ -277,6 +277,10 @@ whale_status_t debug_guard(const Shape& s, const int64_t* offsets, const int64_t
 }
 
 // Both forward attention calls: cand_offsets null for C candidates per request.
+// Longest-first order for jagged batches (see kRankMaxB): every L_b <= max_L
+// and their sum total_L = B max_L mean all lengths are equal.
+bool rank_order(const Shape& s) { return s.B <= kRankMaxB && s.T != (int64_t)s.B * s.max_L; }
+
 whale_status_t xattn_fwd_call(const whale_dims_t* dims, whale_dtype_t dtype, const void* Q, const void* K,
                               const void* V, const int64_t* offsets, const int64_t* cand_offsets, float scale,
                               void* A, float* lse, hipStream_t stream) {
@@ -291,6 +295,7 @@ whale_status_t xattn_fwd_call(const whale_dims_t* dims, whale_dtype_t dtype, con
   a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
   a.cand_offsets = cand_offsets; a.n_q = s.n_q;
+  a.rank_order = rank_order(s);
   whale_status_t g = debug_guard(s, offsets, cand_offsets, &a.guard, stream);
   if (g != WHALE_OK) return g;
   return ret(launch_xattn_fwd(a, dtype == WHALE_BF16, stream));
@@ -450,6 +455,7 @@ size_t whale_jagged_xattn_bwd_workspace_size(const whale_dims_t* dims, whale_dty
   if (splits > 1) c.take((size_t)splits * 2 * s.T * s.d * 4);
   if (xattn_bwd_kv_schedule(s.max_L, s.dh, dtype == WHALE_BF16))
     c.take((size_t)xattn_bwd_kv_qpartial_floats(s.M, s.d, s.max_L) * 4);
+  if (s.B <= kRankMaxB) c.take((size_t)s.B * 4);      // longest-first request order
   return c.used;
 }
 
@@ -490,6 +496,8 @@ whale_status_t xattn_bwd_launch(const Shape& s, whale_dtype_t dtype, const void*
     const int64_t qf = xattn_bwd_kv_qpartial_floats(s.M, s.d, s.max_L);
     a.qpartial = qf > 0 ? (float*)c.take((size_t)qf * 4) : nullptr;
   }
+  // written by the dQ kernel, read by the dK/dV kernel after it
+  a.perm = rank_order(s) ? (int32_t*)c.take((size_t)s.B * 4) : nullptr;
   a.B = s.B; a.QR = s.QR; a.d = s.d; a.h = s.h; a.dh = s.dh; a.max_L = s.max_L; a.T = s.T;
   a.scale = scale > 0.f ? scale : 1.f / std::sqrt((float)s.dh);
   whale_status_t g = debug_guard(s, offsets, nullptr, &a.guard, stream);

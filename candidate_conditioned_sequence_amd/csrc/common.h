@@ -1,6 +1,7 @@
 // Shared device helpers for the libwhalefuse kernels (gfx950 / CDNA4).
 #pragma once
 #include <hip/hip_runtime.h>
+#include <climits>
 #include <stdint.h>
 
 typedef __bf16 bf16;
@@ -168,6 +169,36 @@ WHALE_DEV int pair_xcd_order(int id, int nb, int npairs) {
   if (id >= full) return id;
   const int x = id % 8, i = id / 8;
   return ((i / nb) * 8 + x) * nb + i % nb;
+}
+
+// Longest-first order of the B requests of a batch (ties by index), so
+// that the (request, head) pairs dealt to the XCDs come longest first and
+// the shortest run last (list scheduling): perm[rank] = request, in LDS.
+// Every thread of the workgroup calls it (two barriers); lens holds B
+// rounded up to 4 entries, and each thread ranks its requests against all
+// B lengths, four per LDS read.  Each output element is still produced by
+// one workgroup with the same arithmetic, so the order changes no result.
+WHALE_DEV void rank_requests(const int64_t* __restrict__ offsets, int B, int* lens, int* perm) {
+  const int B4 = (B + 3) & ~3;
+  for (int b = threadIdx.x; b < B4; b += blockDim.x)
+    lens[b] = b < B ? (int)(offsets[b + 1] - offsets[b]) : INT_MIN;
+  __syncthreads();
+  const int4* l4 = reinterpret_cast<const int4*>(lens);
+  for (int b = threadIdx.x; b < B; b += blockDim.x) {
+    const int Lb = lens[b];
+    int rank = 0;
+#pragma unroll 4
+    for (int c4 = 0; c4 < B4 / 4; ++c4) {
+      const int4 v = l4[c4];
+      const int c = 4 * c4;
+      rank += (v.x > Lb) | ((v.x == Lb) & (c < b));
+      rank += (v.y > Lb) | ((v.y == Lb) & (c + 1 < b));
+      rank += (v.z > Lb) | ((v.z == Lb) & (c + 2 < b));
+      rank += (v.w > Lb) | ((v.w == Lb) & (c + 3 < b));
+    }
+    perm[rank] = b;
+  }
+  __syncthreads();
 }
 
 WHALE_DEV float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -17,8 +17,18 @@ struct XattnArgs {
   // every kernel of the call returns at once when it is non-zero.  nullptr
   // otherwise.
   const int32_t* guard = nullptr;
+  // Run the work longest history first (set for batches of at most
+  // kRankMaxB requests whose lengths are not all equal).
+  bool rank_order = false;
 };
 hipError_t launch_xattn_fwd(const XattnArgs& a, bool bf16_data, hipStream_t st);
+
+// Jagged batches of at most kRankMaxB requests run the attention kernels'
+// work longest history first: the forward and dQ kernels rank the requests
+// in each workgroup, and the dQ kernel leaves the order in perm for the
+// dK/dV kernel.  The shape hints tell the host when every history has the
+// same length (total_L = B max_L), and then the index order is kept.
+constexpr int kRankMaxB = 256;
 
 struct XattnBwdArgs {
   const void* Q; const void* K; const void* V; const int64_t* offsets;
@@ -35,6 +45,7 @@ struct XattnBwdArgs {
   // history spans more than one 128-row block.
   bool kv_schedule = false;
   float* qpartial = nullptr;
+  int32_t* perm = nullptr;   // [B] longest-first order, written by the dQ kernel (nullptr: index order)
 };
 hipError_t launch_xattn_bwd(const XattnBwdArgs& a, bool bf16_data, hipStream_t st);
 int xattn_bwd_splits(int B, int h, int QR, int max_L, int dh);

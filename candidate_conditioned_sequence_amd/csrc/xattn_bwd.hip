@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NWQ * 64, DH >= 128 ? 1 : 2) void bwd_dq_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int64_t* __restrict__ offsets, const T* __restrict__ dA, const T* __restrict__ A,
     const float* __restrict__ lse, float* __restrict__ Dbuf, T* __restrict__ dQ, int d, int h, int QR, int nqb,
-    float c, float scale, int nblocks, const int32_t* __restrict__ guard) {
+    float c, float scale, int nblocks, const int32_t* __restrict__ guard, int32_t* __restrict__ perm_out) {
   if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int BN = 64, KS = DH / 16, NE = DH / 32, QB = NWQ * 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = BN * CPR / (NWQ * 64);
@@ -83,10 +83,18 @@ __global__ __launch_bounds__(NWQ * 64, DH >= 128 ? 1 : 2) void bwd_dq_kernel(
   __shared__ __attribute__((aligned(32))) T Ks[2][BN * KLD];
   __shared__ __attribute__((aligned(32))) T Vs[2][BN * KLD];
 
+  __shared__ __attribute__((aligned(16))) int rk_len[kRankMaxB], rk_perm[kRankMaxB];
   const int lid = pair_xcd_order(blockIdx.x, nqb, nblocks / nqb);
   const int qbi = lid % nqb;
   const int bj = lid / nqb;
-  const int j = bj % h, b = bj / h;
+  const int j = bj % h, nreq = nblocks / nqb / h;
+  int b = bj / h;
+  if (perm_out != nullptr && nreq <= kRankMaxB) {   // uniform: longest history first, the order kept for dK/dV
+    rank_requests(offsets, nreq, rk_len, rk_perm);
+    b = rk_perm[b];
+    if (blockIdx.x == 0)
+      for (int i = threadIdx.x; i < nreq; i += blockDim.x) perm_out[i] = rk_perm[i];
+  }
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
     const float* __restrict__ Dbuf, T* __restrict__ dK, T* __restrict__ dV, float* __restrict__ part,
     int d, int h, int QR, int nkt, int qchunk, float c, float scale, int64_t T_rows, int nblocks,
     const int32_t* __restrict__ guard, T* __restrict__ dQ = nullptr, float* __restrict__ qpart = nullptr,
-    int64_t M_rows = 0) {
+    int64_t M_rows = 0, const int32_t* __restrict__ perm = nullptr) {
   if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int QT = 64, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8, NCH = QT * CPR / (NWK * 64);
@@ -274,7 +282,10 @@ __global__ __launch_bounds__(NWK * 64, DH >= 128 ? 1 : 2) void bwd_dkdv_kernel(
   const int lid = pair_xcd_order(blockIdx.x, nkt, nblocks / nkt);
   const int kt = lid % nkt;
   const int bj = lid / nkt;
-  const int j = bj % h, b = bj / h;
+  const int j = bj % h;
+  // longest history first, in the order the dQ kernel left (the KV-parallel
+  // schedule, for histories of one block, keeps the index order)
+  const int b = perm != nullptr ? perm[bj / h] : bj / h;
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
   const int q_begin = split * qchunk;
@@ -653,7 +664,7 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
       const int64_t nblk = (int64_t)a.B * a.h * nqb;
       hipLaunchKernelGGL((bwd_dq_kernel<T, DH, NWQ>), dim3((unsigned)nblk), dim3(NWQ * 64), 0, st, (const T*)a.Q,
                          (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, (const T*)a.A, a.lse, a.Dbuf,
-                         (T*)a.dQ, a.d, a.h, a.QR, nqb, c, a.scale, (int)nblk, a.guard);
+                         (T*)a.dQ, a.d, a.h, a.QR, nqb, c, a.scale, (int)nblk, a.guard, a.perm);
     };
     bool done = false;
     if constexpr (DH == 64) {
@@ -677,7 +688,7 @@ hipError_t bwd_t(const XattnBwdArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<T, DH, NWK>), dim3((unsigned)nblk, a.splits), dim3(NWK * 64), 0, st,
                          (const T*)a.Q, (const T*)a.K, (const T*)a.V, a.offsets, (const T*)a.dA, a.lse, a.Dbuf,
                          (T*)a.dK, (T*)a.dV, part, a.d, a.h, a.QR, nkt, qchunk, c, a.scale, a.T, (int)nblk,
-                         a.guard);
+                         a.guard, nullptr, nullptr, 0, a.perm);
     };
     bool done = false;
     if constexpr (DH == 64) {

@@ -371,7 +371,7 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
     const int64_t* __restrict__ offsets, bf16* __restrict__ A, float* __restrict__ lse,
     int d, int h, int QR, int nqb, float c, int nblocks, const int64_t* __restrict__ coffs, int n_q,
-    const int32_t* __restrict__ guard) {
+    const int32_t* __restrict__ guard, int rank) {
   if (guard != nullptr && *guard != 0) return;   // debug mode: offsets failed validation (uniform)
   constexpr int NQ = kPPQ / 32, KS = DH / 16, NE = DH / 32;
   constexpr int KLD = DH + 8, CPR = DH / 8;
@@ -384,10 +384,16 @@ __global__ __launch_bounds__(kPPW * 64, 1) void xattn_fwd_pp_kernel(
   __shared__ __attribute__((aligned(32))) bf16 Ks[kNBUF][kBN * KLD];
   __shared__ __attribute__((aligned(32))) bf16 Vs[kNBUF][kBN * VLD];
 
+  __shared__ __attribute__((aligned(16))) int rk_len[kRankMaxB], rk_perm[kRankMaxB];
   const int lid = pair_xcd_order(blockIdx.x, nqb, nblocks / nqb);
   const int qbi = lid % nqb;
   const int bj = lid / nqb;
-  const int j = bj % h, b = bj / h;
+  const int j = bj % h, nreq = nblocks / nqb / h;
+  int b = bj / h;
+  if (rank != 0 && nreq <= kRankMaxB) {   // uniform: longest history first
+    rank_requests(offsets, nreq, rk_len, rk_perm);
+    b = rk_perm[b];
+  }
   const int64_t lo = offsets[b];
   const int L = (int)(offsets[b + 1] - lo);
   const int tid = threadIdx.x, lane = tid & 63, l32 = lane & 31, hh = lane >> 5;
@@ -661,7 +667,7 @@ hipError_t launch_fwd_pp(const XattnArgs& a, hipStream_t st) {
   const float c = a.scale * kLog2e;
   hipLaunchKernelGGL((xattn_fwd_pp_kernel<DH>), dim3((unsigned)nblk), dim3(kPPW * 64), 0, st,
                      (const bf16*)a.Q, (const bf16*)a.K, (const bf16*)a.V, a.offsets, (bf16*)a.A, a.lse,
-                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q, a.guard);
+                     a.d, a.h, a.QR, nqb, c, (int)nblk, a.cand_offsets, a.n_q, a.guard, (int)a.rank_order);
   return hipGetLastError();
 }
 
