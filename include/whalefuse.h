@@ -36,8 +36,8 @@
  * Conventions common to every call:
  *   - Data pointers are device pointers; `dims` is host memory.  The data
  *     type of activations and weights is `dtype` (fp32 or bf16).  Norm
- *     parameters gamma/beta, lse, statistics, weight gradients and
- *     workspaces are always fp32.
+ *     parameters gamma/beta, lse, statistics and weight gradients are
+ *     always fp32; workspaces are opaque device memory.
  *   - The caller allocates every buffer; the library allocates nothing and
  *     keeps no state besides its compiled kernels.  Outputs must not alias
  *     inputs.  Weight and gamma/beta gradients are written, not accumulated.
@@ -283,7 +283,11 @@ whale_status_t whale_swiglu_ffn(const whale_dims_t* dims, whale_dtype_t dtype,
  * with no reduction; dK/dV from a kernel parallel over K/V tiles and over
  * query splits, whose fp32 partials are summed in a fixed order.
  * lse must be the forward's.  workspace: at least
- * whale_jagged_xattn_bwd_workspace_size(dims, dtype) bytes of device memory.
+ * whale_jagged_xattn_bwd_workspace_size(dims, dtype) bytes of device memory
+ * (contents on entry do not matter; it holds D, the fp32 partials and, for
+ * jagged batches of at most 256 requests, their longest-first order).
+ * Both attention calls run the work of such batches longest history first;
+ * the order changes no result bit.
  * Shared key-value form: V == K and dV NULL; dK then receives the gradient
  * of the one tensor, scale dS^T Q + P^T dA, summed in fp32 and rounded
  * once.  dV NULL with V != K is WHALE_ERR_SHAPE.
