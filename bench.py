@@ -49,8 +49,8 @@ HSTU_INSTR_PER_SCORE = 9.5     # HSTU forward, per-element form (fixed reference
 # differs, the figure no longer describes the kernel and is reported as null.
 XATTN_FWD_TRAFFIC = {"kernel": "xattn_fwd_pp_kernel<64>", "config": "c3L10k",
                      "source": "candidate_conditioned_sequence_amd/csrc/xattn_fwd.hip",
-                     "source_sha256_16": "082f456ee2d3d46f",
-                     "fetch_kib": 705676, "fetch_scale": 2.000, "write_kib": 147470, "write_scale": 1.000}
+                     "source_sha256_16": "1a65f62065d3bc51",
+                     "fetch_kib": 705704, "fetch_scale": 2.000, "write_kib": 147456, "write_scale": 1.000}
 METRIC = "fusion-attn TFLOP/s + requests/s at L=10k,d=256,C=64; % bf16 MFMA peak"
 
 # Per configuration: what one step covers, and the CPU-oracle sample.
