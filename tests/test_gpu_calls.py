@@ -540,3 +540,40 @@ def test_xattn_bwd_kv_schedule(gpu, case, monkeypatch):
     assert torch.equal(res["q"][1], res["kv"][1])
     if not tied:
         assert torch.equal(res["q"][2], res["kv"][2])
+
+
+# Jagged batches of up to 256 requests run longest history first (each
+# workgroup ranks the requests; the dQ kernel leaves the order in the
+# workspace for the dK/dV kernel); larger batches keep the index order.
+# Both sides of the bound, with the ping-pong forward (C n_q = 1024) and the
+# Q-parallel backward, checked on sampled requests (each request's outputs
+# depend on its own rows only): the longest, an empty one, short ones.
+@pytest.mark.parametrize("B", [256, 257])
+def test_xattn_many_jagged_requests(gpu, B):
+    dtype, d, h, C, n_q = "bf16", 128, 2, 32, 32
+    L = [(37 * b + 11) % 61 for b in range(B)]     # 0 ... 60, every length several times
+    print(f"\n[xattn many jagged] B={B} max_L={max(L)}", flush=True)
+    QR = C * n_q
+    M, off = B * QR, offsets(L)
+    T = int(off[-1])
+    Q, K, V, dA = draw(41, (M, d), dtype), draw(42, (T, d), dtype), draw(43, (T, d), dtype), draw(44, (M, d), dtype)
+    dm = wb.dims(B, C, n_q, d, h, max(L), T)
+    tQ, tK, tV, tdA = (to_dev(x, dtype, gpu) for x in (Q, K, V, dA))
+    toff = i64_dev(off, gpu)
+    A, lse = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+    wb.whale_jagged_xattn_fwd(dm, tQ, tK, tV, toff, 0.0, A, lse)
+    dQ, dK, dV = torch.empty_like(tQ), torch.empty_like(tK), torch.empty_like(tV)
+    ws = torch.empty(wb.whale_jagged_xattn_bwd_workspace_size(dm, wb._dtype_code(tQ)), dtype=torch.uint8, device=gpu)
+    wb.whale_jagged_xattn_bwd(dm, tQ, tK, tV, toff, 0.0, A, lse, tdA, dQ, dK, dV, ws)
+    torch.cuda.synchronize()
+    sample = sorted({int(np.argmax(L)), L.index(0), L.index(1), B // 2, B - 1})
+    for b in sample:
+        q, k = slice(b * QR, (b + 1) * QR), slice(int(off[b]), int(off[b + 1]))
+        o1 = np.array([0, L[b]])
+        A_ref, lse_ref = O.xattn_fwd(Q[q], K[k], V[k], o1, C, n_q, h)
+        dQ_ref, dK_ref, dV_ref = O.xattn_bwd(Q[q], K[k], V[k], o1, C, n_q, h, None, dA[q])
+        assert_close(f"A[{b}]", A[q], A_ref, dtype)
+        assert_close(f"dQ[{b}]", dQ[q], dQ_ref, dtype)
+        if L[b] > 0:
+            assert_close(f"dK[{b}]", dK[k], dK_ref, dtype)
+            assert_close(f"dV[{b}]", dV[k], dV_ref, dtype)
