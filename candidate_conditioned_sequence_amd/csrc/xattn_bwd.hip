@@ -206,9 +206,14 @@ __global__ __launch_bounds__(NWQ * 64, DH >= 128 ? 1 : 2) void bwd_dq_kernel(
         for (int r = 0; r < 16; ++r) s[r] = fmaf(s[r], c, -lse2);
       }
       if (nvalid < BN) {
+        // row 32 kb + acc_row(r, hh) >= nvalid, as 4 hh against a uniform
+        // bound; h4 is opaque, so the row indices are not hoisted out of the
+        // loop into registers of their own
+        int h4 = 4 * hh;
+        __asm__ volatile("" : "+v"(h4));
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kb + acc_row(r, hh) >= nvalid) s[r] = -INFINITY;
+          if (h4 >= nvalid - (32 * kb + acc_row(r, 0))) s[r] = -INFINITY;
       }
       x8_t<T> pf_unused[2];
       p_ds_pack<T>(s, dp, pf_unused, dsf[kb]);   // P itself is not needed here
