@@ -138,3 +138,18 @@ def test_hstu_c5_histories_full_size_sampled(gpu):
         sl = slice(int(off[b]), int(off[b + 1]))
         ref = O.hstu_attn_fwd(host(tq[sl]), host(tk[sl]), host(tv[sl]), np.array([0, L[b]]), h, ts[sl], wp, wt)
         assert_close(f"A[request {b}]", A[sl], ref, "bf16")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hstu_explicit_scale_and_large_biases(gpu, dtype):
+    """A scale other than 1/sqrt(d_h) (the kernel folds -log2(e) scale into
+    Q once) and bias tables twenty times larger (the position bias starts
+    the score accumulators; far tiles read the time table with the last
+    position entry folded in): ragged lengths across far, interior and edge
+    tiles, including the position table's last entry."""
+    L, d, h = [700, 65, 300], 128, 2
+    q, k, v, off, ts, wp, wt = _inputs(13, L, d, dtype, 200, 24)
+    wp, wt = 20.0 * wp, 20.0 * wt
+    A = _run(gpu, q, k, v, off, ts, wp, wt, h, dtype, scale=0.37)
+    ref = O.hstu_attn_fwd(q, k, v, off, h, ts, wp, wt, scale=0.37)
+    assert_close("A", A, ref, dtype)
