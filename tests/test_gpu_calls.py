@@ -551,7 +551,10 @@ def test_xattn_bwd_kv_schedule(gpu, case, monkeypatch):
 @pytest.mark.parametrize("B", [256, 257])
 def test_xattn_many_jagged_requests(gpu, B):
     dtype, d, h, C, n_q = "bf16", 128, 2, 32, 32
-    L = [(37 * b + 11) % 61 for b in range(B)]     # 0 ... 60, every length several times
+    # 129 ... 328 rows (past 128: the Q-parallel schedule of the backward),
+    # plus an empty and a one-row history
+    L = [129 + (37 * b + 11) % 200 for b in range(B)]
+    L[3], L[5] = 0, 1
     print(f"\n[xattn many jagged] B={B} max_L={max(L)}", flush=True)
     QR = C * n_q
     M, off = B * QR, offsets(L)
@@ -577,3 +580,40 @@ def test_xattn_many_jagged_requests(gpu, B):
         if L[b] > 0:
             assert_close(f"dK[{b}]", dK[k], dK_ref, dtype)
             assert_close(f"dV[{b}]", dV[k], dV_ref, dtype)
+
+
+def test_xattn_order_changes_no_bit(gpu):
+    """The same 256 jagged requests run longest history first (alone) and in
+    index order (with a 257th request appended): every output of the 256,
+    forward and backward, is the same bit for bit."""
+    dtype, d, h, C, n_q = "bf16", 128, 2, 32, 32
+    # histories past 128 rows (the Q-parallel backward, one query split for
+    # both batch sizes); the appended request is shorter than the longest, so
+    # the shape hints other than B and total_L are the same
+    L = [130 + (29 * b + 7) % 150 for b in range(256)]
+    QR = C * n_q
+
+    def run(lengths):
+        B = len(lengths)
+        M, off = B * QR, offsets(lengths)
+        T = int(off[-1])
+        Q, K, V, dA = draw(51, (M, d), dtype), draw(52, (T, d), dtype), draw(53, (T, d), dtype), draw(54, (M, d), dtype)
+        dm = wb.dims(B, C, n_q, d, h, max(lengths), T)
+        tQ, tK, tV, tdA = (to_dev(x, dtype, gpu) for x in (Q, K, V, dA))
+        toff = i64_dev(off, gpu)
+        A, lse = torch.empty_like(tQ), torch.empty((M, h), device=gpu)
+        wb.whale_jagged_xattn_fwd(dm, tQ, tK, tV, toff, 0.0, A, lse)
+        dQ, dK, dV = torch.empty_like(tQ), torch.empty_like(tK), torch.empty_like(tV)
+        ws = torch.empty(wb.whale_jagged_xattn_bwd_workspace_size(dm, wb._dtype_code(tQ)), dtype=torch.uint8,
+                         device=gpu)
+        wb.whale_jagged_xattn_bwd(dm, tQ, tK, tV, toff, 0.0, A, lse, tdA, dQ, dK, dV, ws)
+        torch.cuda.synchronize()
+        return A, lse, dQ, dK, dV
+
+    # the appended request's rows come last in every tensor, so the first
+    # 256 requests' inputs (drawn row-major from the same seeds) are identical
+    ranked = run(L)
+    indexed = run(L + [5])
+    M, T = 256 * QR, int(offsets(L)[-1])
+    for name, a, b_, n in zip(("A", "lse", "dQ", "dK", "dV"), ranked, indexed, (M, M, M, T, T)):
+        assert torch.equal(a[:n], b_[:n]), name
