@@ -255,6 +255,8 @@ def main():
     ap.add_argument("--hstu", action="store_true",
                     help="time the HSTU self-attention (whale_hstu_attn_fwd) on the history shapes of --config "
                          "(c5 by default for this mode), position table 4096, time table 32")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the forward replayed from one HIP graph capture (forward-only steps)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run a plain elementwise copy (negation) of 512 MiB fp32, 3 times: the reference kernel "
                          "for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -377,6 +379,45 @@ def main():
     # per step: a stack runs each forward call once per layer
     avg = {n: float(np.sum(v)) / args.steps for n, v in per_call.items()}
 
+    graph_ms, graph_equal = None, None
+    if args.graph:
+        # The same forward captured once in a HIP graph and replayed: no host
+        # launch gaps between the calls.  The replay's output is checked bit
+        # for bit against an eager forward before it is timed.
+        if backward:
+            print("--graph times forward-only steps (use --fwd-only)", file=sys.stderr)
+            sys.exit(2)
+
+        def run_fwd():
+            x = tHw
+            for ell, lay in enumerate(layers):
+                x = lay.forward(x, tHs[ell], toff, max_L, **fwd_kw)["Y"]
+            return x
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run_fwd()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            y_graph = run_fwd()
+        torch.cuda.synchronize()
+        y_eager = run_fwd().clone()
+        g.replay()
+        torch.cuda.synchronize()
+        graph_equal = bool(torch.equal(y_graph, y_eager))
+        gev = []
+        for _ in range(args.steps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            gev.append((e0, e1))
+        torch.cuda.synchronize()
+        graph_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in gev]))
+        del g, y_graph, y_eager
+
     if args.serving:
         f = flops(cfg, T, cfg.H, shared_kv=args.shared_kv, M=int(tHw.shape[0]), pairs=cfg.n_q * float(np.dot(Cb, L)),
                   ffn=cfg.ffn)
@@ -449,6 +490,11 @@ def main():
         "mfma_probe": probe,
         "wall_s": round(wall, 2),
     }
+    if graph_ms is not None:
+        res["graph"] = {"ms_per_step": round(graph_ms, 3),
+                        "tflops": round(step_flops / (graph_ms * 1e-3) / 1e12, 2),
+                        "requests_per_s": round(cfg.B / (graph_ms * 1e-3), 1),
+                        "output_equal_to_eager": graph_equal}
     if not args.no_cpu:
         n_req = args.cpu_requests or SCOPE[key]["cpu_requests"]
         print(f"[bench] cpu baseline ({n_req} requests, fp64 oracle)", file=sys.stderr, flush=True)
