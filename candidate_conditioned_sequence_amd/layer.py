@@ -79,11 +79,12 @@ class FusionLayer:
         V = None if self.tied_kv else _empty((T, d), dt, dev)
         sq = _empty((M, 2), torch.float32, dev) if nn else None
         skv = _empty((T, 2), torch.float32, dev) if nn else None
-        # The normalised inputs are written once (the projections then read them
-        # and the backward reuses them); without them the projections normalise
-        # per tile.
-        Xq = _empty((M, d), dt, dev) if nn else None
-        Xs = _empty((T, d), dt, dev) if nn else None
+        # For the backward the normalised inputs are written once (the
+        # projections then read them and the backward reuses them).  A
+        # forward-only call does not keep them: the projections normalise on
+        # the fly and write only the row statistics.
+        Xq = _empty((M, d), dt, dev) if (nn and save) else None
+        Xs = _empty((T, d), dt, dev) if (nn and save) else None
         wb.whale_proj_qkv(dm, H_w, H_s, self.norm, self.eps, p["g_q"], p["b_q"], p["g_kv"], p["b_kv"], p["W_Q"],
                           p["W_K"], p.get("W_V"), Q, K, V, sq, skv, Xq, Xs, stream)
         if self.tied_kv:
